@@ -1,0 +1,65 @@
+"""Plants plausible mistakes in a COPY of the oracle source (CPU only) and
+checks that the oracle pins catch every one of them.
+
+Each mutant is a one-line edit of oracle/kvq_oracle.c, compiled into a
+temporary library that a child pytest process loads in place of the real
+oracle; the pin suite must fail for it.  (A lower clamp of -128 is not listed:
+|r/s| never rounds beyond 127, so that edit cannot change any output.)
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
+
+MUTANTS = {
+    "round_ties_even": ("float r = roundf(resid[d] / sc);", "float r = rintf(resid[d] / sc);"),
+    "reciprocal": ("float r = roundf(resid[d] / sc);", "float r = roundf(resid[d] * (1.0f / sc));"),
+    "col_multiplies": ("x[d] / col[d]", "x[d] * col[d]"),
+    "no_scale_floor": ("if (sc < 1e-12f) sc = 1e-12f;", ""),
+    "scale_1_over_hd": ("double scale = 1.0 / sqrt((double)hd);\n    double* s",
+                        "double scale = 1.0 / (double)hd;\n    double* s"),
+    "softmax_no_max": ("s[p] = exp(s[p] - m); z += s[p];", "s[p] = exp(s[p]); z += s[p];"),
+    "transposed_v": ("oh[d] += w * vf(vctx, p, d);", "oh[d] += w * vf(vctx, d % n, p % hd);"),
+    "rms_no_mean": ("float c = sqrtf(col[d] / (float)n);", "float c = sqrtf(col[d]);"),
+    "rms_wrong_n": ("float c = sqrtf(col[d] / (float)n);", "float c = sqrtf(col[d] / (float)(n + 1));"),
+    "freeze_one_late": ("if (*n >= ORC_COL_WARMUP && !*frozen)", "if (*n > ORC_COL_WARMUP && !*frozen)"),
+    "dequant_drops_scale": ("(float)q[(size_t)p * hd + d] * s[(size_t)p * ns + d / group];",
+                            "(float)q[(size_t)p * hd + d];"),
+    "q8_drops_col": ("if (r->col != NULL) x = x * (double)r->col[d];", ""),
+    "q8_wrong_group": ("* (double)r->scales[(size_t)p * r->ns + d / r->group];",
+                       "* (double)r->scales[(size_t)p * r->ns + (d / r->group) % 2];"),
+    "fused_rms": ("float sq = x * x;\n            col[d] = col[d] + sq;", "col[d] = fmaf(x, x, col[d]);"),
+    "requant_wrong_row": ("orc_quant_row(rows + (size_t)p * hd, col", "orc_quant_row(rows + 0 * (size_t)p * hd, col"),
+}
+
+RUNNER = r'''
+import sys
+sys.path.insert(0, sys.argv[2])
+import oracle
+oracle._LIB = sys.argv[1]
+oracle.build = lambda force=False: sys.argv[1]
+import pytest
+sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider", sys.argv[3]]))
+'''
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, "mutation site not found: " + name
+    c = tmp_path / (name + ".c")
+    so = tmp_path / (name + ".so")
+    c.write_text(src.replace(old, new, 1))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", str(so), str(c), "-lm"], check=True)
+    runner = tmp_path / "run.py"
+    runner.write_text(RUNNER)
+    pins = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+    r = subprocess.run([sys.executable, str(runner), str(so), ROOT, pins],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "mutant survived the pins: " + name

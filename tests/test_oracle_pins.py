@@ -1,0 +1,558 @@
+"""Pins the CPU oracle to things other than itself (CPU only).
+
+Every check here compares the oracle against something the pages or the
+mathematics fix independently of the oracle's code: values the pages print
+for worked examples (tests/golden/, each cited), closed forms, invariants,
+a library routine that computes the same definition (torch's
+scaled_dot_product_attention in float64), and exact rational arithmetic for
+the f32 codec.
+
+Pages:
+  [P1] cortiq-engine 0.3.4, src/cortiq_engine/kv_cache.rs
+  [P3] franken_ocr 0.8.0, src/native_engine/rswa.rs
+"""
+import decimal
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+HD = 128
+
+
+def bits_f32(h: str) -> float:
+    return struct.unpack("<f", struct.pack("<I", int(h, 16)))[0]
+
+
+def f32_round(x: Fraction) -> float:
+    """Round an exact rational to the nearest float32, ties to even."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                         # subnormal range keeps the exponent
+    m = a / (Fraction(2) ** (e - 23))        # in [2^23, 2^24) for normals
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = Fraction(fl) * Fraction(2) ** (e - 23)
+    return sign * float(np.float32(float(val)))
+
+
+def half_away(x: float) -> int:
+    return int(math.copysign(math.floor(abs(x) + 0.5), x))
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# Attention (float64, by definition)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,hd,hpk", [(1, 4, 1), (2, 4, 1), (3, 32, 2), (9, 128, 1),
+                                      (9, 128, 4), (300, 128, 4), (57, 32, 3)])
+def test_attention_matches_library_sdpa(n, hd, hpk):
+    """Library routine computing the same definition: torch SDPA in float64
+    with its default scale 1/sqrt(hd)."""
+    r = rng(1000 + n * 7 + hd + hpk)
+    q = r.standard_normal((hpk, hd)).astype(np.float32)
+    k = r.standard_normal((n, hd)).astype(np.float32) * 2
+    v = r.standard_normal((n, hd)).astype(np.float32)
+    got = oracle.attend_f32(q, k, v)
+    tq = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
+    tk = torch.from_numpy(k.astype(np.float64))[None, None].expand(1, hpk, n, hd).contiguous()
+    tv = torch.from_numpy(v.astype(np.float64))[None, None].expand(1, hpk, n, hd).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_empty_rows_give_zero():
+    """[P1] attend_group: stored == 0 -> output filled with 0."""
+    q = np.ones((4, HD), np.float32)
+    out = oracle.attend_f32(q, np.zeros((0, HD), np.float32), np.zeros((0, HD), np.float32))
+    assert out.shape == (4, HD) and not out.any()
+
+
+def _e(dim, value, hd=HD):
+    x = np.zeros(hd, np.float32)
+    x[dim] = value
+    return x
+
+
+def test_worked_values_from_rswa_page(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "rswa_worked_values.json")))
+    sk = g["single_key"]
+    out = oracle.attend_f32(_e(sk["q"]["dim"], sk["q"]["value"]),
+                            _e(sk["k0"]["dim"], sk["k0"]["value"])[None],
+                            np.full((1, HD), sk["v"], np.float32))
+    assert np.all(out == sk["expected"])          # a single key has weight exactly 1
+
+    eq = g["equal_scores"]
+    k = np.stack([_e(eq["k"]["dim"], eq["k"]["value"])] * 2)
+    v = np.stack([np.full(HD, x, np.float32) for x in eq["v_rows"]])
+    out = oracle.attend_f32(_e(eq["q"]["dim"], eq["q"]["value"]), k, v)
+    np.testing.assert_allclose(out, eq["expected"], rtol=0, atol=1e-15)
+
+    rp = g["reference_plus_ring"]
+    k = np.stack([_e(rp["ref_key_dim"], 1.0), _e(rp["ring_key_dim"], 1.0)])
+    v = np.stack([np.full(HD, rp["ref_v"], np.float32), np.full(HD, rp["ring_v"], np.float32)])
+    q = _e(0, rp["q_e0"])
+    out = oracle.attend_f32(q, k, v)
+    # the page's printed digits
+    assert abs(out[0] - rp["printed_output"]) < rp["printed_digits_tolerance"]
+    w = oracle.weights_f32(q, k)
+    assert abs(w[1] - rp["printed_ring_weight"]) < rp["printed_digits_tolerance"]
+    assert abs(w[0] - rp["printed_ref_weight"]) < rp["printed_digits_tolerance"]
+    # the page's closed form, two keys: logistic of the score gap
+    e = math.exp(rp["q_e0"] / math.sqrt(HD))
+    np.testing.assert_allclose(out, (e * rp["ring_v"] + rp["ref_v"]) / (e + 1), rtol=0, atol=1e-14)
+
+
+def test_weights_sum_to_one_and_constant_values():
+    r = rng(7)
+    for n in (1, 5, 64, 1000):
+        q = r.standard_normal(HD).astype(np.float32) * 3
+        k = r.standard_normal((n, HD)).astype(np.float32)
+        w = oracle.weights_f32(q, k)
+        assert abs(w.sum() - 1.0) < 1e-12 and np.all(w > 0)
+        out = oracle.attend_f32(q, k, np.ones((n, HD), np.float32))
+        np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-12)
+
+
+def test_permutation_invariance_and_convex_hull():
+    r = rng(8)
+    n = 77
+    q = r.standard_normal((4, HD)).astype(np.float32)
+    k = r.standard_normal((n, HD)).astype(np.float32)
+    v = r.standard_normal((n, HD)).astype(np.float32)
+    perm = r.permutation(n)
+    a = oracle.attend_f32(q, k, v)
+    b = oracle.attend_f32(q, k[perm], v[perm])
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    assert np.all(a <= v.max(axis=0) + 1e-12) and np.all(a >= v.min(axis=0) - 1e-12)
+
+
+def test_zero_query_gives_mean_and_sharp_query_gives_argmax():
+    r = rng(9)
+    n = 33
+    k = r.standard_normal((n, HD)).astype(np.float32)
+    v = r.standard_normal((n, HD)).astype(np.float32)
+    out = oracle.attend_f32(np.zeros(HD, np.float32), k, v)
+    np.testing.assert_allclose(out, v.astype(np.float64).mean(axis=0), rtol=0, atol=1e-13)
+    # a query far along key j: softmax collapses onto row j
+    j = 17
+    q = (k[j] * 200.0).astype(np.float32)
+    out = oracle.attend_f32(q, k, v)
+    np.testing.assert_allclose(out, v[j], rtol=0, atol=1e-9)
+
+
+def test_linearity_in_values():
+    r = rng(10)
+    n = 40
+    q = r.standard_normal(HD).astype(np.float32)
+    k = r.standard_normal((n, HD)).astype(np.float32)
+    v1 = r.standard_normal((n, HD)).astype(np.float32)
+    v2 = r.standard_normal((n, HD)).astype(np.float32)
+    a = oracle.attend_f32(q, k, v1) * 0.5 + oracle.attend_f32(q, k, v2) * 2.0
+    b = oracle.attend_f32(q, k, (v1.astype(np.float64) * 0.5 + v2 * 2.0).astype(np.float32))
+    # (the combined V is rounded to f32 once, so allow that rounding)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-6)
+
+
+def test_gqa_mapping_and_dead_groups():
+    """[P1] attend_group: Q head h reads KV group h // hpk; dead groups
+    store nothing and their Q heads output zeros.  Checked against torch SDPA
+    with K/V repeated per Q head (float64)."""
+    r = rng(11)
+    B, Hq, Hkv, n = 2, 8, 4, 23
+    hpk = Hq // Hkv
+    q = r.standard_normal((B, Hq, HD)).astype(np.float32)
+    k = r.standard_normal((B, Hkv, n, HD)).astype(np.float32)
+    v = r.standard_normal((B, Hkv, n, HD)).astype(np.float32)
+    dead = {1}
+    units = [[None if g in dead else ("f32", k[b, g], v[b, g]) for g in range(Hkv)] for b in range(B)]
+    out = oracle.decode(q, units, Hkv, threads=3)
+    tq = torch.from_numpy(q.astype(np.float64))[:, :, None, :]
+    tk = torch.from_numpy(k.astype(np.float64)).repeat_interleave(hpk, dim=1)
+    tv = torch.from_numpy(v.astype(np.float64)).repeat_interleave(hpk, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[:, :, 0, :].numpy()
+    for h in range(Hq):
+        if h // hpk in dead:
+            assert not out[:, h].any()
+        else:
+            np.testing.assert_allclose(out[:, h], ref[:, h], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# q8_2f codec (IEEE f32, step by step)
+# ---------------------------------------------------------------------------
+def test_quant_row_half_away_fixture(golden_dir):
+    fx = json.load(open(os.path.join(golden_dir, "q8_2f_quant_fixtures.json")))["half_away_row"]
+    x = np.zeros(fx["head_dim"], np.float32)
+    x[: len(fx["row_prefix"])] = fx["row_prefix"]
+    m = len(fx["k_codes_prefix"])
+    q, s = oracle.quant_row(x, None, 32)
+    assert s[0] == fx["k_group0_scale"]
+    assert list(q[:m]) == fx["k_codes_prefix"] and not q[m:].any()
+    tiny = np.float32(fx["zero_group_scale_f32_of"])
+    assert np.all(s[1:] == tiny)
+    qv, sv = oracle.quant_row(x, None, fx["head_dim"])
+    assert sv.shape == (1,) and sv[0] == fx["v_scale"]
+    assert list(qv[:m]) == fx["v_codes_prefix"] and not qv[m:].any()
+
+
+def test_quant_row_divides_and_rounds_half_away(golden_dir):
+    """Expected codes from exact rational arithmetic: s = f32(absmax/127),
+    code = half_away(f32(x/s)).  Each case also shows which wrong reading it
+    rules out (multiplying by f32(1/s), or rounding ties to even)."""
+    fx = json.load(open(os.path.join(golden_dir, "q8_2f_quant_fixtures.json")))["division_cases"]
+    ruled_out = set()
+    for case in fx["cases"]:
+        a, x = bits_f32(case["absmax_bits"]), bits_f32(case["x_bits"])
+        s = f32_round(Fraction(a) / 127)
+        quot = f32_round(Fraction(x) / Fraction(s))
+        want = max(-127, min(127, half_away(quot)))
+        recip = f32_round(Fraction(x) * Fraction(f32_round(1 / Fraction(s))))
+        if half_away(recip) != want:
+            ruled_out.add("reciprocal")
+        if quot == math.floor(quot) + 0.5 and round(quot) != want:   # Python round = ties-even
+            ruled_out.add("ties-even")
+        row = np.zeros(HD, np.float32)
+        row[0], row[1] = a, x
+        q, sc = oracle.quant_row(row, None, 32)
+        assert sc[0] == np.float32(s)
+        assert q[1] == want, (case, q[1], want)
+        assert q[0] == 127
+    assert ruled_out == {"reciprocal", "ties-even"}
+
+
+def test_quant_row_against_exact_rationals_random():
+    """Random rows (with and without a column field): every scale and code
+    equals the exact-rational computation of the page's steps."""
+    r = rng(12)
+    for trial in range(6):
+        x = (r.standard_normal(HD) * r.uniform(0.01, 50)).astype(np.float32)
+        col = None if trial % 2 == 0 else r.uniform(0.2, 9, HD).astype(np.float32)
+        for group in (32, HD):
+            q, s = oracle.quant_row(x, col, group)
+            resid = [Fraction(float(x[d])) if col is None
+                     else Fraction(f32_round(Fraction(float(x[d])) / Fraction(float(col[d]))))
+                     for d in range(HD)]
+            for gi, g0 in enumerate(range(0, HD, group)):
+                am = max(abs(v) for v in resid[g0:g0 + group])
+                sc = max(f32_round(am / 127), float(np.float32(1e-12)))
+                assert s[gi] == np.float32(sc)
+                for d in range(g0, g0 + group):
+                    want = max(-127, min(127, half_away(f32_round(resid[d] / Fraction(sc)))))
+                    assert q[d] == want
+
+
+def test_quant_row_invariants():
+    r = rng(13)
+    for _ in range(20):
+        x = (r.standard_normal(HD) * r.uniform(1e-3, 1e3)).astype(np.float32)
+        q, s = oracle.quant_row(x, None, 32)
+        for gi in range(4):
+            g = slice(32 * gi, 32 * gi + 32)
+            # the group's absmax element maps to +-127
+            j = 32 * gi + int(np.argmax(np.abs(x[g])))
+            assert abs(int(q[j])) == 127 and np.sign(q[j]) == np.sign(x[j])
+            # round-trip bound |x - q*s| <= s/2 (plus the division's rounding)
+            err = np.abs(x[g].astype(np.float64) - q[g].astype(np.float64) * float(s[gi]))
+            assert np.all(err <= 0.5 * float(s[gi]) * (1 + 2 ** -20))
+        # power-of-two scaling is exact: codes unchanged, scales scaled
+        for e in (-3, 5):
+            q2, s2 = oracle.quant_row((x * np.float32(2.0 ** e)).astype(np.float32), None, 32)
+            assert np.array_equal(q, q2) and np.array_equal(s * np.float32(2.0 ** e), s2)
+
+
+def test_quant_row_lossless_integers_exhaustive():
+    """Rows of integers whose groups contain +-127 have scale 1 and codes equal
+    to the values: every code -127..127 round-trips."""
+    codes = np.arange(-127, 128)
+    full = np.concatenate([codes, codes[::-1], codes])[: 3 * HD]
+    for start in range(0, len(full) - HD + 1, HD):
+        x = full[start:start + HD].astype(np.float32).copy()
+        for gi in range(4):
+            x[32 * gi] = 127.0
+        q, s = oracle.quant_row(x, None, 32)
+        assert np.all(s == 1.0) and np.array_equal(q.astype(np.float32), x)
+    covered = set()
+    for start in range(0, len(full) - HD + 1, HD):
+        covered |= set(full[start:start + HD].tolist())
+    assert covered == set(range(-127, 128))
+
+
+def test_zero_group_scale():
+    q, s = oracle.quant_row(np.zeros(HD, np.float32), None, 32)
+    assert not q.any() and np.all(s == np.float32(1e-12))
+    q, s = oracle.quant_row(np.zeros(HD, np.float32), np.full(HD, 3.0, np.float32), HD)
+    assert not q.any() and s[0] == np.float32(1e-12)
+
+
+def _lossless_rows(r, n, c=None):
+    """n rows of integers; every K group and every row contains +-127."""
+    if c is None:
+        x = r.integers(-127, 128, size=(n, HD)).astype(np.float32)
+    else:
+        x = (np.where(r.random((n, HD)) < 0.5, -1.0, 1.0) * c[None, :]).astype(np.float32)
+    x[:, ::32] = np.where(r.random((n, 4)) < 0.5, -127.0, 127.0)
+    return x
+
+
+def test_freeze_constant_magnitude_closed_form():
+    """Channels of constant magnitude c_d over 64 lossless rows: the field is
+    exactly c_d, every requantised residual is +-1, so every code is +-127 and
+    every scale is f32(1/127) ([P1] freeze_cols on closed-form rows)."""
+    r = rng(14)
+    c = r.integers(1, 128, size=HD).astype(np.float64)
+    c[::32] = 127.0
+    k = _lossless_rows(r, 65, c)
+    v = _lossless_rows(r, 65, c)
+    h = oracle.Q8Head(cap=80, hd=HD)
+    h.append(k[:64], v[:64])
+    assert h.n == 64 and not h.frozen                      # 64 rows: not yet frozen
+    assert np.array_equal(h.kq[:64].astype(np.float32), k[:64]) and np.all(h.ks[:64] == 1.0)
+    h.append(k[64:65], v[64:65])                            # the 65th append freezes first
+    assert h.frozen and h.n == 65
+    assert np.array_equal(h.kcol, c.astype(np.float32)) and np.array_equal(h.vcol, c.astype(np.float32))
+    inv127 = np.float32(f32_round(Fraction(1, 127)))
+    code = half_away(f32_round(Fraction(1) / Fraction(float(inv127))))
+    assert code == 127
+    for p in range(65):                                     # row 64 against the frozen field too
+        assert np.array_equal(h.kq[p], (np.sign(k[p]) * 127).astype(np.int8))
+        assert np.array_equal(h.vq[p], (np.sign(v[p]) * 127).astype(np.int8))
+        assert np.all(h.ks[p] == inv127) and h.vs[p] == inv127
+
+
+def _sqrt_f32_exact(x: Fraction) -> float:
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        d = (decimal.Decimal(x.numerator) / decimal.Decimal(x.denominator)).sqrt()
+    return f32_round(Fraction(d))
+
+
+def test_freeze_rms_exact_sums():
+    """Lossless integer rows: sum of squares is exact in f32, so the field is
+    the correctly rounded sqrt(sum/64), floored at 1e-6."""
+    r = rng(15)
+    k = _lossless_rows(r, 65)
+    v = _lossless_rows(r, 65)
+    k[:64, 5] = 0.0                                         # an all-zero channel -> 1e-6
+    h = oracle.Q8Head(cap=70, hd=HD)
+    h.append(k, v)
+    for name, x, col in (("k", k, h.kcol), ("v", v, h.vcol)):
+        for d in range(HD):
+            s = int(np.sum(x[:64, d].astype(np.int64) ** 2))
+            want = max(_sqrt_f32_exact(Fraction(s, 64)), float(np.float32(1e-6)))
+            assert col[d] == np.float32(want), (name, d)
+
+
+def test_freeze_rms_rounds_each_operation():
+    """Non-integer rows: the field follows the page's f32 steps exactly --
+    x^ = f32(code*scale), acc = f32(acc + f32(x^*x^)) sequentially over rows
+    (a multiply and an add, each rounded; no fused multiply-add),
+    col = max(f32(sqrt(f32(acc/n))), 1e-6).  Recomputed with exact rationals;
+    the fused variant is also computed to show the case separates the two."""
+    r = rng(20)
+    k = (r.standard_normal((65, HD)) * r.uniform(0.3, 7, HD)).astype(np.float32)
+    v = (r.standard_normal((65, HD)) * 2.5).astype(np.float32)
+    h = oracle.Q8Head(cap=65, hd=HD)
+    h.append(k[:64], v[:64])
+    kq0, ks0 = h.kq[:64].copy(), h.ks[:64].copy()
+    h.append(k[64:], v[64:])
+    fused_differs = False
+    for d in range(0, HD, 3):
+        acc = Fraction(0)
+        acc_fma = Fraction(0)
+        for p in range(64):
+            xh = Fraction(f32_round(Fraction(int(kq0[p, d])) * Fraction(float(ks0[p, d // 32]))))
+            acc = Fraction(f32_round(acc + Fraction(f32_round(xh * xh))))
+            acc_fma = Fraction(f32_round(acc_fma + xh * xh))
+        want = max(_sqrt_f32_exact(Fraction(f32_round(acc / 64))), float(np.float32(1e-6)))
+        assert h.kcol[d] == np.float32(want), d
+        fused_differs |= acc != acc_fma
+    assert fused_differs
+
+
+def test_freeze_requantises_dequantised_rows():
+    """After the freeze, rows 0..63 are the quantisation of the DEQUANTISED
+    rows against the field; later rows quantise the raw input against it."""
+    r = rng(16)
+    k = (r.standard_normal((70, HD)) * 3).astype(np.float32)
+    v = (r.standard_normal((70, HD)) * 3).astype(np.float32)
+    h = oracle.Q8Head(cap=70, hd=HD)
+    h.append(k[:64], v[:64])
+    kq0, ks0 = h.kq[:64].copy(), h.ks[:64].copy()
+    h.append(k[64:], v[64:])
+    xh = (kq0.astype(np.float32) * np.repeat(ks0, 32, axis=1)).astype(np.float32)
+    for p in (0, 31, 63):
+        q, s = oracle.quant_row(xh[p], h.kcol, 32)
+        assert np.array_equal(q, h.kq[p]) and np.array_equal(s, h.ks[p])
+    for p in (64, 69):
+        q, s = oracle.quant_row(k[p], h.kcol, 32)
+        assert np.array_equal(q, h.kq[p]) and np.array_equal(s, h.ks[p])
+        q, s = oracle.quant_row(v[p], h.vcol, HD)
+        assert np.array_equal(q, h.vq[p]) and s[0] == h.vs[p]
+
+
+def test_chunked_append_equals_row_by_row_and_explicit_freeze():
+    r = rng(17)
+    k = (r.standard_normal((130, HD)) * 2).astype(np.float32)
+    v = (r.standard_normal((130, HD)) * 2).astype(np.float32)
+    a = oracle.Q8Head(cap=130)
+    for p in range(130):
+        a.append(k[p:p + 1], v[p:p + 1])
+    b = oracle.Q8Head(cap=130)
+    for lo, hi in ((0, 7), (7, 64), (64, 65), (65, 130)):
+        b.append(k[lo:hi], v[lo:hi])
+    c = oracle.Q8Head(cap=130)
+    c.append(k, v)
+    for o in (b, c):
+        for f in ("kq", "ks", "vq", "vs", "kcol", "vcol"):
+            assert np.array_equal(getattr(a, f), getattr(o, f)), f
+    # an explicit freeze is a no-op once frozen, and freezes early otherwise
+    assert not a.freeze()
+    e = oracle.Q8Head(cap=40)
+    e.append(k[:40], v[:40])
+    assert not e.frozen and e.freeze() and e.frozen and not e.freeze()
+
+
+def test_q8_attention_within_page_grid_bound():
+    """[P1] test q8_attend_matches_f32_within_grid: 100 positions (crossing the
+    freeze), 2 heads x 32 channels of the page's modular pattern with even
+    channels x4 and odd x0.25; q8 output within 0.03*max|o| + 1e-3 of f32 and
+    probabilities within 0.02."""
+    heads, hd = 2, 32
+
+    def synth(p, salt):
+        i = np.arange(heads * hd)
+        x = ((i * 31 + p * 17 + salt * 7 + 3) % 97).astype(np.float32) / np.float32(97.0) - np.float32(0.5)
+        return np.where(i % 2 == 0, x * np.float32(4.0), x * np.float32(0.25)).astype(np.float32)
+
+    K = np.stack([synth(p, 1) for p in range(100)]).reshape(100, heads, hd)
+    V = np.stack([synth(p, 2) for p in range(100)]).reshape(100, heads, hd)
+    q = (((np.arange(hd) * 13 + 5) % 89).astype(np.float32) / np.float32(89.0) - np.float32(0.5)).astype(np.float32)
+    for g in range(heads):
+        h = oracle.Q8Head(cap=100, hd=hd)
+        h.append(K[:, g], V[:, g])
+        assert h.frozen
+        of = oracle.attend_f32(q, K[:, g], V[:, g])
+        o8 = oracle.attend_q8(q, h)
+        scale = max(np.abs(of).max(), 1e-6)
+        assert np.all(np.abs(of - o8) <= scale * 0.03 + 1e-3)
+        pf = oracle.weights_f32(q, K[:, g])
+        p8 = oracle.weights_f32(q, h.dequant_k().astype(np.float32))
+        assert np.all(np.abs(pf - p8) < 0.02)
+
+
+def test_q8_attention_equals_attention_on_dequantised_rows():
+    """attend_q8 is attention over K^ = code*scale*col, V^ = code*scale*col."""
+    r = rng(18)
+    h = oracle.Q8Head(cap=100)
+    h.append((r.standard_normal((100, HD)) * 4).astype(np.float32),
+             (r.standard_normal((100, HD)) * 4).astype(np.float32))
+    q = r.standard_normal((4, HD)).astype(np.float32)
+    got = oracle.attend_q8(q, h)
+    kk, vv = h.dequant_k(), h.dequant_v()
+    tq = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
+    tk = torch.from_numpy(kk)[None, None].expand(1, 4, 100, HD).contiguous()
+    tv = torch.from_numpy(vv)[None, None].expand(1, 4, 100, HD).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# R-SWA ring cursors
+# ---------------------------------------------------------------------------
+def test_ring_slots_from_page(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "ring_slots.json")))
+    W = g["window"]
+    m = oracle.RingModel(W)
+    m.record_prefill(4)
+    for t in range(W):
+        assert m.write(t) == t and m.ring_len == t + 1 and m.effective_len() == 4 + t + 1
+    assert m.ring_len == g["warmup"]["ring_len_after"] and m.ring_pos == g["warmup"]["ring_pos_after"]
+    for slot, pos in zip(g["steady"]["slots"], g["steady"]["ring_pos_after_each"]):
+        assert m.write("x") == slot and m.ring_pos == pos and m.ring_len == W
+    m2 = oracle.RingModel(W)
+    m2.record_prefill(1)
+    for t in range(W):
+        m2.write(t)
+    for s in range(W):
+        assert m2.write(W + s) == s
+    assert m2.ring_pos == g["wrap"]["ring_pos_after"]
+    for n, key in ((165, "writes_165_ring_pos"), (500, "writes_500_ring_pos")):
+        m3 = oracle.RingModel(W)
+        m3.record_prefill(0)
+        for t in range(n):
+            m3.write(t)
+        assert m3.ring_pos == g["workload_cursors"][key] == n % W
+
+
+def test_ring_physical_slots_closed_form():
+    """After n writes token t sits in slot t mod W for every live t, and the
+    live set is exactly the last min(n, W) tokens."""
+    W = 128
+    for n in (1, 5, 127, 128, 129, 300, 500):
+        m = oracle.RingModel(W)
+        m.record_prefill(3)
+        for t in range(n):
+            m.write(t)
+        phys = m.physical()
+        assert len(phys) == min(n, W)
+        for t in range(max(0, n - W), n):
+            assert phys[t % W] == t
+        assert sorted(phys) == m.window() == list(range(max(0, n - W), n))
+
+
+def test_ring_attention_equals_explicit_window():
+    """Attention over reference rows ++ physical ring slots equals attention
+    over reference rows ++ the explicit window of the last W tokens."""
+    r = rng(19)
+    W, prefill, n = 16, 5, 41
+    ref_k = r.standard_normal((prefill, HD)).astype(np.float32)
+    ref_v = r.standard_normal((prefill, HD)).astype(np.float32)
+    tok_k = r.standard_normal((n, HD)).astype(np.float32)
+    tok_v = r.standard_normal((n, HD)).astype(np.float32)
+    m = oracle.RingModel(W)
+    m.record_prefill(prefill)
+    ring_k = np.zeros((W, HD), np.float32)
+    ring_v = np.zeros((W, HD), np.float32)
+    q = r.standard_normal((2, HD)).astype(np.float32)
+    for t in range(n):
+        s = m.write(t)
+        ring_k[s], ring_v[s] = tok_k[t], tok_v[t]
+        phys_k = np.concatenate([ref_k, ring_k[: m.ring_len]])
+        phys_v = np.concatenate([ref_v, ring_v[: m.ring_len]])
+        win = m.window()
+        exp_k = np.concatenate([ref_k, tok_k[win]])
+        exp_v = np.concatenate([ref_v, tok_v[win]])
+        np.testing.assert_allclose(oracle.attend_f32(q, phys_k, phys_v),
+                                   oracle.attend_f32(q, exp_k, exp_v), rtol=0, atol=1e-13)
+
+
+def test_workload_generators_are_deterministic():
+    s = workloads.get("batched_q8")
+    L = s.lengths()
+    assert L.min() >= 1024 and L.max() <= 32768 and len(L) == 64
+    k1, v1 = s.kv_rows(3, 10, 5)
+    k2, v2 = s.kv_rows(3, 0, 15)
+    assert np.array_equal(k1, k2[10:]) and np.array_equal(v1, v2[10:])
+    fk, fv = s.factors(3)
+    assert fk.min() >= 0.25 and fk.max() <= 8.0 and not np.array_equal(fk, fv)
