@@ -1,0 +1,291 @@
+"""Decode-attention benchmark on one MI355X.
+
+One step = one decode step of the two 32k-context workloads, every part of
+the hot path through the C ABI:
+  * R-SWA long reference, f32: rswa_decode (ring write + split-K attention +
+    combine) over 10 MHA heads x (32640 reference rows + a full 128-slot ring);
+  * batched GQA q8_2f: kv_append_q8 of one new row per sequence (the
+    quantiser; sequences crossing 64 rows would freeze), then decode_attn_q8
+    over 64 sequences x 8 KV heads (32 Q heads), lengths uniform in
+    [1024, 32768].
+Inputs are seeded synthetic tensors already resident in HBM.  The f32
+caches are rotated over replicas totalling >= 1 GB so the 256 MB Infinity
+Cache cannot serve repeated reads; the q8 cache alone is ~2.3 GB.
+
+Prints ONE JSON line: KV positions/s for the whole step, per-part GB/s and
+fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
+q8 decode) timed with HIP events on its own stream, and the CPU oracle timed
+on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "decode-attn KV positions/s + achieved HBM GB/s (% of peak), f32 and q8"
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--replicas", type=int, default=4, help="f32 R-SWA cache replicas (>= 1 GB total)")
+    p.add_argument("--part", choices=["both", "rswa", "q8"], default="both")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seqs", type=int, default=8)
+    return p.parse_args()
+
+
+def algorithmic_bytes_q8(lens, n_live, hq):
+    rows = int(np.sum(lens)) * n_live
+    return rows * 276 + len(lens) * n_live * 2 * 128 * 4 + len(lens) * hq * 128 * 4 * 2
+
+
+def algorithmic_bytes_rswa(n_rows, heads):
+    # K and V rows read once, q read, out written, the step's K/V read and written once
+    return n_rows * heads * 1024 + heads * 512 * 2 + heads * 512 * 2 * 2
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_internal.h"):
+        h.update(open(os.path.join(ROOT, "int8_kv_cache_decode_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when missing or taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, kernel_tag + "_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from int8_kv_cache_decode_amd import kvq as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    do_rswa = args.part in ("both", "rswa")
+    do_q8 = args.part in ("both", "q8")
+    total_steps = args.warmup + args.steps
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    # ---------------- R-SWA long reference, f32 ----------------
+    rs = workloads.get("rswa_long_f32")
+    rswa = []
+    if do_rswa:
+        rk, rv = rs.reference()
+        rk_d = t(rk.transpose(1, 0, 2))
+        rv_d = t(rv.transpose(1, 0, 2))
+        pool = [tuple(t(x[None]) for x in rs.step(s)) for s in range(16)]
+        for rep in range(args.replicas):
+            c = K.KvCache(K.KIND_F32, 1, rs.n_heads, rs.prefill + rs.window)
+            rings = K.Rings(1)
+            K.kv_append_f32(c, 0, rs.prefill, rk_d, rv_d)
+            K.rswa_record_prefill(c, rings, 0)
+            out = torch.zeros((1, rs.n_heads, 128), device=dev)
+            for s in range(rs.writes - 1):          # reach the steady state (ring full)
+                q, kk, vv = pool[s % 16]
+                K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+            rswa.append((c, rings, out))
+        del rk_d, rv_d
+        torch.cuda.synchronize()
+        log("rswa replicas ready: %d x %.1f MB, ring_len %d ring_pos %d" % (
+            args.replicas, rs.n_heads * (rs.prefill + rs.window) * 1024 / 1e6,
+            rswa[0][1][0].ring_len, rswa[0][1][0].ring_pos))
+
+    # ---------------- batched GQA q8_2f ----------------
+    bq = workloads.get("batched_q8")
+    lens = bq.lengths()
+    if do_q8:
+        from concurrent.futures import ThreadPoolExecutor
+        cq = K.KvCache(K.KIND_Q8, bq.batch, bq.n_kv_heads, int(lens.max()) + total_steps + 64)
+        with ThreadPoolExecutor(16) as ex:
+            for b, (k, v) in enumerate(ex.map(bq.kv_rows, range(bq.batch))):
+                K.kv_append_q8(cq, b, int(lens[b]), t(k), t(v))
+        qq = t(bq.query())
+        qout = torch.zeros((bq.batch, bq.n_q_heads, 128), device=dev)
+        newk = t(workloads.normal_f32(workloads.key(bq.seed, 99), (bq.batch, bq.n_kv_heads, 128)))
+        newv = t(workloads.normal_f32(workloads.key(bq.seed, 98), (bq.batch, bq.n_kv_heads, 128)))
+        ws_q8 = cq.workspace(bq.n_q_heads)
+        torch.cuda.synchronize()
+        log("q8 cache ready: %d rows, %.2f GB stored" % (int(lens.sum()), cq.cache_bytes() / 1e9))
+
+    def step(i):
+        if do_rswa:
+            c, rings, out = rswa[i % len(rswa)]
+            q, kk, vv = pool[i % 16]
+            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+        if do_q8:
+            K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
+            K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # positions attended per step (context rows per sequence)
+    pos_rswa = (rs.prefill + rs.window) if do_rswa else 0
+    pos_q8 = int(cq.len.sum()) if do_q8 else 0
+    positions = pos_rswa + pos_q8
+    value = positions / (ms_per_step / 1e3)
+
+    # ---------------- per-part kernel timing with HIP events ----------------
+    def time_calls(fn, n):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        fn(0)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for i in range(n):
+            fn(i)
+        e.record(stream)
+        e.synchronize()
+        return s.elapsed_time(e) / n * 1e3      # us per call
+
+    parts = {}
+    if do_rswa:
+        def rswa_call(i):
+            c, rings, out = rswa[i % len(rswa)]
+            q, kk, vv = pool[i % 16]
+            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+        us = min(time_calls(rswa_call, 50) for _ in range(3))
+        nb = algorithmic_bytes_rswa(rs.prefill + rs.window, rs.n_heads)
+        parts["rswa_decode_f32"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "kv_positions_per_s": round((rs.prefill + rs.window) / us * 1e6, 1)}
+    if do_q8:
+        def q8_call(i):
+            K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)
+        us = min(time_calls(q8_call, 20) for _ in range(3))
+        nb = algorithmic_bytes_q8(cq.len, cq.n_live, bq.n_q_heads)
+        parts["decode_attn_q8"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "kv_positions_per_s": round(int(cq.len.sum()) / us * 1e6, 1)}
+
+        def app_call(i):
+            K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
+        if int(cq.len.max()) + 40 <= cq.capacity:
+            parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 10), 2)}
+
+    dominant = "decode_attn_q8" if do_q8 else "rswa_decode_f32"
+    kernel_tag = "k_decode_q8_batched_q8" if do_q8 else "k_decode_f32_rswa_long_f32"
+    d = parts[dominant]
+    roofline = {"bound": "hbm", "achieved": d["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac_of_peak"], "traffic": committed_traffic(kernel_tag),
+                "kernel": dominant}
+
+    # ---------------- CPU oracle on the host cores ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, rs, bq, do_rswa, do_q8)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "KV positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32+i8",
+        "data": "synthetic (seeded SplitMix64 / Box-Muller; no datasets or weights)",
+        "config": {"workload": "decode step: " + " + ".join(
+            (["rswa_long_f32 (10 MHA heads x 128, 32640 reference rows + 128-slot ring, f32)"] if do_rswa else [])
+            + (["batched_q8 (64 seqs, 32 Q / 8 KV heads x 128, ctx U[1024,32768], q8_2f, +1 appended row/seq)"]
+               if do_q8 else [])),
+            "positions_per_step": positions, "rswa_replicas": args.replicas if do_rswa else 0},
+        "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, rs, bq, do_rswa, do_q8):
+    """The oracle as it stands, on the host cores: one decode of the R-SWA
+    workload (all 10 heads) and of the first few sequences of the batched q8
+    workload (their q8 storage built by the oracle's own codec first, not
+    timed).  Reported in the same unit, KV positions/s."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    threads = min(16, os.cpu_count() or 1)
+    units_r, q_r, units_q, q_q = None, None, None, None
+    positions = 0
+    if do_rswa:
+        rk, rv = rs.reference()
+        win_k = np.stack([rs.step(s)[1] for s in range(rs.writes - rs.window, rs.writes)])
+        win_v = np.stack([rs.step(s)[2] for s in range(rs.writes - rs.window, rs.writes)])
+        q_r = rs.step(rs.writes - 1)[0][None]
+        units_r = [[("f32", np.concatenate([rk[g], win_k[:, g]]), np.concatenate([rv[g], win_v[:, g]]))
+                    for g in range(rs.n_heads)]]
+        positions += rs.prefill + rs.window
+    if do_q8:
+        nseq = min(args.cpu_sample_seqs, bq.batch)
+        lens = bq.lengths()
+        q_q = bq.query()[:nseq]
+        units_q = []
+        for b in range(nseq):
+            k, v = bq.kv_rows(b)
+
+            def mk(g):
+                h = oracle.Q8Head(cap=int(lens[b]))
+                h.append(k[:, g], v[:, g])
+                return ("q8", h)
+            with ThreadPoolExecutor(threads) as ex:
+                units_q.append(list(ex.map(mk, range(bq.n_kv_heads))))
+        positions += int(lens[:nseq].sum())
+    t0 = time.perf_counter()
+    if units_r is not None:
+        oracle.decode(q_r, units_r, rs.n_heads, threads=threads)
+    if units_q is not None:
+        oracle.decode(q_q, units_q, bq.n_kv_heads, threads=threads)
+    wall = time.perf_counter() - t0
+    sample = []
+    if do_rswa:
+        sample.append("rswa_long_f32: one decode, 10 heads x 32768 rows")
+    if do_q8:
+        sample.append("batched_q8: sequences 0..%d of 64 (%d rows x 8 KV heads x 4 Q heads)"
+                      % (args.cpu_sample_seqs - 1, positions - (rs.prefill + rs.window if do_rswa else 0)))
+    return {"value": round(positions / wall, 1), "unit": "KV positions/s", "cores": threads,
+            "kind": "oracle", "sample": "; ".join(sample) + "; float64 oracle, %.2f s wall" % wall}
+
+
+if __name__ == "__main__":
+    main()

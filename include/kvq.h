@@ -1,0 +1,286 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) decode-attention library over a
+ * head-major f32 or int8 ("q8_2f") KV cache.
+ *
+ * Sources (web pages the operations come from):
+ *   [P1] cortiq-engine 0.3.4, src/cortiq_engine/kv_cache.rs
+ *        (LayerKvCache: head-major storage, quant_row, freeze_cols, append,
+ *         attend, attend_group)
+ *   [P2] cortiq-engine 0.8.49, src/cortiq_engine/kv_cache.rs (same codec)
+ *   [P3] franken_ocr 0.8.0, src/native_engine/rswa.rs
+ *        (RingCache: record_prefill, write_decode_step, decode_attention,
+ *         fold, attention, batched_decode_attention)
+ *
+ * Conventions for every call below
+ *   - Status: 0 (KVQ_OK) on success, a negative KVQ_E* code otherwise; the
+ *     message of the last failure on the calling thread is returned by
+ *     kvq_last_error().
+ *   - All validation happens on the host BEFORE anything is enqueued: a call
+ *     that fails leaves the cache (device buffers and host counters) exactly
+ *     as it was.  The one exception is KVQ_EDEVICE (a launch the HIP runtime
+ *     refused), which is reported after the fact.
+ *   - Ownership: the caller allocates and owns every buffer -- the kvq_cache
+ *     and kvq_ring structs, the host counter arrays they point to, and every
+ *     device buffer (cache storage, q, k_new/v_new, out, workspace).  The
+ *     library never allocates, frees or synchronises.
+ *   - Device pointers are HIP device addresses on the current device.  Calls
+ *     are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     Host counters (len, frozen, ring cursors) are updated when the work is
+ *     enqueued, i.e. they describe the cache as it will be once the stream
+ *     reaches that point.
+ *   - Calls that share a cache, or a workspace, must be ordered (same stream
+ *     or explicit synchronisation); overlapping calls race.
+ *   - Only head_dim == 128 is accepted.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_HEAD_DIM      128   /* channels per head (the only supported value) */
+#define KVQ_K_GROUP       32    /* K channels per scale ([P1] const KV_K_GROUP) */
+#define KVQ_COL_WARMUP    64    /* rows before the column field freezes ([P1] const KV_COL_WARMUP) */
+#define KVQ_RING_WINDOW   128   /* R-SWA ring slots ([P3] const RING_WINDOW) */
+#define KVQ_MAX_KV_HEADS  64
+#define KVQ_ALL_SEQS      (-1)  /* `seq` value: one row for every sequence */
+
+#define KVQ_OK         0
+#define KVQ_EINVAL    (-1)  /* null pointer, bad shape or geometry, unsupported size */
+#define KVQ_ECAPACITY (-2)  /* the rows would not fit in the cache's capacity */
+#define KVQ_ESTATE    (-3)  /* wrong cache kind or state (e.g. ring prefill not recorded) */
+#define KVQ_EDEVICE   (-4)  /* the HIP runtime refused a launch */
+
+#define KVQ_KIND_F32  1
+#define KVQ_KIND_Q8   2
+
+/* Device buffers of a cache, for kvq_buffer_bytes(). */
+#define KVQ_BUF_K     0   /* f32:  float [batch][n_live][capacity][128]            */
+#define KVQ_BUF_V     1   /* f32:  float [batch][n_live][capacity][128]            */
+#define KVQ_BUF_KQ    2   /* q8:   int8  [batch][n_live][capacity][128] (16 B rows) */
+#define KVQ_BUF_KS    3   /* q8:   float [batch][n_live][capacity][4]  (one 16 B record per row) */
+#define KVQ_BUF_VQ    4   /* q8:   int8  [batch][n_live][capacity][128]            */
+#define KVQ_BUF_VS    5   /* q8:   float [batch][n_live][capacity]                 */
+#define KVQ_BUF_KCOL  6   /* q8:   float [batch][n_live][128]                      */
+#define KVQ_BUF_VCOL  7   /* q8:   float [batch][n_live][128]                      */
+
+/*
+ * A per-layer KV cache of `batch` independent sequences ([P1] LayerKvCache,
+ * one per sequence; [P3] BatchedRingCache for the batch dimension).
+ *
+ * Storage is head-major: every (sequence, live KV head) owns `capacity`
+ * contiguous rows of 128 channels ([P1] module doc: one contiguous
+ * [pos x head_dim] block per KV head).  Dead KV heads -- GQA groups whose Q
+ * heads are all masked -- own no storage at all and get no work ([P1] module
+ * doc: masked heads cost neither FLOPs nor memory); live heads are numbered
+ * densely by live_slot.  The alive mask is fixed when the cache is created.
+ *
+ * f32 kind: K and V rows as float.
+ * q8 kind ([P1] KvMode q8_2f): K rows as int8 codes with one f32 scale per
+ * 32 channels, V rows as int8 codes with one f32 scale per row, and per
+ * (sequence, live head) f32 column fields kcol/vcol that are 1 until the
+ * freeze and the per-channel RMS afterwards.  A stored value is
+ *   K^[p][d] = kq[p][d] * ks[p][d/32] * kcol[d],
+ *   V^[p][d] = vq[p][d] * vs[p] * vcol[d].
+ *
+ * Fill it with kvq_cache_init(), then set the device pointers of the kind's
+ * buffers (sizes from kvq_buffer_bytes(); every base must be 16-byte
+ * aligned).  `len` and `frozen` point to caller-owned host arrays of `batch`
+ * entries that the library keeps up to date.
+ */
+typedef struct kvq_cache {
+    int32_t kind;            /* KVQ_KIND_F32 or KVQ_KIND_Q8 */
+    int32_t batch;           /* sequences */
+    int32_t n_kv_heads;      /* KV heads, dead ones included */
+    int32_t head_dim;        /* 128 */
+    int32_t capacity;        /* rows per (sequence, live head) */
+    int32_t n_live;          /* live KV heads (set by kvq_cache_init) */
+    int8_t  live_slot[KVQ_MAX_KV_HEADS];  /* storage slot of KV head g, -1 if dead */
+    int32_t* len;            /* host [batch]: rows appended per sequence */
+    uint8_t* frozen;         /* host [batch]: q8 column field frozen (0/1) */
+    float*   k;              /* KVQ_BUF_K */
+    float*   v;              /* KVQ_BUF_V */
+    int8_t*  kq;             /* KVQ_BUF_KQ */
+    float*   ks;             /* KVQ_BUF_KS */
+    int8_t*  vq;             /* KVQ_BUF_VQ */
+    float*   vs;             /* KVQ_BUF_VS */
+    float*   kcol;           /* KVQ_BUF_KCOL */
+    float*   vcol;           /* KVQ_BUF_VCOL */
+} kvq_cache;
+
+/*
+ * R-SWA cursors of one sequence ([P3] RingCache fields prefill_len,
+ * ring_len, ring_pos, decode_writes).  The sequence's rows are the read-only
+ * reference block [0, prefill_len) followed by a ring of KVQ_RING_WINDOW
+ * slots stored at rows [prefill_len, prefill_len + 128).
+ */
+typedef struct kvq_ring {
+    int32_t prefill_len;     /* -1 until recorded */
+    int32_t ring_len;        /* live ring slots, 0..128 */
+    int32_t ring_pos;        /* next slot to overwrite once the ring is full */
+    int32_t reserved;
+    int64_t writes;          /* ring writes since the prefill was recorded */
+} kvq_ring;
+
+/*
+ * Fill `c` for a new, empty cache: geometry, live-slot numbering from
+ * `alive` (host [n_kv_heads], nonzero = live; NULL = all live), len[] = 0,
+ * frozen[] = 0, device pointers NULL.  `len_host` and `frozen_host` are
+ * caller-owned host arrays of `batch` entries and must outlive the cache.
+ * Errors: KVQ_EINVAL (kind, head_dim != 128, batch/capacity < 1,
+ * n_kv_heads outside 1..64, null arrays).
+ */
+int kvq_cache_init(kvq_cache* c, int kind, int batch, int n_kv_heads, int head_dim,
+                   int capacity, const uint8_t* alive, int32_t* len_host,
+                   uint8_t* frozen_host);
+
+/* Bytes of device buffer `which` (KVQ_BUF_*) for this cache's geometry;
+ * 0 for a buffer the kind does not use or an invalid argument. */
+size_t kvq_buffer_bytes(const kvq_cache* c, int which);
+
+/*
+ * Bytes the stored rows occupy at the current lengths ([P1]
+ * LayerKvCache::memory_bytes restricted to K/V storage): per (row, live
+ * head) 2*4*128 = 1024 B for f32, 128 + 16 + 128 + 4 = 276 B for q8, plus
+ * 2*4*128 B of column fields per live head of a frozen q8 sequence.
+ */
+size_t kvq_cache_bytes(const kvq_cache* c);
+
+/*
+ * kv_append_f32 -- [P1] LayerKvCache::append (f32 mode); [P3]
+ * RingCache::record_prefill is this call followed by rswa_record_prefill.
+ *
+ * Appends `n_rows` rows to sequence `seq`: k_new/v_new are device float
+ * [n_rows][n_kv_heads][128] (every KV head's values, dead ones included and
+ * ignored).  Rows land at positions len[seq] .. len[seq]+n_rows-1 of every
+ * live head; len[seq] += n_rows.
+ * seq == KVQ_ALL_SEQS appends ONE row to every sequence: n_rows must be 1 and
+ * k_new/v_new are [batch][n_kv_heads][128].
+ * n_rows == 0 is a no-op.
+ * Errors: KVQ_EINVAL (null, seq out of range, negative n_rows, missing
+ * buffers), KVQ_ESTATE (not an f32 cache), KVQ_ECAPACITY (len + n_rows >
+ * capacity for any affected sequence).
+ */
+int kv_append_f32(kvq_cache* c, int seq, int n_rows, const float* k_new,
+                  const float* v_new, void* stream);
+
+/*
+ * kv_append_q8 -- [P1] LayerKvCache::append (q8_2f mode) with
+ * [P1] quant_row, freezing through kv_freeze_col_and_requant exactly when
+ * the page does.
+ *
+ * Same arguments and layout as kv_append_f32.  Each row is appended as if
+ * alone, in order: at the start of appending a row to a sequence that holds
+ * >= 64 rows and is not frozen, that sequence is frozen first (so rows
+ * 0..63 are requantised and row 64 is the first one quantised against the
+ * field).  A row r is quantised per live head as
+ *   resid[d] = r[d] / col[d]            (col = 1 before the freeze),
+ *   per group (32 channels for K, all 128 for V):
+ *     s = max(max_d |resid[d]| / 127, 1e-12),
+ *     code[d] = clamp(round_half_away(resid[d] / s), -127, 127),
+ * in IEEE f32 with one rounding per operation.
+ * Errors: as kv_append_f32, with KVQ_ESTATE for a non-q8 cache.
+ */
+int kv_append_q8(kvq_cache* c, int seq, int n_rows, const float* k_new,
+                 const float* v_new, void* stream);
+
+/*
+ * kv_freeze_col_and_requant -- [P1] LayerKvCache::freeze_cols for one
+ * sequence (seq == KVQ_ALL_SEQS: every sequence).
+ *
+ * For every live head, separately for K (group 32) and V (group 128), over
+ * the n = len[seq] stored rows: x^ = f32(code) * scale; col[d] =
+ * max(sqrtf((sum_p x^[p][d]^2) / n), 1e-6) with the sum taken in row order
+ * in f32, multiply then add; every row is then requantised from x^ against
+ * col.  Sets frozen[seq].  No-op for a sequence that is already frozen or
+ * empty.  kv_append_q8 calls it by itself at row 64; calling it earlier
+ * freezes the field over the rows stored so far.
+ * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not a q8 cache).
+ */
+int kv_freeze_col_and_requant(kvq_cache* c, int seq, void* stream);
+
+/*
+ * Bytes of workspace the decode calls need for this cache with n_q_heads
+ * query heads (independent of the current lengths).  The workspace holds
+ * per-chunk partial softmax states; its contents need no initialisation.
+ * Returns 0 on invalid arguments.
+ */
+size_t kvq_workspace_bytes(const kvq_cache* c, int n_q_heads);
+
+/*
+ * decode_attn_f32 -- single-query decode attention over every sequence of
+ * an f32 cache: [P1] attend_group (GQA, each stored row read once per
+ * group) and attend (per-head semantics); [P3] decode_attention_scalar_head
+ * and fold (online softmax, never materialising the score row).
+ *
+ * q   device float [batch][n_q_heads][128]
+ * out device float [batch][n_q_heads][128]
+ * Q head h reads KV head g = h / (n_q_heads / n_kv_heads).  For a live g:
+ *   out[b][h] = sum_p softmax_p(q[b][h] . K[b][g][p] / sqrt(128)) V[b][g][p]
+ * over the len[b] stored rows, with no mask.  Q heads of dead groups, and
+ * of sequences with no rows, get out = 0 ([P1] attend_group: stored == 0).
+ * Results are f32; the summation order differs from the pages' serial loops.
+ * ws/ws_bytes: device workspace of at least kvq_workspace_bytes().
+ * Errors: KVQ_EINVAL (null, n_q_heads not a multiple of n_kv_heads, group
+ * size n_q_heads/n_kv_heads not in {1, 2, 4, 8}, workspace too small),
+ * KVQ_ESTATE (not an f32 cache).
+ */
+int decode_attn_f32(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * decode_attn_q8 -- decode_attn_f32 over a q8 cache: [P1] attend (q8
+ * branch) / attend_group, where a score is (1/sqrt(128)) * sum over K groups
+ * of ks * <q (.) kcol, kq> and the output is (sum_p w_p vs_p vq_p) (.) vcol.
+ * The query stays f32 (it is never quantised).  Same arguments, layout and
+ * errors as decode_attn_f32 (KVQ_ESTATE for a non-q8 cache).
+ */
+int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rswa_record_prefill -- [P3] RingCache::record_prefill for sequence `seq`
+ * of an f32 cache whose reference block has just been appended with
+ * kv_append_f32: prefill_len = len[seq], ring_len = ring_pos = writes = 0.
+ * rings: host array [batch].  A prefill of 0 rows is allowed.
+ * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not an f32 cache),
+ * KVQ_ECAPACITY (len[seq] + 128 > capacity: no room for the ring).
+ */
+int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
+
+/*
+ * rswa_decode -- one R-SWA decode step for every sequence of an f32 cache:
+ * [P3] attention() = write_decode_step() then decode_attention().
+ *
+ * k_new, v_new  device float [batch][n_kv_heads][128]: this step's K/V
+ * q             device float [batch][n_q_heads][128]
+ * out           device float [batch][n_q_heads][128]
+ * For each sequence b the step's K/V go to ring slot
+ *   slot = ring_len            while ring_len < 128 (warm-up; ring_len += 1,
+ *                              ring_pos = ring_len mod 128),
+ *   slot = ring_pos            once full (ring_pos = (ring_pos + 1) mod 128),
+ * i.e. to cache row prefill_len + slot, overwriting in place; then the query
+ * attends, with NO causal mask, over rows [0, prefill_len + ring_len) --
+ * the reference block and every live ring slot, itself included.  len[b]
+ * becomes prefill_len + ring_len.  The reference rows are never written.
+ * Errors: KVQ_EINVAL (null, bad group size, workspace too small),
+ * KVQ_ESTATE (not an f32 cache, or a sequence whose prefill was not
+ * recorded, or whose len no longer matches its ring cursors),
+ * KVQ_ECAPACITY (prefill_len + 128 > capacity).
+ */
+int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q,
+                const float* k_new, const float* v_new, float* out,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

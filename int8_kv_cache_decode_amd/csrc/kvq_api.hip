@@ -1,0 +1,499 @@
+// kvq_api.hip -- the C ABI declared in include/kvq.h: host-side validation,
+// work partitioning and kernel launches.  Every check runs before anything
+// is enqueued, so a refused call leaves the cache untouched ([P3]
+// franken_ocr 0.8.0 rswa.rs: malformed steps are refused before any K/V
+// write; record_prefill / write_decode_step validate first).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Geometry checks shared by every call; `kind` 0 accepts either kind.
+int check_cache(const kvq_cache* c, int kind, const char* fn) {
+    if (!c) return fail(KVQ_EINVAL, "%s: null cache", fn);
+    if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_EINVAL, "%s: head_dim %d != 128", fn, c->head_dim);
+    if (c->batch < 1 || c->capacity < 1) return fail(KVQ_EINVAL, "%s: batch %d / capacity %d must be >= 1", fn, c->batch, c->capacity);
+    if (c->n_kv_heads < 1 || c->n_kv_heads > KVQ_MAX_KV_HEADS)
+        return fail(KVQ_EINVAL, "%s: n_kv_heads %d outside 1..%d", fn, c->n_kv_heads, KVQ_MAX_KV_HEADS);
+    int live = 0;
+    for (int g = 0; g < c->n_kv_heads; ++g) {
+        if (c->live_slot[g] >= 0) {
+            if (c->live_slot[g] != live) return fail(KVQ_EINVAL, "%s: live_slot table is not dense", fn);
+            ++live;
+        }
+    }
+    if (live != c->n_live) return fail(KVQ_EINVAL, "%s: n_live %d does not match live_slot", fn, c->n_live);
+    if (!c->len || !c->frozen) return fail(KVQ_EINVAL, "%s: null host len/frozen arrays", fn);
+    if (kind && c->kind != kind)
+        return fail(KVQ_ESTATE, "%s: cache kind %d, this call needs kind %d", fn, c->kind, kind);
+    if (c->kind == KVQ_KIND_F32) {
+        if (!c->k || !c->v) return fail(KVQ_EINVAL, "%s: f32 cache without k/v buffers", fn);
+        if (!aligned16(c->k) || !aligned16(c->v)) return fail(KVQ_EINVAL, "%s: k/v not 16-byte aligned", fn);
+    } else if (c->kind == KVQ_KIND_Q8) {
+        if (!c->kq || !c->ks || !c->vq || !c->vs || !c->kcol || !c->vcol)
+            return fail(KVQ_EINVAL, "%s: q8 cache with a missing buffer", fn);
+        if (!aligned16(c->kq) || !aligned16(c->ks) || !aligned16(c->vq) || !aligned16(c->vs) ||
+            !aligned16(c->kcol) || !aligned16(c->vcol))
+            return fail(KVQ_EINVAL, "%s: q8 buffers not 16-byte aligned", fn);
+    } else {
+        return fail(KVQ_EINVAL, "%s: unknown cache kind %d", fn, c->kind);
+    }
+    for (int b = 0; b < c->batch; ++b)
+        if (c->len[b] < 0 || c->len[b] > c->capacity)
+            return fail(KVQ_ESTATE, "%s: len[%d] = %d outside 0..capacity", fn, b, c->len[b]);
+    return KVQ_OK;
+}
+
+void fill_live(const kvq_cache* c, int8_t* live_head) {
+    for (int g = 0; g < c->n_kv_heads; ++g)
+        if (c->live_slot[g] >= 0) live_head[c->live_slot[g]] = (int8_t)g;
+}
+
+int device_status(hipError_t e, const char* fn) {
+    if (e != hipSuccess) return fail(KVQ_EDEVICE, "%s: %s", fn, hipGetErrorString(e));
+    return KVQ_OK;
+}
+
+// ---- append ---------------------------------------------------------------
+struct Seg {
+    int seq, src_row0, dst_row0, n;
+    bool frozen;
+};
+
+AppendArgs base_append(const kvq_cache* c, const float* k_new, const float* v_new) {
+    AppendArgs a;
+    memset(&a, 0, sizeof a);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k = c->k;
+    a.v = c->v;
+    a.kq = c->kq;
+    a.ks = c->ks;
+    a.vq = c->vq;
+    a.vs = c->vs;
+    a.kcol = c->kcol;
+    a.vcol = c->vcol;
+    a.n_kv_heads = c->n_kv_heads;
+    a.n_live = c->n_live;
+    a.capacity = c->capacity;
+    fill_live(c, a.live_head);
+    return a;
+}
+
+// Launch equal-length segments (same n) in batches of kSeqPerLaunch.
+int launch_segments(const kvq_cache* c, const float* k_new, const float* v_new,
+                    const std::vector<Seg>& segs, bool q8, hipStream_t s, const char* fn) {
+    if (c->n_live == 0) return KVQ_OK;
+    size_t i = 0;
+    while (i < segs.size()) {
+        AppendArgs a = base_append(c, k_new, v_new);
+        const int n = segs[i].n;
+        int ns = 0;
+        while (i < segs.size() && ns < kSeqPerLaunch && segs[i].n == n) {
+            a.seq[ns] = segs[i].seq;
+            a.src_row0[ns] = segs[i].src_row0;
+            a.dst_row0[ns] = segs[i].dst_row0;
+            a.frozen[ns] = segs[i].frozen ? 1 : 0;
+            ++ns;
+            ++i;
+        }
+        a.n_seq = ns;
+        if (n == 0) continue;
+        const int rc = device_status(q8 ? launch_append_q8(a, n, s) : launch_append_f32(a, n, s), fn);
+        if (rc) return rc;
+    }
+    return KVQ_OK;
+}
+
+int launch_freeze_list(const kvq_cache* c, const std::vector<std::pair<int, int>>& list,
+                       hipStream_t s, const char* fn) {
+    if (c->n_live == 0) return KVQ_OK;
+    for (size_t i = 0; i < list.size(); i += kSeqPerLaunch) {
+        FreezeArgs f;
+        memset(&f, 0, sizeof f);
+        f.kq = c->kq;
+        f.ks = c->ks;
+        f.vq = c->vq;
+        f.vs = c->vs;
+        f.kcol = c->kcol;
+        f.vcol = c->vcol;
+        f.n_live = c->n_live;
+        f.capacity = c->capacity;
+        f.n_seq = (int)std::min<size_t>(kSeqPerLaunch, list.size() - i);
+        for (int j = 0; j < f.n_seq; ++j) {
+            f.seq[j] = list[i + j].first;
+            f.n[j] = list[i + j].second;
+        }
+        const int rc = device_status(launch_freeze(f, s), fn);
+        if (rc) return rc;
+    }
+    return KVQ_OK;
+}
+
+int check_append_args(const kvq_cache* c, int seq, int n_rows, const float* k_new,
+                      const float* v_new, const char* fn) {
+    if (seq == KVQ_ALL_SEQS) {
+        if (n_rows != 1) return fail(KVQ_EINVAL, "%s: seq=ALL appends exactly one row (n_rows=%d)", fn, n_rows);
+        for (int b = 0; b < c->batch; ++b)
+            if (c->len[b] + 1 > c->capacity)
+                return fail(KVQ_ECAPACITY, "%s: sequence %d is full (len %d, capacity %d)", fn, b, c->len[b], c->capacity);
+    } else {
+        if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+        if (n_rows < 0) return fail(KVQ_EINVAL, "%s: n_rows %d < 0", fn, n_rows);
+        if ((int64_t)c->len[seq] + n_rows > c->capacity)
+            return fail(KVQ_ECAPACITY, "%s: len %d + n_rows %d exceeds capacity %d", fn, c->len[seq], n_rows, c->capacity);
+    }
+    if (n_rows > 0 && (!k_new || !v_new)) return fail(KVQ_EINVAL, "%s: null k_new/v_new", fn);
+    if (n_rows > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(KVQ_EINVAL, "%s: k_new/v_new not 16-byte aligned", fn);
+    return KVQ_OK;
+}
+
+// ---- decode ---------------------------------------------------------------
+size_t max_items(const kvq_cache* c) {
+    return (size_t)kTargetItems + (size_t)std::min(c->batch, kSeqPerLaunch) * (size_t)c->n_live;
+}
+
+size_t ws_need(const kvq_cache* c, int hpk) {
+    const size_t items = max_items(c);
+    size_t bytes = items * hpk * kHD * sizeof(float) + items * hpk * 2 * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int check_decode_args(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                      void* ws, size_t ws_bytes, const char* fn, int* hpk_out) {
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "%s: n_q_heads %d is not a multiple of n_kv_heads %d", fn, n_q_heads, c->n_kv_heads);
+    const int hpk = n_q_heads / c->n_kv_heads;
+    if (hpk != 1 && hpk != 2 && hpk != 4 && hpk != 8)
+        return fail(KVQ_EINVAL, "%s: group size %d not in {1,2,4,8}", fn, hpk);
+    if (!q || !out) return fail(KVQ_EINVAL, "%s: null q/out", fn);
+    if (!aligned16(q) || !aligned16(out)) return fail(KVQ_EINVAL, "%s: q/out not 16-byte aligned", fn);
+    if (!ws) return fail(KVQ_EINVAL, "%s: null workspace", fn);
+    if (!aligned16(ws)) return fail(KVQ_EINVAL, "%s: workspace not 16-byte aligned", fn);
+    const size_t need = ws_need(c, hpk);
+    if (ws_bytes < need) return fail(KVQ_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    *hpk_out = hpk;
+    return KVQ_OK;
+}
+
+// Partition and launch one decode over every sequence.  lens: rows attended
+// per sequence; wrows: R-SWA row fed from k_new/v_new (or null).
+int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float* out, void* ws,
+               const int32_t* lens, const int32_t* wrows, const float* k_new, const float* v_new,
+               hipStream_t s, const char* fn) {
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.out = out;
+    a.k = c->k;
+    a.v = c->v;
+    a.kq = c->kq;
+    a.ks = c->ks;
+    a.vq = c->vq;
+    a.vs = c->vs;
+    a.kcol = c->kcol;
+    a.vcol = c->vcol;
+    a.ws_acc = (float*)ws;
+    a.ws_ml = (float*)ws + max_items(c) * hpk * kHD;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_store = c->k;
+    a.v_store = c->v;
+    a.n_kv_heads = c->n_kv_heads;
+    a.n_live = c->n_live;
+    a.n_q_heads = n_q_heads;
+    a.hpk = hpk;
+    a.capacity = c->capacity;
+    fill_live(c, a.live_head);
+    memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
+    for (int s0 = 0; s0 < c->batch; s0 += kSeqPerLaunch) {
+        const int ns = std::min(kSeqPerLaunch, c->batch - s0);
+        int64_t total = 0;
+        for (int j = 0; j < ns; ++j) total += (int64_t)lens[s0 + j] * c->n_live;
+        int64_t chunk = (total + kTargetItems - 1) / kTargetItems;
+        chunk = (chunk + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        chunk = std::max<int64_t>(chunk, kChunkMin);
+        a.chunk = (int)chunk;
+        a.seq0 = s0;
+        a.n_seq = ns;
+        int items = 0;
+        for (int j = 0; j < ns; ++j) {
+            const int L = lens[s0 + j];
+            a.len[j] = L;
+            a.nchunk[j] = (int)((L + chunk - 1) / chunk);
+            a.wrow[j] = wrows ? wrows[s0 + j] : -1;
+            a.frozen[j] = c->frozen[s0 + j] ? 1 : 0;
+            a.item_base[j] = items;
+            items += a.nchunk[j] * c->n_live;
+        }
+        a.item_base[ns] = items;
+        a.n_items = items;
+        const hipError_t e = (c->kind == KVQ_KIND_Q8) ? launch_decode_q8(a, s) : launch_decode_f32(a, s);
+        const int rc = device_status(e, fn);
+        if (rc) return rc;
+    }
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_cache_init(kvq_cache* c, int kind, int batch, int n_kv_heads, int head_dim, int capacity,
+                   const uint8_t* alive, int32_t* len_host, uint8_t* frozen_host) {
+    const char* fn = "kvq_cache_init";
+    if (!c) return fail(KVQ_EINVAL, "%s: null cache", fn);
+    if (kind != KVQ_KIND_F32 && kind != KVQ_KIND_Q8) return fail(KVQ_EINVAL, "%s: unknown kind %d", fn, kind);
+    if (head_dim != KVQ_HEAD_DIM) return fail(KVQ_EINVAL, "%s: head_dim %d != 128", fn, head_dim);
+    if (batch < 1 || capacity < 1) return fail(KVQ_EINVAL, "%s: batch/capacity must be >= 1", fn);
+    if (n_kv_heads < 1 || n_kv_heads > KVQ_MAX_KV_HEADS)
+        return fail(KVQ_EINVAL, "%s: n_kv_heads %d outside 1..%d", fn, n_kv_heads, KVQ_MAX_KV_HEADS);
+    if (!len_host || !frozen_host) return fail(KVQ_EINVAL, "%s: null len/frozen host arrays", fn);
+    memset(c, 0, sizeof *c);
+    c->kind = kind;
+    c->batch = batch;
+    c->n_kv_heads = n_kv_heads;
+    c->head_dim = head_dim;
+    c->capacity = capacity;
+    for (int g = 0; g < KVQ_MAX_KV_HEADS; ++g) c->live_slot[g] = -1;
+    int live = 0;
+    for (int g = 0; g < n_kv_heads; ++g)
+        if (!alive || alive[g]) c->live_slot[g] = (int8_t)live++;
+    c->n_live = live;
+    c->len = len_host;
+    c->frozen = frozen_host;
+    for (int b = 0; b < batch; ++b) {
+        len_host[b] = 0;
+        frozen_host[b] = 0;
+    }
+    return KVQ_OK;
+}
+
+size_t kvq_buffer_bytes(const kvq_cache* c, int which) {
+    if (!c || c->head_dim != KVQ_HEAD_DIM || c->batch < 1 || c->capacity < 1) return 0;
+    const size_t rows = (size_t)c->batch * c->n_live * c->capacity;
+    const size_t heads = (size_t)c->batch * c->n_live;
+    const bool f32 = c->kind == KVQ_KIND_F32, q8 = c->kind == KVQ_KIND_Q8;
+    switch (which) {
+        case KVQ_BUF_K:
+        case KVQ_BUF_V: return f32 ? rows * kHD * sizeof(float) : 0;
+        case KVQ_BUF_KQ:
+        case KVQ_BUF_VQ: return q8 ? rows * kHD : 0;
+        case KVQ_BUF_KS: return q8 ? rows * kKScales * sizeof(float) : 0;
+        case KVQ_BUF_VS: return q8 ? rows * sizeof(float) : 0;
+        case KVQ_BUF_KCOL:
+        case KVQ_BUF_VCOL: return q8 ? heads * kHD * sizeof(float) : 0;
+        default: return 0;
+    }
+}
+
+size_t kvq_cache_bytes(const kvq_cache* c) {
+    if (!c || !c->len || !c->frozen) return 0;
+    size_t bytes = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        const size_t rows = (size_t)c->len[b] * c->n_live;
+        if (c->kind == KVQ_KIND_F32) {
+            bytes += rows * 2 * kHD * sizeof(float);
+        } else {
+            bytes += rows * (kHD + kKScales * sizeof(float) + kHD + sizeof(float));
+            if (c->frozen[b]) bytes += (size_t)c->n_live * 2 * kHD * sizeof(float);
+        }
+    }
+    return bytes;
+}
+
+int kv_append_f32(kvq_cache* c, int seq, int n_rows, const float* k_new, const float* v_new,
+                  void* stream) {
+    const char* fn = "kv_append_f32";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if ((rc = check_append_args(c, seq, n_rows, k_new, v_new, fn))) return rc;
+    std::vector<Seg> segs;
+    if (seq == KVQ_ALL_SEQS) {
+        for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, c->len[b], 1, false});
+    } else if (n_rows > 0) {
+        segs.push_back({seq, 0, c->len[seq], n_rows, false});
+    }
+    if ((rc = launch_segments(c, k_new, v_new, segs, false, (hipStream_t)stream, fn))) return rc;
+    for (const Seg& sg : segs) c->len[sg.seq] += sg.n;
+    return KVQ_OK;
+}
+
+int kv_append_q8(kvq_cache* c, int seq, int n_rows, const float* k_new, const float* v_new,
+                 void* stream) {
+    const char* fn = "kv_append_q8";
+    int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    if ((rc = check_append_args(c, seq, n_rows, k_new, v_new, fn))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (seq == KVQ_ALL_SEQS) {
+        // Sequences holding >= 64 rows and not frozen freeze before the row.
+        std::vector<std::pair<int, int>> fl;
+        for (int b = 0; b < c->batch; ++b)
+            if (!c->frozen[b] && c->len[b] >= KVQ_COL_WARMUP) fl.push_back({b, c->len[b]});
+        if ((rc = launch_freeze_list(c, fl, s, fn))) return rc;
+        for (auto& f : fl) c->frozen[f.first] = 1;
+        std::vector<Seg> segs;
+        for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, c->len[b], 1, c->frozen[b] != 0});
+        if ((rc = launch_segments(c, k_new, v_new, segs, true, s, fn))) return rc;
+        for (int b = 0; b < c->batch; ++b) c->len[b] += 1;
+        return KVQ_OK;
+    }
+    if (n_rows == 0) return KVQ_OK;
+    const int L = c->len[seq];
+    if (c->frozen[seq] || L + n_rows <= KVQ_COL_WARMUP) {
+        std::vector<Seg> one{{seq, 0, L, n_rows, c->frozen[seq] != 0}};
+        if ((rc = launch_segments(c, k_new, v_new, one, true, s, fn))) return rc;
+        c->len[seq] = L + n_rows;
+        return KVQ_OK;
+    }
+    // The chunk reaches a row appended while >= 64 rows are stored: rows up
+    // to 64 go in unfrozen, then the freeze, then the rest against the field.
+    const int n1 = std::max(0, KVQ_COL_WARMUP - L);
+    if (n1 > 0) {
+        std::vector<Seg> first{{seq, 0, L, n1, false}};
+        if ((rc = launch_segments(c, k_new, v_new, first, true, s, fn))) return rc;
+        c->len[seq] = L + n1;
+    }
+    std::vector<std::pair<int, int>> fl{{seq, c->len[seq]}};
+    if ((rc = launch_freeze_list(c, fl, s, fn))) return rc;
+    c->frozen[seq] = 1;
+    std::vector<Seg> rest{{seq, n1, c->len[seq], n_rows - n1, true}};
+    if ((rc = launch_segments(c, k_new, v_new, rest, true, s, fn))) return rc;
+    c->len[seq] = L + n_rows;
+    return KVQ_OK;
+}
+
+int kv_freeze_col_and_requant(kvq_cache* c, int seq, void* stream) {
+    const char* fn = "kv_freeze_col_and_requant";
+    int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    if (seq != KVQ_ALL_SEQS && (seq < 0 || seq >= c->batch))
+        return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    std::vector<std::pair<int, int>> fl;
+    for (int b = 0; b < c->batch; ++b) {
+        if (seq != KVQ_ALL_SEQS && b != seq) continue;
+        if (!c->frozen[b] && c->len[b] > 0) fl.push_back({b, c->len[b]});
+    }
+    if ((rc = launch_freeze_list(c, fl, (hipStream_t)stream, fn))) return rc;
+    for (auto& f : fl) c->frozen[f.first] = 1;
+    return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_cache* c, int n_q_heads) {
+    if (!c || c->n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % c->n_kv_heads) return 0;
+    return ws_need(c, n_q_heads / c->n_kv_heads);
+}
+
+int decode_attn_f32(const kvq_cache* c, int n_q_heads, const float* q, float* out, void* ws,
+                    size_t ws_bytes, void* stream) {
+    const char* fn = "decode_attn_f32";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr,
+                      (hipStream_t)stream, fn);
+}
+
+int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out, void* ws,
+                   size_t ws_bytes, void* stream) {
+    const char* fn = "decode_attn_q8";
+    int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr,
+                      (hipStream_t)stream, fn);
+}
+
+int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq) {
+    const char* fn = "rswa_record_prefill";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (!rings) return fail(KVQ_EINVAL, "%s: null rings", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if ((int64_t)c->len[seq] + KVQ_RING_WINDOW > c->capacity)
+        return fail(KVQ_ECAPACITY, "%s: prefill %d + ring %d exceeds capacity %d", fn, c->len[seq],
+                    KVQ_RING_WINDOW, c->capacity);
+    rings[seq].prefill_len = c->len[seq];
+    rings[seq].ring_len = 0;
+    rings[seq].ring_pos = 0;
+    rings[seq].reserved = 0;
+    rings[seq].writes = 0;
+    return KVQ_OK;
+}
+
+int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, const float* k_new,
+                const float* v_new, float* out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "rswa_decode";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    if (!rings) return fail(KVQ_EINVAL, "%s: null rings", fn);
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "%s: null k_new/v_new", fn);
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KVQ_EINVAL, "%s: k_new/v_new not 16-byte aligned", fn);
+    std::vector<int32_t> lens(c->batch), wrows(c->batch);
+    std::vector<kvq_ring> next(rings, rings + c->batch);
+    for (int b = 0; b < c->batch; ++b) {
+        kvq_ring& r = next[b];
+        if (r.prefill_len < 0) return fail(KVQ_ESTATE, "%s: sequence %d: decode before record_prefill", fn, b);
+        if ((int64_t)r.prefill_len + KVQ_RING_WINDOW > c->capacity)
+            return fail(KVQ_ECAPACITY, "%s: sequence %d: prefill %d + ring exceeds capacity %d", fn, b,
+                        r.prefill_len, c->capacity);
+        if (r.ring_len < 0 || r.ring_len > KVQ_RING_WINDOW || r.ring_pos < 0 || r.ring_pos >= KVQ_RING_WINDOW)
+            return fail(KVQ_ESTATE, "%s: sequence %d: corrupt ring cursors", fn, b);
+        if (c->len[b] != r.prefill_len + r.ring_len)
+            return fail(KVQ_ESTATE, "%s: sequence %d: len %d != prefill %d + ring %d (appended since record?)", fn,
+                        b, c->len[b], r.prefill_len, r.ring_len);
+        int slot;
+        if (r.ring_len < KVQ_RING_WINDOW) {   // warm-up: append, no eviction
+            slot = r.ring_len;
+            r.ring_len += 1;
+            r.ring_pos = r.ring_len % KVQ_RING_WINDOW;
+        } else {                              // steady state: overwrite in place
+            slot = r.ring_pos;
+            r.ring_pos = (r.ring_pos + 1) % KVQ_RING_WINDOW;
+        }
+        r.writes += 1;
+        wrows[b] = r.prefill_len + slot;
+        lens[b] = r.prefill_len + r.ring_len;
+    }
+    if ((rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new,
+                         (hipStream_t)stream, fn)))
+        return rc;
+    for (int b = 0; b < c->batch; ++b) {
+        rings[b] = next[b];
+        c->len[b] = lens[b];
+    }
+    return KVQ_OK;
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// kvq_internal.h -- argument blocks and launchers shared by the library's
+// host code (kvq_api.hip) and its kernels (kvq_codec.hip, kvq_decode.hip).
+//
+// Per-sequence values (lengths, destination rows, ring rows, work offsets)
+// travel inside the kernel-argument block, so a call never has to stage a
+// table in device memory.  One launch covers at most kSeqPerLaunch
+// sequences; larger batches are processed in consecutive launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kHD = KVQ_HEAD_DIM;           // channels per head
+constexpr int kKGroup = KVQ_K_GROUP;        // K channels per scale
+constexpr int kKScales = kHD / kKGroup;     // K scales per row (4)
+constexpr int kSeqPerLaunch = 128;
+
+// Work split of the decode kernels: a (sequence, live KV head) row range is
+// cut into chunks of `chunk` rows, one workgroup per chunk.  The chunk is the
+// smallest multiple of kChunkAlign (and at least kChunkMin) that keeps the
+// number of chunks of a launch near kTargetItems.
+#ifndef KVQ_TARGET_ITEMS
+#define KVQ_TARGET_ITEMS 4096
+#endif
+#ifndef KVQ_CHUNK_MIN
+#define KVQ_CHUNK_MIN 64
+#endif
+constexpr int kTargetItems = KVQ_TARGET_ITEMS;
+constexpr int kChunkMin = KVQ_CHUNK_MIN;
+constexpr int kChunkAlign = 64;
+
+// ---- codec ---------------------------------------------------------------
+struct AppendArgs {
+    const float* k_new;        // source rows [src_row][n_kv_heads][128]
+    const float* v_new;
+    float* k;                  // f32 cache storage
+    float* v;
+    int8_t* kq;                // q8 cache storage
+    float* ks;
+    int8_t* vq;
+    float* vs;
+    const float* kcol;
+    const float* vcol;
+    int n_kv_heads;
+    int n_live;
+    int capacity;
+    int n_seq;                 // sequences in this launch
+    int8_t live_head[KVQ_MAX_KV_HEADS];      // KV head of live slot
+    int32_t seq[kSeqPerLaunch];              // absolute sequence index
+    int32_t src_row0[kSeqPerLaunch];         // first source row of the sequence
+    int32_t dst_row0[kSeqPerLaunch];         // first destination row
+    int32_t frozen[kSeqPerLaunch];           // q8: quantise against the column field
+};
+
+struct FreezeArgs {
+    int8_t* kq;
+    float* ks;
+    int8_t* vq;
+    float* vs;
+    float* kcol;
+    float* vcol;
+    int n_live;
+    int capacity;
+    int n_seq;
+    int32_t seq[kSeqPerLaunch];
+    int32_t n[kSeqPerLaunch];                // rows to freeze over
+};
+
+// grid (n_rows, n_seq, n_live)
+hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s);
+hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s);
+// grid (n_live, n_seq)
+hipError_t launch_freeze(const FreezeArgs& a, hipStream_t s);
+
+// ---- decode --------------------------------------------------------------
+struct DecodeArgs {
+    const float* q;            // [batch][n_q_heads][128]
+    float* out;                // [batch][n_q_heads][128]
+    const float* k;            // f32 storage
+    const float* v;
+    const int8_t* kq;          // q8 storage
+    const float* ks;
+    const int8_t* vq;
+    const float* vs;
+    const float* kcol;
+    const float* vcol;
+    float* ws_acc;             // [items][hpk][128] partial weighted V sums
+    float* ws_ml;              // [items][hpk][2]   partial (max, sum) in log2 units
+    const float* k_new;        // R-SWA step K/V [batch][n_kv_heads][128] (or null)
+    const float* v_new;
+    float* k_store;            // writable f32 storage for the ring write
+    float* v_store;
+    int n_kv_heads;
+    int n_live;
+    int n_q_heads;
+    int hpk;
+    int capacity;
+    int chunk;                 // rows per work item
+    int n_seq;                 // sequences in this launch
+    int seq0;                  // first absolute sequence of this launch
+    int n_items;
+    int8_t live_head[KVQ_MAX_KV_HEADS];      // KV head of live slot
+    int8_t live_slot[KVQ_MAX_KV_HEADS];      // live slot of KV head, -1 dead
+    int32_t item_base[kSeqPerLaunch + 1];    // first item of each sequence
+    int32_t nchunk[kSeqPerLaunch];           // chunks per (sequence, live head)
+    int32_t len[kSeqPerLaunch];              // rows attended
+    int32_t wrow[kSeqPerLaunch];             // R-SWA row taken from k_new/v_new, -1 none
+    uint8_t frozen[kSeqPerLaunch];           // q8: column fields hold the frozen RMS
+};
+
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace kvq

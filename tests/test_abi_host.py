@@ -1,0 +1,212 @@
+"""C-ABI library checks that need no GPU: it loads, exports every entry
+point include/kvq.h declares, validates arguments on the host before
+touching anything (a refused call leaves the host counters unchanged), and
+accounts memory as the pages do.  Device pointers here are fake aligned
+addresses that a refused call never dereferences."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from int8_kv_cache_decode_amd import kvq as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"kv_append_f32", "kv_append_q8", "kv_freeze_col_and_requant", "decode_attn_f32",
+            "decode_attn_q8", "rswa_decode"} <= set(names)
+    lib = ctypes.CDLL(K.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    bound = {s[0] for s in K._SIGNATURES}
+    assert set(names) == bound, set(names) ^ bound
+
+
+def fake_cache(kind, batch=2, hkv=8, cap=256, alive=None):
+    c = K.KvCache(kind, batch, hkv, cap, alive=alive, allocate=False)
+    names = ("k", "v") if kind == K.KIND_F32 else ("kq", "ks", "vq", "vs", "kcol", "vcol")
+    for i, n in enumerate(names):
+        setattr(c.c, n, FAKE + 4096 * i)
+    return c
+
+
+def snapshot(c, rings=None):
+    s = (c.len.copy(), c.frozen.copy(), bytes(c.c))
+    if rings is not None:
+        s += (bytes(rings.arr),)
+    return s
+
+
+def call(fn, *args):
+    return getattr(K.lib(), fn)(*args)
+
+
+def expect(rc, code, c, before, rings=None):
+    assert rc == code, (rc, K.last_error())
+    assert K.last_error()
+    after = snapshot(c, rings)
+    for a, b in zip(before, after):
+        assert np.array_equal(np.frombuffer(a, np.uint8) if isinstance(a, bytes) else a,
+                              np.frombuffer(b, np.uint8) if isinstance(b, bytes) else b)
+
+
+def test_cache_init_validation():
+    c = K.kvq_cache()
+    ln = np.zeros(2, np.int32)
+    fr = np.zeros(2, np.uint8)
+    L = K.lib()
+    assert L.kvq_cache_init(ctypes.byref(c), 3, 2, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 8, 64, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 1, 0, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 65, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 8, 128, 16, None, None, fr.ctypes.data) == K.EINVAL
+    alive = np.array([1, 1, 0, 1, 1, 0, 1, 1], np.uint8)
+    assert L.kvq_cache_init(ctypes.byref(c), 2, 2, 8, 128, 16, alive.ctypes.data,
+                            ln.ctypes.data, fr.ctypes.data) == K.OK
+    assert c.n_live == 6 and list(c.live_slot[:8]) == [0, 1, -1, 2, 3, -1, 4, 5]
+
+
+def test_append_refusals_leave_cache_unchanged():
+    for kind, fn in ((K.KIND_F32, "kv_append_f32"), (K.KIND_Q8, "kv_append_q8")):
+        c = fake_cache(kind, cap=100)
+        c.len[:] = [90, 5]
+        before = snapshot(c)
+        expect(call(fn, c.ref, 0, 11, FAKE, FAKE, None), K.ECAPACITY, c, before)
+        expect(call(fn, c.ref, 2, 1, FAKE, FAKE, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, -2, 1, FAKE, FAKE, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 1, -1, FAKE, FAKE, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 1, 3, None, FAKE, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 1, 3, FAKE + 4, FAKE, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, K.ALL_SEQS, 2, FAKE, FAKE, None), K.EINVAL, c, before)
+        c.len[:] = [100, 5]
+        before = snapshot(c)
+        expect(call(fn, c.ref, K.ALL_SEQS, 1, FAKE, FAKE, None), K.ECAPACITY, c, before)
+    # wrong kind
+    c = fake_cache(K.KIND_F32)
+    before = snapshot(c)
+    expect(call("kv_append_q8", c.ref, 0, 1, FAKE, FAKE, None), K.ESTATE, c, before)
+    expect(call("kv_freeze_col_and_requant", c.ref, 0, None), K.ESTATE, c, before)
+    c = fake_cache(K.KIND_Q8)
+    before = snapshot(c)
+    expect(call("kv_append_f32", c.ref, 0, 1, FAKE, FAKE, None), K.ESTATE, c, before)
+    expect(call("kv_freeze_col_and_requant", c.ref, 5, None), K.EINVAL, c, before)
+
+
+def test_missing_or_misaligned_buffers_refused():
+    c = fake_cache(K.KIND_Q8)
+    c.c.vs = 0
+    before = snapshot(c)
+    expect(call("kv_append_q8", c.ref, 0, 1, FAKE, FAKE, None), K.EINVAL, c, before)
+    c = fake_cache(K.KIND_F32)
+    c.c.k = FAKE + 8
+    before = snapshot(c)
+    expect(call("decode_attn_f32", c.ref, 8, FAKE, FAKE, FAKE, 1 << 30, None), K.EINVAL, c, before)
+
+
+def test_decode_refusals():
+    for kind, fn in ((K.KIND_F32, "decode_attn_f32"), (K.KIND_Q8, "decode_attn_q8")):
+        c = fake_cache(kind)
+        c.len[:] = [10, 20]
+        need = K.kvq_workspace_bytes(c, 32)
+        assert need > 0 and need % 256 == 0
+        before = snapshot(c)
+        expect(call(fn, c.ref, 30, FAKE, FAKE, FAKE, need, None), K.EINVAL, c, before)     # 30 % 8
+        expect(call(fn, c.ref, 8 * 16, FAKE, FAKE, FAKE, 1 << 40, None), K.EINVAL, c, before)  # group 16
+        expect(call(fn, c.ref, 32, None, FAKE, FAKE, need, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 32, FAKE, FAKE, None, need, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 32, FAKE, FAKE, FAKE, need - 1, None), K.EINVAL, c, before)
+        c.len[1] = 300                                     # len beyond capacity
+        before = snapshot(c)
+        expect(call(fn, c.ref, 32, FAKE, FAKE, FAKE, need, None), K.ESTATE, c, before)
+    c = fake_cache(K.KIND_Q8)
+    before = snapshot(c)
+    expect(call("decode_attn_f32", c.ref, 32, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE, c, before)
+
+
+def test_rswa_refusals_leave_cache_and_rings_unchanged():
+    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=200)
+    rings = K.Rings(2)
+    ws = K.kvq_workspace_bytes(c, 10)
+    before = snapshot(c, rings)
+    # decode before record_prefill ([P3] decode_before_prefill_errors)
+    expect(call("rswa_decode", c.ref, rings.ref, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None), K.ESTATE,
+           c, before, rings)
+    c.len[:] = [73, 72]
+    before = snapshot(c, rings)
+    # prefill + W beyond capacity
+    expect(call("rswa_record_prefill", c.ref, rings.ref, 0), K.ECAPACITY, c, before, rings)
+    expect(call("rswa_record_prefill", c.ref, rings.ref, 2), K.EINVAL, c, before, rings)
+    assert call("rswa_record_prefill", c.ref, rings.ref, 1) == K.OK
+    assert rings[1].prefill_len == 72 and rings[1].ring_len == 0 and rings[1].ring_pos == 0
+    c.len[0] = 10
+    assert call("rswa_record_prefill", c.ref, rings.ref, 0) == K.OK
+    before = snapshot(c, rings)
+    # malformed steps must not write ([P3] malformed q/k/v do not mutate)
+    expect(call("rswa_decode", c.ref, rings.ref, 10, FAKE, None, FAKE, FAKE, FAKE, ws, None), K.EINVAL,
+           c, before, rings)
+    expect(call("rswa_decode", c.ref, rings.ref, 10, None, FAKE, FAKE, FAKE, FAKE, ws, None), K.EINVAL,
+           c, before, rings)
+    expect(call("rswa_decode", c.ref, rings.ref, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 256, None),
+           K.EINVAL, c, before, rings)
+    expect(call("rswa_decode", c.ref, rings.ref, 15, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None), K.EINVAL,
+           c, before, rings)
+    # the sequence was appended to after its prefill was recorded
+    c.len[0] = 11
+    before = snapshot(c, rings)
+    expect(call("rswa_decode", c.ref, rings.ref, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None), K.ESTATE,
+           c, before, rings)
+
+
+def test_buffer_and_workspace_sizes():
+    c = fake_cache(K.KIND_Q8, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
+    rows = 3 * 6 * 1000
+    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == rows * 128
+    assert K.kvq_buffer_bytes(c, K.BUF_KS) == rows * 16
+    assert K.kvq_buffer_bytes(c, K.BUF_VQ) == rows * 128
+    assert K.kvq_buffer_bytes(c, K.BUF_VS) == rows * 4
+    assert K.kvq_buffer_bytes(c, K.BUF_KCOL) == 3 * 6 * 512
+    assert K.kvq_buffer_bytes(c, K.BUF_K) == 0
+    f = fake_cache(K.KIND_F32, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
+    assert K.kvq_buffer_bytes(f, K.BUF_K) == rows * 512 and K.kvq_buffer_bytes(f, K.BUF_KQ) == 0
+    assert K.kvq_workspace_bytes(c, 30) == 0 and K.kvq_workspace_bytes(c, 32) > 0
+
+
+def test_memory_accounting_matches_pages():
+    """[P1] test append_tracks_seq_len_and_layout / dead_head_stores_nothing,
+    scaled to head_dim 128: one f32 row of a live head is 2*4*128 bytes and a
+    dead head stores nothing; q8_2f is 276 B per (row, head) plus the frozen
+    column fields -> the x3.71 ratio the pages quote as "~3.7"."""
+    f = fake_cache(K.KIND_F32, batch=1, hkv=2, cap=64, alive=[1, 0])
+    f.len[0] = 2
+    assert K.kvq_cache_bytes(f) == 2 * 2 * 128 * 4
+    q = fake_cache(K.KIND_Q8, batch=1, hkv=2, cap=64, alive=[1, 0])
+    q.len[0] = 2
+    assert K.kvq_cache_bytes(q) == 2 * 276
+    q.frozen[0] = 1
+    assert K.kvq_cache_bytes(q) == 2 * 276 + 2 * 128 * 4
+    big_f = fake_cache(K.KIND_F32, batch=1, hkv=8, cap=1 << 20)
+    big_q = fake_cache(K.KIND_Q8, batch=1, hkv=8, cap=1 << 20)
+    big_f.len[0] = big_q.len[0] = 1 << 20
+    big_q.frozen[0] = 1
+    ratio = K.kvq_cache_bytes(big_f) / K.kvq_cache_bytes(big_q)
+    assert abs(ratio - 1024 / 276) < 1e-3 and round(ratio, 1) == 3.7
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(K, "_lib", None)
+    monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        K.lib()
