@@ -435,32 +435,77 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
 // Combine: per (sequence, Q head), merge the chunk partials with the same
 // rescaling as the fold, divide, and apply the V column field (q8 only).
 // Q heads of dead groups, and sequences with no rows, get zeros.
+// 256 threads: a block max over the chunk maxima, then 8 sub-groups of 32
+// lanes (a float4 of channels each) stride over the chunks, merged in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+constexpr int kCombineGroups = kCombineThreads / 32;
+
 template <bool kQ8>
-__global__ __launch_bounds__(128) void k_combine(const DecodeArgs a) {
-    const int h = blockIdx.x, j = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a) {
+    __shared__ float sm_red[kCombineThreads / 64];
+    __shared__ float4 sm_acc[kCombineGroups][32];
+    __shared__ float sm_l[kCombineGroups];
+    const int h = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
     const int b = a.seq0 + j;
     const int g = h / a.hpk, hh = h - g * a.hpk;
     const int gl = a.live_slot[g];
     float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD;
     if (gl < 0 || a.len[j] == 0) {
-        o[d] = 0.0f;
+        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
     const int nch = a.nchunk[j];
-    const int it0 = a.item_base[j] + gl * nch;
+    const size_t it0 = (size_t)a.item_base[j] + (size_t)gl * nch;
+    const float* ml = a.ws_ml + (it0 * a.hpk + hh) * 2;          // stride hpk*2 per chunk
+    const float* acc = a.ws_acc + (it0 * a.hpk + hh) * kHD;      // stride hpk*128 per chunk
+    const size_t mstride = (size_t)a.hpk * 2, astride = (size_t)a.hpk * kHD;
+
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, a.ws_ml[((size_t)(it0 + c) * a.hpk + hh) * 2]);
-    float L = 0.0f, A = 0.0f;
-    for (int c = 0; c < nch; ++c) {
-        const size_t ix = (size_t)(it0 + c) * a.hpk + hh;
-        const float e = fast_exp2(a.ws_ml[ix * 2] - M);
-        L += e * a.ws_ml[ix * 2 + 1];
-        A += e * a.ws_acc[ix * kHD + d];
+    for (int c = tid; c < nch; c += kCombineThreads) M = fmaxf(M, ml[c * mstride]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) sm_red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+
+    const int sg = tid >> 5, lane = tid & 31;
+    float L = 0.0f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int c = sg; c < nch; c += kCombineGroups) {
+        const float e = fast_exp2(ml[c * mstride] - M);
+        const float4 x = *(const float4*)(acc + c * astride + 4 * lane);
+        L = fmaf(e, ml[c * mstride + 1], L);
+        A.x = fmaf(e, x.x, A.x);
+        A.y = fmaf(e, x.y, A.y);
+        A.z = fmaf(e, x.z, A.z);
+        A.w = fmaf(e, x.w, A.w);
     }
-    float r = A / L;
-    if (kQ8 && a.frozen[j]) r *= a.vcol[((size_t)b * a.n_live + gl) * kHD + d];
-    o[d] = r;
+    sm_acc[sg][lane] = A;
+    if (lane == 0) sm_l[sg] = L;
+    __syncthreads();
+    if (tid < 32) {
+        float Lt = 0.0f;
+        float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kCombineGroups; ++k) {
+            Lt += sm_l[k];
+            At.x += sm_acc[k][tid].x;
+            At.y += sm_acc[k][tid].y;
+            At.z += sm_acc[k][tid].z;
+            At.w += sm_acc[k][tid].w;
+        }
+        const float inv = 1.0f / Lt;
+        float4 r = make_float4(At.x * inv, At.y * inv, At.z * inv, At.w * inv);
+        if (kQ8 && a.frozen[j]) {
+            const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + 4 * tid);
+            r.x *= vc.x;
+            r.y *= vc.y;
+            r.z *= vc.z;
+            r.w *= vc.w;
+        }
+        *(float4*)(o + 4 * tid) = r;
+    }
 }
 
 }  // namespace
@@ -476,7 +521,7 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(k_combine<false>, dim3(a.n_q_heads, a.n_seq), dim3(kHD), 0, s, a);
+    hipLaunchKernelGGL(k_combine<false>, dim3(a.n_q_heads, a.n_seq), dim3(kCombineThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -491,7 +536,7 @@ hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(k_combine<true>, dim3(a.n_q_heads, a.n_seq), dim3(kHD), 0, s, a);
+    hipLaunchKernelGGL(k_combine<true>, dim3(a.n_q_heads, a.n_seq), dim3(kCombineThreads), 0, s, a);
     return hipGetLastError();
 }
 
