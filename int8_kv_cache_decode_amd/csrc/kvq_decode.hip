@@ -220,22 +220,33 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// q8 cache.  Lane layout: ri = lane >> 3 picks one of 8 rows, seg = lane & 7
-// the 16 channels [16 seg, 16 seg + 16) (half of a 32-channel K group).  One
-// 16-byte load per lane covers eight consecutive 128-byte int8 rows; a wave
-// takes 32 rows per step.
+// q8 cache.
 //
-// Scores are computed exactly.  The query side of a score, q (.) kcol
-// ([P1] attend: score = s_k * <q (.) col_k, k_q>), is split once per work
-// item into four balanced base-128 int8 digits relative to a power of two
-// per (Q head, K group): qc = 2^(e-27) * (((d0*128 + d1)*128 + d2)*128 + d3)
-// with |qc - that| <= 2^(e-28).  Each digit's dot with the int8 codes is an
-// exact i32 (v_dot4), the digits combine exactly in f64, and the K group
-// scale and 1/sqrt(128) multiply in f64; the score stays f64 until the
-// running max is subtracted.  V codes become f32 with one sign-extending byte
-// convert each, V row scales fold into the softmax weight, and the V column
+// Scores are computed exactly, on the matrix cores.  The query side of a
+// score, q (.) kcol ([P1] attend: score = s_k * <q (.) col_k, k_q>), is split
+// once per work item into four balanced base-128 int8 digits relative to a
+// power of two per (Q head, K group):
+//   qc = 2^(e-27) * (((d0*128 + d1)*128 + d2)*128 + d3),  |error| <= 2^(e-28).
+// For a tile of 16 rows and one 32-channel K group, one
+// v_mfma_i32_16x16x32_i8 multiplies A = digits (16 = 4 heads x 4 digits) by
+// B = the int8 codes (32 channels x 16 rows) into exact i32 sums; lane
+// (head hq = lane >> 4, row n = lane & 15) receives all four digit sums of its
+// (head, row), combines them exactly in f64 and adds ks * 2^(e-27) *
+// log2(e)/sqrt(128) of each group.  The score stays f64 until the running max
+// is subtracted.
+//
+// The online softmax runs in that (head, row) layout with a lazily refreshed
+// max: it moves only when a tile exceeds it by more than kLazy (log2 units),
+// so weights stay <= 2^kLazy and the accumulators are rarely rescaled.  The
+// weights times the V row scales go through a per-wave LDS slot to the V
+// layout -- lane (ri = lane >> 3, seg = lane & 7) owns rows ri and ri + 8 and
+// channels [16 seg, 16 seg + 16) -- where V codes become f32 (one
+// sign-extending byte convert each) and accumulate per head.  The V column
 // field is applied once in the combine ([P1] attend: acc (.) vcol at the end).
 // ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr float kLazy = 8.0f;
+
 __device__ __forceinline__ void unpack16(const uint4 x, float (&f)[16]) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -255,22 +266,6 @@ __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
     return *reinterpret_cast<double*>(&r);
 }
 
-// Sum 4 per-lane partials over the 8 lanes of a row group so that lanes with
-// (seg >> 1) == i end with the total of partial i.
-__device__ __forceinline__ double reduce4_over8_f64(const double (&v)[4], int seg) {
-    const bool b2 = seg & 4, b1 = seg & 2;
-    double x[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const double keep = b2 ? v[i + 2] : v[i];
-        const double send = b2 ? v[i] : v[i + 2];
-        x[i] = keep + shfl_xor_f64(send, 4);
-    }
-    double z = (b1 ? x[1] : x[0]) + shfl_xor_f64(b1 ? x[0] : x[1], 2);
-    z += shfl_xor_f64(z, 1);
-    return z;
-}
-
 // One balanced base-128 digit: x = 128 * next + digit, digit in [-64, 63].
 __device__ __forceinline__ int take_digit(int& x) {
     const int d = ((x + 64) & 127) - 64;
@@ -278,137 +273,227 @@ __device__ __forceinline__ int take_digit(int& x) {
     return d;
 }
 
+// Max over the 16 lanes sharing lane >> 4.
+__device__ __forceinline__ float max16(float x) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// Orders this wave's LDS writes before its following LDS reads.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int HPK>
 __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
+    constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
     __shared__ float sm_acc[kWaves][HPK][kHD];
     __shared__ float sm_ml[kWaves][HPK][2];
+    __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
+    __shared__ float sm_alpha[kWaves][2][HPK];        // per wave, two tiles: rescale factor per head
     const Item it = decode_item(a);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int ri = lane >> 3, seg = lane & 7, grp = seg >> 1;
+    const int hq = lane >> 4, n = lane & 15;          // score layout
+    const int ri = lane >> 3, seg = lane & 7;         // V layout
     const int8_t* KQ = a.kq + it.hrow * kHD;
     const float* KS = a.ks + it.hrow * kKScales;
     const int8_t* VQ = a.vq + it.hrow * kHD;
     const float* VS = a.vs + it.hrow;
     const bool frz = a.frozen[it.j] != 0;
-    const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD + 16 * seg;
+    const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
-    // Query digits: dig[h][j][w] packs digit j of channels 16 seg + 4w .. +3.
-    int dig[HPK][4][4];
-    double gscale[HPK];            // 2^(e-27) * log2(e)/sqrt(128) for this lane's group
+    // ---- query digits (MFMA A operand) and per-group scales ----
+    // A[m][k]: m = lane & 15 = 4 * head + digit, k = 8 * (lane >> 4) + t of a group.
+    long qa[NB][4];
+    double gsc[NB][4];                                // for this lane's score head 4 hb + hq
 #pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 16 * seg;
-        double qc[16];
-        double amax = 0.0;
+    for (int hb = 0; hb < NB; ++hb) {
+        const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
+        double qc[4][8];
+        double gmax[4];
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 t = *(const float4*)(qp + 4 * c4);
-            float4 cc = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (frz) cc = *(const float4*)(kcol + 4 * c4);
-            qc[4 * c4 + 0] = (double)t.x * (double)cc.x;      // exact products
-            qc[4 * c4 + 1] = (double)t.y * (double)cc.y;
-            qc[4 * c4 + 2] = (double)t.z * (double)cc.z;
-            qc[4 * c4 + 3] = (double)t.w * (double)cc.w;
+        for (int g = 0; g < 4; ++g) {
+            gmax[g] = 0.0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qc[g][t] = 0.0;
+            if (hm < HPK) {
+                const int d0 = 32 * g + 8 * kb;
+                const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
+#pragma unroll
+                for (int t4 = 0; t4 < 2; ++t4) {
+                    const float4 qv = *(const float4*)(qp + 4 * t4);
+                    float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
+                    if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
+                    qc[g][4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
+                    qc[g][4 * t4 + 1] = (double)qv.y * (double)cv.y;
+                    qc[g][4 * t4 + 2] = (double)qv.z * (double)cv.z;
+                    qc[g][4 * t4 + 3] = (double)qv.w * (double)cv.w;
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) gmax[g] = fmax(gmax[g], fabs(qc[g][t]));
+            }
+            gmax[g] = fmax(gmax[g], shfl_xor_f64(gmax[g], 16));
+            gmax[g] = fmax(gmax[g], shfl_xor_f64(gmax[g], 32));
         }
 #pragma unroll
-        for (int c = 0; c < 16; ++c) amax = fmax(amax, fabs(qc[c]));
-        amax = fmax(amax, shfl_xor_f64(amax, 1));             // the other half of the K group
-        int e = 0;
-        (void)frexp(amax, &e);                                 // amax < 2^e
-        const double up = ldexp(1.0, 27 - e);
-        gscale[h] = ldexp(kQScale64, e - 27);
+        for (int g = 0; g < 4; ++g) {
+            int e = 0;
+            (void)frexp(gmax[g], &e);                 // gmax < 2^e
+            const double up = ldexp(1.0, 27 - e);
+            long pk = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            int pk[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                int x = (int)rint(qc[4 * w + c] * up);          // |x| <= 2^27
+            for (int t = 0; t < 8; ++t) {
+                int x = (int)rint(qc[g][t] * up);     // |x| <= 2^27
                 const int d3 = take_digit(x);
                 const int d2 = take_digit(x);
                 const int d1 = take_digit(x);
-                const int d0 = x;                               // |d0| <= 64
-                pk[0] |= (d0 & 0xff) << (8 * c);
-                pk[1] |= (d1 & 0xff) << (8 * c);
-                pk[2] |= (d2 & 0xff) << (8 * c);
-                pk[3] |= (d3 & 0xff) << (8 * c);
+                const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
+                pk |= (long)(d & 0xff) << (8 * t);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dig[h][j][w] = pk[j];
+            qa[hb][g] = pk;
+            const int es = __shfl(e, 4 * hq, 64);     // lane 4 hq holds head 4 hb + hq
+            gsc[hb][g] = ldexp(kQScale64, es - 27);
         }
     }
-    float m[HPK], l[HPK], acc[HPK][16];
+
+    float m[NB], l[NB];
+    float acc[HPK][16];
 #pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
+    for (int hb = 0; hb < NB; ++hb) {
+        m[hb] = -INFINITY;
+        l[hb] = 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < HPK; ++h)
 #pragma unroll
         for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
-    }
 
-    for (int r = it.row0 + wave * 32; r < it.row1; r += kWaves * 32) {
-        uint4 kx[4], vx[4];
-        float ksv[4], vsv[4];
+    // Rows of the chunk go to the waves in 16-row tiles, two tiles per step;
+    // the loads of the next step are issued before this step's arithmetic.
+    constexpr int kTiles = 2;
+    constexpr int kStep = 16 * kTiles * kWaves;
+    struct Tile {
+        long kb4[4];
+        float4 ks4;
+        float vsn;
+        uint4 vx0, vx1;
+    };
+    auto load_tile = [&](int r0, Tile& t) {
+        const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const size_t row = (size_t)min(r + 8 * i + ri, it.row1 - 1);
-            kx[i] = *(const uint4*)(KQ + row * kHD + 16 * seg);
-            ksv[i] = KS[row * kKScales + grp];
-            vx[i] = *(const uint4*)(VQ + row * kHD + 16 * seg);
-            vsv[i] = VS[row];
-        }
-        double part[HPK][4];
+        for (int g = 0; g < 4; ++g) t.kb4[g] = *(const long*)(KQ + rk * kHD + 32 * g + 8 * (lane >> 4));
+        t.ks4 = *(const float4*)(KS + rk * kKScales);
+        t.vsn = VS[rk];
+        const size_t rv0 = (size_t)min(r0 + ri, it.row1 - 1);
+        const size_t rv1 = (size_t)min(r0 + ri + 8, it.row1 - 1);
+        t.vx0 = *(const uint4*)(VQ + rv0 * kHD + 16 * seg);
+        t.vx1 = *(const uint4*)(VQ + rv1 * kHD + 16 * seg);
+    };
+    int buf = 0;
+    auto compute_tile = [&](int r0, const Tile& t) {
+        const bool valid = r0 + n < it.row1;
+        // ---- scores (exact), softmax weights in the (head, row) layout ----
+        bool rescale = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double ks64 = (double)ksv[i];
+        for (int hb = 0; hb < NB; ++hb) {
+            const v4i zero = {0, 0, 0, 0};
+            double sc = 0.0;
+            const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-                int sj[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    int t = __builtin_amdgcn_sdot4(dig[h][j][0], (int)kx[i].x, 0, false);
-                    t = __builtin_amdgcn_sdot4(dig[h][j][1], (int)kx[i].y, t, false);
-                    t = __builtin_amdgcn_sdot4(dig[h][j][2], (int)kx[i].z, t, false);
-                    t = __builtin_amdgcn_sdot4(dig[h][j][3], (int)kx[i].w, t, false);
-                    sj[j] = t;
-                }
-                double x = (double)sj[0];
-                x = fma(x, 128.0, (double)sj[1]);
-                x = fma(x, 128.0, (double)sj[2]);
-                x = fma(x, 128.0, (double)sj[3]);
-                part[h][i] = x * (ks64 * gscale[h]);
+            for (int g = 0; g < 4; ++g) {
+                const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[hb][g], t.kb4[g], zero, 0, 0, 0);
+                const int t1 = dsum[0] * 128 + dsum[1];
+                const int t2 = dsum[2] * 128 + dsum[3];
+                const double x = fma((double)t1, 16384.0, (double)t2);
+                sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+            }
+            const int h = 4 * hb + hq;
+            if (!valid || h >= HPK) sc = -INFINITY;
+            const float tmax = max16((float)sc);
+            float mnew = m[hb], alpha = 1.0f;
+            if (tmax > m[hb] + kLazy) {               // uniform over the head's 16 lanes
+                mnew = tmax;
+                alpha = fast_exp2(m[hb] - tmax);
+            }
+            rescale |= __any(alpha != 1.0f);
+            const float p = sc == -INFINITY ? 0.0f : fast_exp2((float)(sc - (double)mnew));
+            l[hb] = l[hb] * alpha + p;
+            m[hb] = mnew;
+            if (h < HPK) {
+                sm_pw[wave][buf][n][h] = p * t.vsn;
+                if (n == 0) sm_alpha[wave][buf][h] = alpha;
             }
         }
-        const int myrow = r + 8 * (seg >> 1) + ri;
-        float pw[HPK][4];
+        wave_lds_sync();
+
+        // ---- V accumulation in the (row, channel) layout ----
+        if (rescale) {
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                const float al = sm_alpha[wave][buf][h];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[h][c] *= al;
+            }
+        }
+        float w0[HPK], w1[HPK];
 #pragma unroll
         for (int h = 0; h < HPK; ++h) {
-            double s = reduce4_over8_f64(part[h], seg);
-            if (myrow >= it.row1) s = -INFINITY;
-            const float mnew = fmaxf(m[h], wave_max((float)s));
-            const float alpha = fast_exp2(m[h] - mnew);
-            const float p = fast_exp2((float)(s - (double)mnew));
-            l[h] = l[h] * alpha + ((seg & 1) == 0 ? p : 0.0f);
+            w0[h] = sm_pw[wave][buf][ri][h];
+            w1[h] = sm_pw[wave][buf][ri + 8][h];
+        }
+        float vf[16];
+        unpack16(t.vx0, vf);
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[h][c] *= alpha;
+        for (int h = 0; h < HPK; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pw[h][i] = __shfl(p, ri * 8 + 2 * i, 64) * vsv[i];
-            m[h] = mnew;
+            for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(w0[h], vf[c], acc[h][c]);
+        unpack16(t.vx1, vf);
+#pragma unroll
+        for (int h = 0; h < HPK; ++h)
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(w1[h], vf[c], acc[h][c]);
+        buf ^= 1;
+    };
+
+    int r0 = it.row0 + 16 * kTiles * wave;
+    Tile cur[kTiles];
+    if (r0 < it.row1) {
+#pragma unroll
+        for (int k = 0; k < kTiles; ++k) load_tile(r0 + 16 * k, cur[k]);
+    }
+    for (; r0 < it.row1; r0 += kStep) {
+        Tile nxt[kTiles];
+        const bool more = r0 + kStep < it.row1;
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < kTiles; ++k) load_tile(r0 + kStep + 16 * k, nxt[k]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float vf[16];
-            unpack16(vx[i], vf);
+        for (int k = 0; k < kTiles; ++k)
+            if (r0 + 16 * k < it.row1) compute_tile(r0 + 16 * k, cur[k]);
+        if (more) {
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(pw[h][i], vf[c], acc[h][c]);
-            }
+            for (int k = 0; k < kTiles; ++k) cur[k] = nxt[k];
         }
     }
 
+    // ---- per-wave state -> LDS, then the 4-wave merge ----
+#pragma unroll
+    for (int hb = 0; hb < NB; ++hb) {
+        const float lt = sum16(l[hb]);
+        const int h = 4 * hb + hq;
+        if (n == 0 && h < HPK) {
+            sm_ml[wave][h][0] = m[hb];
+            sm_ml[wave][h][1] = lt;
+        }
+    }
 #pragma unroll
     for (int h = 0; h < HPK; ++h) {
-        const float lt = wave_sum(l[h]);
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             float x = acc[h][c];
@@ -422,10 +507,6 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
             for (int c4 = 0; c4 < 4; ++c4)
                 *(float4*)&sm_acc[wave][h][16 * seg + 4 * c4] =
                     make_float4(acc[h][4 * c4], acc[h][4 * c4 + 1], acc[h][4 * c4 + 2], acc[h][4 * c4 + 3]);
-        }
-        if (lane == 0) {
-            sm_ml[wave][h][0] = m[h];
-            sm_ml[wave][h][1] = lt;
         }
     }
     write_partials<HPK>(a, sm_acc, sm_ml);
