@@ -24,7 +24,7 @@ constexpr int kSeqPerLaunch = 128;
 // smallest multiple of kChunkAlign (and at least kChunkMin) that keeps the
 // number of chunks of a launch near kTargetItems.
 #ifndef KVQ_TARGET_ITEMS
-#define KVQ_TARGET_ITEMS 4096
+#define KVQ_TARGET_ITEMS 2048
 #endif
 #ifndef KVQ_CHUNK_MIN
 #define KVQ_CHUNK_MIN 64
