@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 // power of two per (Q head, K group):
 //   qc = 2^(e-27) * (((d0*128 + d1)*128 + d2)*128 + d3),  |error| <= 2^(e-28).
 // For a tile of 16 rows and one 32-channel K group, one
-// v_mfma_i32_16x16x32_i8 multiplies A = digits (16 = 4 heads x 4 digits) by
-// B = the int8 codes (32 channels x 16 rows) into exact i32 sums; lane
+// v_mfma_i32_16x16x64_i8 multiplies A = digits (16 = 4 heads x 4 digits, the
+// other group of the 64-channel span zeroed) by B = the int8 codes (64
+// channels x 16 rows, 16 contiguous bytes per lane) into exact i32 sums; lane
 // (head hq = lane >> 4, row n = lane & 15) receives all four digit sums of its
 // (head, row), combines them exactly in f64 and adds ks * 2^(e-27) *
 // log2(e)/sqrt(128) of each group.  The score stays f64 until the running max
@@ -324,56 +325,61 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
     const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
     // ---- query digits (MFMA A operand) and per-group scales ----
-    // A[m][k]: m = lane & 15 = 4 * head + digit, k = 8 * (lane >> 4) + t of a group.
-    long qa[NB][4];
+    // One v_mfma_i32_16x16x64_i8 spans 64 channels = two K groups.  A[m][k]:
+    // m = lane & 15 = 4 * head + digit, k = 16 * (lane >> 4) + t of the span,
+    // so lanes with lane >> 4 in {0, 1} hold the span's first group and lanes
+    // {2, 3} its second; each group gets its own product by zeroing the other
+    // half of A.
+    const bool first_half = (lane >> 4) < 2;
+    v4i qa_lo[NB][2], qa_hi[NB][2];                   // [head block][span]
     double gsc[NB][4];                                // for this lane's score head 4 hb + hq
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
         const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
-        double qc[4][8];
-        double gmax[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            gmax[g] = 0.0;
+        for (int sp = 0; sp < 2; ++sp) {
+            const int d0 = 64 * sp + 16 * kb;
+            double qc[16];
+            double gmax = 0.0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) qc[g][t] = 0.0;
+            for (int t = 0; t < 16; ++t) qc[t] = 0.0;
             if (hm < HPK) {
-                const int d0 = 32 * g + 8 * kb;
                 const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
 #pragma unroll
-                for (int t4 = 0; t4 < 2; ++t4) {
+                for (int t4 = 0; t4 < 4; ++t4) {
                     const float4 qv = *(const float4*)(qp + 4 * t4);
                     float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
                     if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
-                    qc[g][4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
-                    qc[g][4 * t4 + 1] = (double)qv.y * (double)cv.y;
-                    qc[g][4 * t4 + 2] = (double)qv.z * (double)cv.z;
-                    qc[g][4 * t4 + 3] = (double)qv.w * (double)cv.w;
+                    qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
+                    qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
+                    qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
+                    qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
                 }
 #pragma unroll
-                for (int t = 0; t < 8; ++t) gmax[g] = fmax(gmax[g], fabs(qc[g][t]));
+                for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
             }
-            gmax[g] = fmax(gmax[g], shfl_xor_f64(gmax[g], 16));
-            gmax[g] = fmax(gmax[g], shfl_xor_f64(gmax[g], 32));
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
+            gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
             int e = 0;
-            (void)frexp(gmax[g], &e);                 // gmax < 2^e
+            (void)frexp(gmax, &e);                         // gmax < 2^e
             const double up = ldexp(1.0, 27 - e);
-            long pk = 0;
+            v4i pk = {0, 0, 0, 0};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                int x = (int)rint(qc[g][t] * up);     // |x| <= 2^27
+            for (int t = 0; t < 16; ++t) {
+                int x = (int)rint(qc[t] * up);             // |x| <= 2^27
                 const int d3 = take_digit(x);
                 const int d2 = take_digit(x);
                 const int d1 = take_digit(x);
                 const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
-                pk |= (long)(d & 0xff) << (8 * t);
+                pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
             }
-            qa[hb][g] = pk;
-            const int es = __shfl(e, 4 * hq, 64);     // lane 4 hq holds head 4 hb + hq
-            gsc[hb][g] = ldexp(kQScale64, es - 27);
+            const v4i zero = {0, 0, 0, 0};
+            qa_lo[hb][sp] = first_half ? pk : zero;
+            qa_hi[hb][sp] = first_half ? zero : pk;
+#pragma unroll
+            for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
+                const int es = __shfl(e, 4 * hq + 32 * gs, 64);
+                gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
+            }
         }
     }
 
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
     constexpr int kTiles = 2;
     constexpr int kStep = 16 * kTiles * kWaves;
     struct Tile {
-        long kb4[4];
+        uint4 kb2[2];                                  // B operand: 16 channels of row n per span
         float4 ks4;
         float vsn;
         uint4 vx0, vx1;
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
     auto load_tile = [&](int r0, Tile& t) {
         const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) t.kb4[g] = *(const long*)(KQ + rk * kHD + 32 * g + 8 * (lane >> 4));
+        for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
         t.ks4 = ld_stream(KS + rk * kKScales);
         t.vsn = ld_stream1(VS + rk);
         const size_t rv0 = (size_t)min(r0 + ri, it.row1 - 1);
@@ -421,12 +427,18 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
             double sc = 0.0;
             const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa[hb][g], t.kb4[g], zero, 0, 0, 0);
-                const int t1 = dsum[0] * 128 + dsum[1];
-                const int t2 = dsum[2] * 128 + dsum[3];
-                const double x = fma((double)t1, 16384.0, (double)t2);
-                sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+            for (int sp = 0; sp < 2; ++sp) {
+                const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+#pragma unroll
+                for (int gs = 0; gs < 2; ++gs) {
+                    const int g = 2 * sp + gs;
+                    const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(gs ? qa_hi[hb][sp] : qa_lo[hb][sp],
+                                                                         kbv, zero, 0, 0, 0);
+                    const int t1 = dsum[0] * 128 + dsum[1];
+                    const int t2 = dsum[2] * 128 + dsum[3];
+                    const double x = fma((double)t1, 16384.0, (double)t2);
+                    sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+                }
             }
             const int h = 4 * hb + hq;
             if (!valid || h >= HPK) sc = -INFINITY;
