@@ -46,7 +46,22 @@ def parse():
     p.add_argument("--part", choices=["both", "rswa", "q8"], default="both")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=8)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 512 MiB device-to-device copy (for counter calibration)")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain device copy of known size: under rocprofv3 --pmc its FETCH_SIZE
+    and WRITE_SIZE per dispatch give the counters' bytes-per-byte factors."""
+    import torch
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "dispatches": 5}))
 
 
 def algorithmic_bytes_q8(lens, n_live, hq):
@@ -82,6 +97,9 @@ def committed_traffic(kernel_tag):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

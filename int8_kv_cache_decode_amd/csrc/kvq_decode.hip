@@ -256,13 +256,30 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 // max: it moves only when a tile exceeds it by more than kLazy (log2 units),
 // so weights stay <= 2^kLazy and the accumulators are rarely rescaled.  The
 // weights times the V row scales go through a per-wave LDS slot to the V
-// layout -- lane (ri = lane >> 3, seg = lane & 7) owns rows ri and ri + 8 and
-// channels [16 seg, 16 seg + 16) -- where V codes become f32 (one
+// layout -- lane (ri = lane / kVSeg, seg = lane % kVSeg) owns rows
+// ri + kVRows * i of each tile and kVDim channels -- where V codes become f32 (one
 // sign-extending byte convert each) and accumulate per head.  The V column
 // field is applied once in the combine ([P1] attend: acc (.) vcol at the end).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr float kLazy = 8.0f;
+
+// V layout of the q8 kernel: a load group covers kVRows rows of a 16-row tile,
+// kVSeg lanes per row, kVDim channels (one 8- or 16-byte load) per lane.
+#ifndef KVQ_Q8_VROWS
+#define KVQ_Q8_VROWS 4
+#endif
+#ifndef KVQ_Q8_TILES
+#define KVQ_Q8_TILES 1
+#endif
+constexpr int kVRows = KVQ_Q8_VROWS;
+constexpr int kVSeg = 64 / kVRows;
+constexpr int kVDim = kHD / kVSeg;
+constexpr int kVLoads = 16 / kVRows;
+template <int N> struct VBytes;
+template <> struct VBytes<16> { typedef uint4 type; };
+template <> struct VBytes<8> { typedef uint2 type; };
+typedef typename VBytes<kVDim>::type vbytes_t;
 
 __device__ __forceinline__ void unpack16(const uint4 x, float (&f)[16]) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -273,6 +290,24 @@ __device__ __forceinline__ void unpack16(const uint4 x, float (&f)[16]) {
         f[4 * k + 2] = (float)(int8_t)((w[k] >> 16) & 0xffu);
         f[4 * k + 3] = (float)((int32_t)w[k] >> 24);
     }
+}
+
+__device__ __forceinline__ void unpack(const uint4 x, float (&f)[16]) { unpack16(x, f); }
+__device__ __forceinline__ void unpack(const uint2 x, float (&f)[8]) {
+    const uint32_t w[2] = {x.x, x.y};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        f[4 * k + 0] = (float)(int8_t)(w[k] & 0xffu);
+        f[4 * k + 1] = (float)(int8_t)((w[k] >> 8) & 0xffu);
+        f[4 * k + 2] = (float)(int8_t)((w[k] >> 16) & 0xffu);
+        f[4 * k + 3] = (float)((int32_t)w[k] >> 24);
+    }
+}
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ld_v(const int8_t* p, uint4& x) { x = ld_stream(p); }
+__device__ __forceinline__ void ld_v(const int8_t* p, uint2& x) {
+    const v2u_t t = __builtin_nontemporal_load(reinterpret_cast<const v2u_t*>(p));
+    x = make_uint2(t.x, t.y);
 }
 
 __device__ __forceinline__ double shfl_xor_f64(double x, int m) {
@@ -306,8 +341,11 @@ __device__ __forceinline__ float sum16(float x) {
 // Orders this wave's LDS writes before its following LDS reads.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+#ifndef KVQ_Q8_MIN_WAVES
+#define KVQ_Q8_MIN_WAVES 3
+#endif
 template <int HPK>
-__global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
+__global__ __launch_bounds__(256, KVQ_Q8_MIN_WAVES) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
     __shared__ float sm_acc[kWaves][HPK][kHD];
     __shared__ float sm_ml[kWaves][HPK][2];
@@ -316,7 +354,7 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
     const Item it = decode_item(a);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hq = lane >> 4, n = lane & 15;          // score layout
-    const int ri = lane >> 3, seg = lane & 7;         // V layout
+    const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
     const int8_t* KQ = a.kq + it.hrow * kHD;
     const float* KS = a.ks + it.hrow * kKScales;
     const int8_t* VQ = a.vq + it.hrow * kHD;
@@ -384,7 +422,7 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
     }
 
     float m[NB], l[NB];
-    float acc[HPK][16];
+    float acc[HPK][kVDim];
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
         m[hb] = -INFINITY;
@@ -393,17 +431,18 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < HPK; ++h)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
+        for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
 
-    // Rows of the chunk go to the waves in 16-row tiles, two tiles per step;
-    // the loads of the next step are issued before this step's arithmetic.
-    constexpr int kTiles = 2;
+    // Rows of the chunk go to the waves in 16-row tiles, kTiles tiles per
+    // step; the loads of the next step are issued before this step's
+    // arithmetic.
+    constexpr int kTiles = KVQ_Q8_TILES;
     constexpr int kStep = 16 * kTiles * kWaves;
     struct Tile {
         uint4 kb2[2];                                  // B operand: 16 channels of row n per span
         float4 ks4;
         float vsn;
-        uint4 vx0, vx1;
+        vbytes_t vx[kVLoads];                          // rows ri + kVRows * i, channels of seg
     };
     auto load_tile = [&](int r0, Tile& t) {
         const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
@@ -411,10 +450,11 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
         for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
         t.ks4 = ld_stream(KS + rk * kKScales);
         t.vsn = ld_stream1(VS + rk);
-        const size_t rv0 = (size_t)min(r0 + ri, it.row1 - 1);
-        const size_t rv1 = (size_t)min(r0 + ri + 8, it.row1 - 1);
-        t.vx0 = ld_stream(VQ + rv0 * kHD + 16 * seg);
-        t.vx1 = ld_stream(VQ + rv1 * kHD + 16 * seg);
+#pragma unroll
+        for (int i = 0; i < kVLoads; ++i) {
+            const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
+            ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
+        }
     };
     int buf = 0;
     auto compute_tile = [&](int r0, const Tile& t) {
@@ -465,48 +505,57 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
             for (int h = 0; h < HPK; ++h) {
                 const float al = sm_alpha[wave][buf][h];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) acc[h][c] *= al;
+                for (int c = 0; c < kVDim; ++c) acc[h][c] *= al;
             }
         }
-        float w0[HPK], w1[HPK];
+        // The tile's rows are summed into a fresh register first and added to
+        // the running accumulator once per tile: the long f32 chain grows by
+        // one addition per tile instead of kVLoads (rounding error ~ sqrt(n)).
+        float ts[HPK][kVDim];
 #pragma unroll
-        for (int h = 0; h < HPK; ++h) {
-            w0[h] = sm_pw[wave][buf][ri][h];
-            w1[h] = sm_pw[wave][buf][ri + 8][h];
+        for (int i = 0; i < kVLoads; ++i) {
+            float w[HPK];
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) w[h] = sm_pw[wave][buf][ri + kVRows * i][h];
+            float vf[kVDim];
+            unpack(t.vx[i], vf);
+#pragma unroll
+            for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                for (int c = 0; c < kVDim; ++c) ts[h][c] = i == 0 ? w[h] * vf[c] : fmaf(w[h], vf[c], ts[h][c]);
         }
-        float vf[16];
-        unpack16(t.vx0, vf);
 #pragma unroll
         for (int h = 0; h < HPK; ++h)
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(w0[h], vf[c], acc[h][c]);
-        unpack16(t.vx1, vf);
-#pragma unroll
-        for (int h = 0; h < HPK; ++h)
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(w1[h], vf[c], acc[h][c]);
+            for (int c = 0; c < kVDim; ++c) acc[h][c] += ts[h][c];
         buf ^= 1;
     };
 
-    int r0 = it.row0 + 16 * kTiles * wave;
-    Tile cur[kTiles];
-    if (r0 < it.row1) {
+    // Two register sets, ping-pong: the next step's loads are issued before
+    // this step's arithmetic.  Rows are clamped into the chunk, so a
+    // prefetch past the end re-reads the chunk's last row (and is unused).
+    auto load_step = [&](int r, Tile (&t)[kTiles]) {
 #pragma unroll
-        for (int k = 0; k < kTiles; ++k) load_tile(r0 + 16 * k, cur[k]);
-    }
-    for (; r0 < it.row1; r0 += kStep) {
-        Tile nxt[kTiles];
-        const bool more = r0 + kStep < it.row1;
-        if (more) {
-#pragma unroll
-            for (int k = 0; k < kTiles; ++k) load_tile(r0 + kStep + 16 * k, nxt[k]);
-        }
+        for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
+    };
+    auto compute_step = [&](int r, const Tile (&t)[kTiles]) {
 #pragma unroll
         for (int k = 0; k < kTiles; ++k)
-            if (r0 + 16 * k < it.row1) compute_tile(r0 + 16 * k, cur[k]);
-        if (more) {
-#pragma unroll
-            for (int k = 0; k < kTiles; ++k) cur[k] = nxt[k];
+            if (r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
+    };
+    int r0 = it.row0 + 16 * kTiles * wave;
+    if (r0 < it.row1) {
+        Tile ta[kTiles], tb[kTiles];
+        load_step(r0, ta);
+        while (true) {
+            load_step(r0 + kStep, tb);
+            compute_step(r0, ta);
+            r0 += kStep;
+            if (r0 >= it.row1) break;
+            load_step(r0 + kStep, ta);
+            compute_step(r0, tb);
+            r0 += kStep;
+            if (r0 >= it.row1) break;
         }
     }
 
@@ -523,17 +572,16 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < HPK; ++h) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
+        for (int c = 0; c < kVDim; ++c) {
             float x = acc[h][c];
-            x += __shfl_xor(x, 8, 64);
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
+#pragma unroll
+            for (int msk = kVSeg; msk < 64; msk <<= 1) x += __shfl_xor(x, msk, 64);
             acc[h][c] = x;
         }
         if (ri == 0) {
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4)
-                *(float4*)&sm_acc[wave][h][16 * seg + 4 * c4] =
+            for (int c4 = 0; c4 < kVDim / 4; ++c4)
+                *(float4*)&sm_acc[wave][h][kVDim * seg + 4 * c4] =
                     make_float4(acc[h][4 * c4], acc[h][4 * c4 + 1], acc[h][4 * c4 + 2], acc[h][4 * c4 + 3]);
         }
     }
@@ -545,9 +593,10 @@ __global__ __launch_bounds__(256) void k_decode_q8(const DecodeArgs a) {
 // rescaling as the fold ([P3] fold: accumulators are rescaled by
 // exp(old max - new max)), divide, and apply the V column field (q8 only).
 // Q heads of dead groups, and sequences with no rows, get zeros.
-// 512 threads = 16 sub-groups of 32 lanes (a float4 of channels each); a
-// sub-group takes every 16th chunk, issuing the loads of up to 8 chunks at
-// once and folding them with a running max; the sub-groups then merge in LDS.
+// Up to 512 threads = 16 sub-groups of 32 lanes (a float4 of channels each),
+// sized to the number of chunks; a sub-group takes every ngroups-th chunk,
+// issuing the loads of up to 8 chunks at once and folding them with a
+// running max; the sub-groups then merge in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 512;
 constexpr int kCombineGroups = kCombineThreads / 32;
@@ -572,15 +621,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     const float* acc = a.ws_acc + (it0 * a.hpk + hh) * kHD;      // stride hpk*128 per chunk
     const size_t mstride = (size_t)a.hpk * 2, astride = (size_t)a.hpk * kHD;
     const int sg = tid >> 5, lane = tid & 31;
+    const int ngroups = (int)(blockDim.x >> 5);
 
     float M = -INFINITY, L = 0.0f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c0 = sg; c0 < nch; c0 += kCombineGroups * kCombineBatch) {
+    for (int c0 = sg; c0 < nch; c0 += ngroups * kCombineBatch) {
         float mv[kCombineBatch], lv[kCombineBatch];
         float4 xv[kCombineBatch];
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k) {
-            const int c = c0 + k * kCombineGroups;
+            const int c = c0 + k * ngroups;
             const bool ok = c < nch;
             mv[k] = ok ? ml[c * mstride] : -INFINITY;
             lv[k] = ok ? ml[c * mstride + 1] : 0.0f;
@@ -614,12 +664,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     __syncthreads();
     if (tid < 32) {
         float Mt = sm_m[0];
-#pragma unroll
-        for (int k = 1; k < kCombineGroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
+        for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
         float Lt = 0.0f;
         float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int k = 0; k < kCombineGroups; ++k) {
+        for (int k = 0; k < ngroups; ++k) {
             const float e = fast_exp2(sm_m[k] - Mt);    // 0 for sub-groups without chunks
             Lt = fmaf(e, sm_l[k], Lt);
             At.x = fmaf(e, sm_acc[k][tid].x, At.x);
@@ -640,6 +688,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     }
 }
 
+// Threads per combine block: enough 32-lane sub-groups that each folds at
+// most one batch of chunks, between 1 and 16 sub-groups.
+int combine_threads(const DecodeArgs& a) {
+    int nmax = 1;
+    for (int j = 0; j < a.n_seq; ++j) nmax = a.nchunk[j] > nmax ? a.nchunk[j] : nmax;
+    int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
+    groups = groups < 1 ? 1 : (groups > kCombineGroups ? kCombineGroups : groups);
+    return 32 * groups;
+}
+
 }  // namespace
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
@@ -653,7 +711,7 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(k_combine<false>, dim3(a.n_q_heads, a.n_seq), dim3(kCombineThreads), 0, s, a);
+    hipLaunchKernelGGL(k_combine<false>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
     return hipGetLastError();
 }
 
@@ -668,7 +726,7 @@ hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) {
             default: return hipErrorInvalidValue;
         }
     }
-    hipLaunchKernelGGL(k_combine<true>, dim3(a.n_q_heads, a.n_seq), dim3(kCombineThreads), 0, s, a);
+    hipLaunchKernelGGL(k_combine<true>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
     return hipGetLastError();
 }
 
