@@ -205,9 +205,10 @@ int kv_freeze_col_and_requant(kvq_cache* c, int seq, void* stream);
 
 /*
  * Bytes of workspace the decode calls need for this cache with n_q_heads
- * query heads (independent of the current lengths).  The workspace holds
- * per-chunk partial softmax states; its contents need no initialisation.
- * Returns 0 on invalid arguments.
+ * query heads (independent of the current lengths): partial softmax states
+ * (max, sum, 128 accumulators per Q head of a group) for 8192 +
+ * min(batch, 128) * n_live slots, rounded up to 256 bytes.  Its contents
+ * need no initialisation.  Returns 0 on invalid arguments.
  */
 size_t kvq_workspace_bytes(const kvq_cache* c, int n_q_heads);
 

@@ -173,13 +173,11 @@ int check_append_args(const kvq_cache* c, int seq, int n_rows, const float* k_ne
 }
 
 // ---- decode ---------------------------------------------------------------
-size_t max_items(const kvq_cache* c) {
-    return (size_t)kTargetItems + (size_t)std::min(c->batch, kSeqPerLaunch) * (size_t)c->n_live;
-}
+size_t ws_slots(const kvq_cache* c) { return max_slots(std::min(c->batch, kSeqPerLaunch), c->n_live); }
 
 size_t ws_need(const kvq_cache* c, int hpk) {
-    const size_t items = max_items(c);
-    size_t bytes = items * hpk * kHD * sizeof(float) + items * hpk * 2 * sizeof(float);
+    const size_t slots = ws_slots(c);
+    size_t bytes = slots * hpk * kHD * sizeof(float) + slots * hpk * 2 * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
 }
 
@@ -218,7 +216,7 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
     a.kcol = c->kcol;
     a.vcol = c->vcol;
     a.ws_acc = (float*)ws;
-    a.ws_ml = (float*)ws + max_items(c) * hpk * kHD;
+    a.ws_ml = (float*)ws + ws_slots(c) * hpk * kHD;
     a.k_new = k_new;
     a.v_new = v_new;
     a.k_store = c->k;
@@ -232,26 +230,23 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
     memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
     for (int s0 = 0; s0 < c->batch; s0 += kSeqPerLaunch) {
         const int ns = std::min(kSeqPerLaunch, c->batch - s0);
-        int64_t total = 0;
-        for (int j = 0; j < ns; ++j) total += (int64_t)lens[s0 + j] * c->n_live;
-        int64_t chunk = (total + kTargetItems - 1) / kTargetItems;
-        chunk = (chunk + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-        chunk = std::max<int64_t>(chunk, kChunkMin);
-        a.chunk = (int)chunk;
         a.seq0 = s0;
         a.n_seq = ns;
-        int items = 0;
+        int64_t tiles = 0;
         for (int j = 0; j < ns; ++j) {
             const int L = lens[s0 + j];
             a.len[j] = L;
-            a.nchunk[j] = (int)((L + chunk - 1) / chunk);
+            a.ntile[j] = (L + kTileRows - 1) / kTileRows;
             a.wrow[j] = wrows ? wrows[s0 + j] : -1;
             a.frozen[j] = c->frozen[s0 + j] ? 1 : 0;
-            a.item_base[j] = items;
-            items += a.nchunk[j] * c->n_live;
+            a.tile_base[j] = (int32_t)tiles;
+            tiles += (int64_t)a.ntile[j] * c->n_live;
+            // unreachable with real memory sizes (2^31 tiles of q8 rows > 9 TB)
+            if (tiles >= ((int64_t)1 << 31))
+                return fail(KVQ_EINVAL, "%s: more than 2^31 tiles in one launch", fn);
         }
-        a.item_base[ns] = items;
-        a.n_items = items;
+        a.tile_base[ns] = (int32_t)tiles;
+        a.n_tiles = (int)tiles;
         const hipError_t e = (c->kind == KVQ_KIND_Q8) ? launch_decode_q8(a, s) : launch_decode_f32(a, s);
         const int rc = device_status(e, fn);
         if (rc) return rc;

@@ -1,16 +1,17 @@
-// kvq_decode.hip -- split-K single-query decode attention for gfx950.
+// kvq_decode.hip -- stream-K single-query decode attention for gfx950.
 //
-// One workgroup (256 threads = 4 wave64s) per work item = one chunk of rows
-// of one (sequence, live KV head).  Every K and V row of the chunk is read
-// from HBM exactly once and serves all hpk Q heads of the GQA group
-// (cortiq-engine 0.3.4 kv_cache.rs, LayerKvCache::attend_group: each stored
-// row read once for all heads of its group).  Each wave streams 16-byte
-// loads, keeps an online-softmax state per Q head in registers (franken_ocr
-// 0.8.0 rswa.rs, fold: rescale the running sum and accumulator when the
-// running max grows, never materialising the score row), the four waves
-// merge in LDS, and the item writes one partial (max, sum, acc[128]) per Q
-// head.  A second kernel merges the partials of a (sequence, Q head) with
-// the same rescaling and divides.
+// The rows of every (sequence, live KV head) are cut into 16-row tiles laid
+// end to end, and each wave of a grid that is resident all at once takes an
+// equal, contiguous share of that tile stream (kvq_internal.h).  Every K and
+// V row is read from HBM exactly once and serves all hpk Q heads of the GQA
+// group (cortiq-engine 0.3.4 kv_cache.rs, LayerKvCache::attend_group: each
+// stored row read once for all heads of its group).  A wave streams its
+// share with 16-byte loads, keeps an online-softmax state per Q head in
+// registers (franken_ocr 0.8.0 rswa.rs, fold: rescale the running sum and
+// accumulator when the running max grows, never materialising the score
+// row), and writes one partial (max, sum, acc[128]) per Q head for each
+// segment its share touches.  A second kernel merges the partials of a
+// (sequence, Q head) with the same rescaling and divides.
 //
 // Scores are kept in log2 units (the query is pre-scaled by
 // log2(e)/sqrt(128)) so every exponential is one v_exp_f32.
@@ -23,7 +24,7 @@ namespace {
 
 constexpr float kQScale = 0.12751743082459868f;   // log2(e) / sqrt(128)
 constexpr double kQScale64 = 0.12751743082459868;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;   // waves per workgroup
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -55,62 +56,58 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Sequence slot of a work item: the last j with item_base[j] <= item.
-__device__ __forceinline__ int find_seq(const DecodeArgs& a, int item) {
-    int lo = 0, hi = a.n_seq - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.item_base[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+// First share [w T / W, (w + 1) T / W) holding tile t.
+__host__ __device__ inline int tile_owner(int t, int T, int W) {
+    return (int)(((int64_t)(t + 1) * W - 1) / T);
 }
 
-struct Item {
-    int j, b, gl, g, row0, row1;
+// The part of one share that lies in one (sequence, live head) segment.
+struct Piece {
+    int j, gl, b, g;
+    int row0, row1;  // rows of the segment, [row0, row1)
+    int slot;        // partial slot: share + segment index
     size_t hrow;     // first storage row of the (sequence, live head)
 };
 
-__device__ __forceinline__ Item decode_item(const DecodeArgs& a) {
-    Item it;
-    const int item = blockIdx.x;
-    it.j = find_seq(a, item);
-    const int nch = a.nchunk[it.j];
-    const int rem = item - a.item_base[it.j];
-    it.gl = rem / nch;
-    const int ch = rem - it.gl * nch;
-    it.b = a.seq0 + it.j;
-    it.g = a.live_head[it.gl];
-    it.row0 = ch * a.chunk;
-    it.row1 = min(it.row0 + a.chunk, a.len[it.j]);
-    it.hrow = ((size_t)it.b * a.n_live + it.gl) * a.capacity;
-    return it;
-}
-
-// Merge the four waves' states in LDS and write the item's partials.
-template <int HPK>
-__device__ __forceinline__ void write_partials(const DecodeArgs& a, float (*sm_acc)[HPK][kHD],
-                                               float (*sm_ml)[HPK][2]) {
-    __syncthreads();
-    const int item = blockIdx.x;
-    for (int t = threadIdx.x; t < HPK * kHD; t += kWaves * 64) {
-        const int h = t / kHD, d = t - h * kHD;
-        float M = sm_ml[0][h][0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float e = fast_exp2(sm_ml[w][h][0] - M);
-            L += e * sm_ml[w][h][1];
-            A += e * sm_acc[w][h][d];
-        }
-        const size_t ix = (size_t)item * HPK + h;
-        a.ws_acc[ix * kHD + d] = A;
-        if (d == 0) {
-            a.ws_ml[ix * 2] = M;
-            a.ws_ml[ix * 2 + 1] = L;
+// Calls f(piece) for each piece of share w, in stream order.
+template <class F>
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, F&& f) {
+    const int T = a.n_tiles, W = a.n_shares;
+    int t = (int)((int64_t)w * T / W);
+    const int t1 = (int)((int64_t)(w + 1) * T / W);
+    // sequence of tile t: the last j with tile_base[j] <= t (it has tiles)
+    int lo = 0, hi = a.n_seq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.tile_base[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    int j = lo;
+    int gl = (t - a.tile_base[j]) / a.ntile[j];
+    while (t < t1) {
+        const int nt = a.ntile[j];
+        const int sb = a.tile_base[j] + gl * nt;
+        const int pe = min(t1, sb + nt);
+        Piece p;
+        p.j = j;
+        p.gl = gl;
+        p.b = a.seq0 + j;
+        p.g = a.live_head[gl];
+        p.row0 = kTileRows * (t - sb);
+        p.row1 = min(kTileRows * (pe - sb), a.len[j]);
+        p.slot = w + j * a.n_live + gl;
+        p.hrow = ((size_t)p.b * a.n_live + gl) * a.capacity;
+        f(p);
+        t = pe;
+        if (t < t1 && ++gl == a.n_live) {   // next segment with tiles
+            gl = 0;
+            do ++j; while (a.ntile[j] == 0);
         }
     }
+}
+
+// Share of the calling wave (wave-uniform): one share per wave.
+__device__ __forceinline__ int share_index() {
+    return blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,95 +141,97 @@ __device__ __forceinline__ float reduce8_over32(const float (&v)[8], int seg) {
 
 template <int HPK>
 __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
-    __shared__ float sm_acc[kWaves][HPK][kHD];
-    __shared__ float sm_ml[kWaves][HPK][2];
-    const Item it = decode_item(a);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int w = share_index();
+    if (w >= a.n_shares) return;
+    const int lane = threadIdx.x & 63;
     const int half = lane >> 5, seg = lane & 31;
-    const float* K = a.k + it.hrow * kHD;
-    const float* V = a.v + it.hrow * kHD;
-    const int wrow = a.wrow[it.j];
-    const bool has_w = wrow >= it.row0 && wrow < it.row1;
-    const float* kn = has_w ? a.k_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : K;
-    const float* vn = has_w ? a.v_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : V;
+    for_each_piece(a, w, [&](const Piece& it) {
+        const float* K = a.k + it.hrow * kHD;
+        const float* V = a.v + it.hrow * kHD;
+        const int wrow = a.wrow[it.j];
+        const bool has_w = wrow >= it.row0 && wrow < it.row1;
+        const float* kn = has_w ? a.k_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : K;
+        const float* vn = has_w ? a.v_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : V;
 
-    // R-SWA ring write: this item owns the row, nobody else reads it.
-    if (has_w && tid < 32) {
-        *(float4*)(a.k_store + (it.hrow + wrow) * kHD + 4 * tid) = *(const float4*)(kn + 4 * tid);
-        *(float4*)(a.v_store + (it.hrow + wrow) * kHD + 4 * tid) = *(const float4*)(vn + 4 * tid);
-    }
-
-    float4 qv[HPK];
-#pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        const float4 t = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 4 * seg);
-        qv[h] = make_float4(t.x * kQScale, t.y * kQScale, t.z * kQScale, t.w * kQScale);
-    }
-    float m[HPK], l[HPK];
-    float4 acc[HPK];
-#pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-        acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    for (int r = it.row0 + wave * 16; r < it.row1; r += kWaves * 16) {
-        float4 kx[8], vx[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = min(r + 2 * i + half, it.row1 - 1);
-            const bool w = has_w && row == wrow;
-            kx[i] = ld_stream((w ? kn : K + (size_t)row * kHD) + 4 * seg);
-            vx[i] = ld_stream((w ? vn : V + (size_t)row * kHD) + 4 * seg);
+        // R-SWA ring write: this wave's share holds the row, nobody else reads it.
+        if (has_w && lane < 32) {
+            *(float4*)(a.k_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(kn + 4 * lane);
+            *(float4*)(a.v_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(vn + 4 * lane);
         }
-        const int myrow = r + 2 * (seg >> 2) + half;
+
+        float4 qv[HPK];
 #pragma unroll
         for (int h = 0; h < HPK; ++h) {
-            float part[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float d = qv[h].x * kx[i].x;
-                d = fmaf(qv[h].y, kx[i].y, d);
-                d = fmaf(qv[h].z, kx[i].z, d);
-                d = fmaf(qv[h].w, kx[i].w, d);
-                part[i] = d;
-            }
-            float s = reduce8_over32(part, seg);
-            if (myrow >= it.row1) s = -INFINITY;
-            const float mnew = fmaxf(m[h], wave_max(s));
-            const float alpha = fast_exp2(m[h] - mnew);
-            const float p = fast_exp2(s - mnew);
-            l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
-            float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pi = __shfl(p, half * 32 + 4 * i, 64);
-                ac.x = fmaf(pi, vx[i].x, ac.x);
-                ac.y = fmaf(pi, vx[i].y, ac.y);
-                ac.z = fmaf(pi, vx[i].z, ac.z);
-                ac.w = fmaf(pi, vx[i].w, ac.w);
-            }
-            acc[h] = ac;
-            m[h] = mnew;
+            const float4 t = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 4 * seg);
+            qv[h] = make_float4(t.x * kQScale, t.y * kQScale, t.z * kQScale, t.w * kQScale);
         }
-    }
+        float m[HPK], l[HPK];
+        float4 acc[HPK];
+#pragma unroll
+        for (int h = 0; h < HPK; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.0f;
+            acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 
+        for (int r = it.row0; r < it.row1; r += kTileRows) {
+            float4 kx[8], vx[8];
 #pragma unroll
-    for (int h = 0; h < HPK; ++h) {
-        const float lt = wave_sum(l[h]);
-        float4 at = acc[h];
-        at.x += __shfl_xor(at.x, 32, 64);
-        at.y += __shfl_xor(at.y, 32, 64);
-        at.z += __shfl_xor(at.z, 32, 64);
-        at.w += __shfl_xor(at.w, 32, 64);
-        if (half == 0) *(float4*)&sm_acc[wave][h][4 * seg] = at;
-        if (lane == 0) {
-            sm_ml[wave][h][0] = m[h];
-            sm_ml[wave][h][1] = lt;
+            for (int i = 0; i < 8; ++i) {
+                const int row = min(r + 2 * i + half, it.row1 - 1);
+                const bool wr = has_w && row == wrow;
+                kx[i] = ld_stream((wr ? kn : K + (size_t)row * kHD) + 4 * seg);
+                vx[i] = ld_stream((wr ? vn : V + (size_t)row * kHD) + 4 * seg);
+            }
+            const int myrow = r + 2 * (seg >> 2) + half;
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                float part[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float d = qv[h].x * kx[i].x;
+                    d = fmaf(qv[h].y, kx[i].y, d);
+                    d = fmaf(qv[h].z, kx[i].z, d);
+                    d = fmaf(qv[h].w, kx[i].w, d);
+                    part[i] = d;
+                }
+                float sc = reduce8_over32(part, seg);
+                if (myrow >= it.row1) sc = -INFINITY;
+                const float mnew = fmaxf(m[h], wave_max(sc));
+                const float alpha = fast_exp2(m[h] - mnew);
+                const float p = fast_exp2(sc - mnew);
+                l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
+                float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float pi = __shfl(p, half * 32 + 4 * i, 64);
+                    ac.x = fmaf(pi, vx[i].x, ac.x);
+                    ac.y = fmaf(pi, vx[i].y, ac.y);
+                    ac.z = fmaf(pi, vx[i].z, ac.z);
+                    ac.w = fmaf(pi, vx[i].w, ac.w);
+                }
+                acc[h] = ac;
+                m[h] = mnew;
+            }
         }
-    }
-    write_partials<HPK>(a, sm_acc, sm_ml);
+
+        // the piece's partial: (max, sum) and the two row halves' accumulators
+#pragma unroll
+        for (int h = 0; h < HPK; ++h) {
+            const float lt = wave_sum(l[h]);
+            float4 at = acc[h];
+            at.x += __shfl_xor(at.x, 32, 64);
+            at.y += __shfl_xor(at.y, 32, 64);
+            at.z += __shfl_xor(at.z, 32, 64);
+            at.w += __shfl_xor(at.w, 32, 64);
+            const size_t ix = (size_t)it.slot * HPK + h;
+            if (half == 0) *(float4*)(a.ws_acc + ix * kHD + 4 * seg) = at;
+            if (lane == 0) {
+                a.ws_ml[ix * 2] = m[h];
+                a.ws_ml[ix * 2 + 1] = lt;
+            }
+        }
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -240,8 +239,8 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 //
 // Scores are computed exactly, on the matrix cores.  The query side of a
 // score, q (.) kcol ([P1] attend: score = s_k * <q (.) col_k, k_q>), is split
-// once per work item into four balanced base-128 int8 digits relative to a
-// power of two per (Q head, K group):
+// once per piece into four balanced base-128 int8 digits relative to a power
+// of two per (Q head, K group):
 //   qc = 2^(e-27) * (((d0*128 + d1)*128 + d2)*128 + d3),  |error| <= 2^(e-28).
 // For a tile of 16 rows and one 32-channel K group, one
 // v_mfma_i32_16x16x64_i8 multiplies A = digits (16 = 4 heads x 4 digits, the
@@ -258,41 +257,31 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 // weights times the V row scales go through a per-wave LDS slot to the V
 // layout -- lane (ri = lane / kVSeg, seg = lane % kVSeg) owns rows
 // ri + kVRows * i of each tile and kVDim channels -- where V codes become f32 (one
-// sign-extending byte convert each) and accumulate per head.  The V column
-// field is applied once in the combine ([P1] attend: acc (.) vcol at the end).
+// sign-extending byte convert each) and accumulate per head in f32.  Every
+// KVQ_Q8_FLUSH tiles the f32 accumulators are summed over the four row
+// groups and added into f64 accumulators in LDS (each lane owns 2 hpk of
+// them), and the running sum of weights is f64, so a wave's long share adds
+// no error that grows with its length.  The V column field is applied once
+// in the combine ([P1] attend: acc (.) vcol at the end).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr float kLazy = 8.0f;
 
-// V layout of the q8 kernel: a load group covers kVRows rows of a 16-row tile,
-// kVSeg lanes per row, kVDim channels (one 8- or 16-byte load) per lane.
-#ifndef KVQ_Q8_VROWS
-#define KVQ_Q8_VROWS 4
-#endif
-#ifndef KVQ_Q8_TILES
-#define KVQ_Q8_TILES 1
-#endif
-constexpr int kVRows = KVQ_Q8_VROWS;
+// V layout of the q8 kernel: lane (ri = lane / 16, seg = lane % 16) owns
+// rows ri + 4 i (i < 4) of a 16-row tile and the 8 channels [8 seg, 8 seg + 8),
+// one 8-byte load per row.
+constexpr int kVRows = 4;
 constexpr int kVSeg = 64 / kVRows;
 constexpr int kVDim = kHD / kVSeg;
 constexpr int kVLoads = 16 / kVRows;
-template <int N> struct VBytes;
-template <> struct VBytes<16> { typedef uint4 type; };
-template <> struct VBytes<8> { typedef uint2 type; };
-typedef typename VBytes<kVDim>::type vbytes_t;
+#ifndef KVQ_Q8_TILES
+#define KVQ_Q8_TILES 1
+#endif
+// Tiles between two flushes of the f32 V accumulators into f64.
+#ifndef KVQ_Q8_FLUSH
+#define KVQ_Q8_FLUSH 16
+#endif
 
-__device__ __forceinline__ void unpack16(const uint4 x, float (&f)[16]) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        f[4 * k + 0] = (float)(int8_t)(w[k] & 0xffu);
-        f[4 * k + 1] = (float)(int8_t)((w[k] >> 8) & 0xffu);
-        f[4 * k + 2] = (float)(int8_t)((w[k] >> 16) & 0xffu);
-        f[4 * k + 3] = (float)((int32_t)w[k] >> 24);
-    }
-}
-
-__device__ __forceinline__ void unpack(const uint4 x, float (&f)[16]) { unpack16(x, f); }
 __device__ __forceinline__ void unpack(const uint2 x, float (&f)[8]) {
     const uint32_t w[2] = {x.x, x.y};
 #pragma unroll
@@ -304,7 +293,6 @@ __device__ __forceinline__ void unpack(const uint2 x, float (&f)[8]) {
     }
 }
 typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void ld_v(const int8_t* p, uint4& x) { x = ld_stream(p); }
 __device__ __forceinline__ void ld_v(const int8_t* p, uint2& x) {
     const v2u_t t = __builtin_nontemporal_load(reinterpret_cast<const v2u_t*>(p));
     x = make_uint2(t.x, t.y);
@@ -345,258 +333,290 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #define KVQ_Q8_MIN_WAVES 3
 #endif
 template <int HPK>
-__global__ __launch_bounds__(256, KVQ_Q8_MIN_WAVES) void k_decode_q8(const DecodeArgs a) {
+__global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
-    __shared__ float sm_acc[kWaves][HPK][kHD];
-    __shared__ float sm_ml[kWaves][HPK][2];
     __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
     __shared__ float sm_alpha[kWaves][2][HPK];        // per wave, two tiles: rescale factor per head
-    const Item it = decode_item(a);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ double sm_v64[kWaves][HPK][kHD];       // per wave: flushed V accumulators
+    const int w = share_index();
+    if (w >= a.n_shares) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int hq = lane >> 4, n = lane & 15;          // score layout
     const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
-    const int8_t* KQ = a.kq + it.hrow * kHD;
-    const float* KS = a.ks + it.hrow * kKScales;
-    const int8_t* VQ = a.vq + it.hrow * kHD;
-    const float* VS = a.vs + it.hrow;
-    const bool frz = a.frozen[it.j] != 0;
-    const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
+    for_each_piece(a, w, [&](const Piece& it) {
+        const int8_t* KQ = a.kq + it.hrow * kHD;
+        const float* KS = a.ks + it.hrow * kKScales;
+        const int8_t* VQ = a.vq + it.hrow * kHD;
+        const float* VS = a.vs + it.hrow;
+        const bool frz = a.frozen[it.j] != 0;
+        const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
-    // ---- query digits (MFMA A operand) and per-group scales ----
-    // One v_mfma_i32_16x16x64_i8 spans 64 channels = two K groups.  A[m][k]:
-    // m = lane & 15 = 4 * head + digit, k = 16 * (lane >> 4) + t of the span,
-    // so lanes with lane >> 4 in {0, 1} hold the span's first group and lanes
-    // {2, 3} its second; each group gets its own product by zeroing the other
-    // half of A.
-    const bool first_half = (lane >> 4) < 2;
-    v4i qa_lo[NB][2], qa_hi[NB][2];                   // [head block][span]
-    double gsc[NB][4];                                // for this lane's score head 4 hb + hq
-#pragma unroll
-    for (int hb = 0; hb < NB; ++hb) {
-        const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const int d0 = 64 * sp + 16 * kb;
-            double qc[16];
-            double gmax = 0.0;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) qc[t] = 0.0;
-            if (hm < HPK) {
-                const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
-#pragma unroll
-                for (int t4 = 0; t4 < 4; ++t4) {
-                    const float4 qv = *(const float4*)(qp + 4 * t4);
-                    float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
-                    if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
-                    qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
-                    qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
-                    qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
-                    qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
-                }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
-            }
-            gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
-            int e = 0;
-            (void)frexp(gmax, &e);                         // gmax < 2^e
-            const double up = ldexp(1.0, 27 - e);
-            v4i pk = {0, 0, 0, 0};
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                int x = (int)rint(qc[t] * up);             // |x| <= 2^27
-                const int d3 = take_digit(x);
-                const int d2 = take_digit(x);
-                const int d1 = take_digit(x);
-                const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
-                pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
-            }
-            const v4i zero = {0, 0, 0, 0};
-            qa_lo[hb][sp] = first_half ? pk : zero;
-            qa_hi[hb][sp] = first_half ? zero : pk;
-#pragma unroll
-            for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
-                const int es = __shfl(e, 4 * hq + 32 * gs, 64);
-                gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
-            }
-        }
-    }
-
-    float m[NB], l[NB];
-    float acc[HPK][kVDim];
-#pragma unroll
-    for (int hb = 0; hb < NB; ++hb) {
-        m[hb] = -INFINITY;
-        l[hb] = 0.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < HPK; ++h)
-#pragma unroll
-        for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
-
-    // Rows of the chunk go to the waves in 16-row tiles, kTiles tiles per
-    // step; the loads of the next step are issued before this step's
-    // arithmetic.
-    constexpr int kTiles = KVQ_Q8_TILES;
-    constexpr int kStep = 16 * kTiles * kWaves;
-    struct Tile {
-        uint4 kb2[2];                                  // B operand: 16 channels of row n per span
-        float4 ks4;
-        float vsn;
-        vbytes_t vx[kVLoads];                          // rows ri + kVRows * i, channels of seg
-    };
-    auto load_tile = [&](int r0, Tile& t) {
-        const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
-        t.ks4 = ld_stream(KS + rk * kKScales);
-        t.vsn = ld_stream1(VS + rk);
-#pragma unroll
-        for (int i = 0; i < kVLoads; ++i) {
-            const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
-            ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
-        }
-    };
-    int buf = 0;
-    auto compute_tile = [&](int r0, const Tile& t) {
-        const bool valid = r0 + n < it.row1;
-        // ---- scores (exact), softmax weights in the (head, row) layout ----
-        bool rescale = false;
+        // ---- query digits (MFMA A operand) and per-group scales ----
+        // One v_mfma_i32_16x16x64_i8 spans 64 channels = two K groups.  A[m][k]:
+        // m = lane & 15 = 4 * head + digit, k = 16 * (lane >> 4) + t of the span,
+        // so lanes with lane >> 4 in {0, 1} hold the span's first group and lanes
+        // {2, 3} its second; each group gets its own product by zeroing the other
+        // half of A.
+        const bool first_half = (lane >> 4) < 2;
+        v4i qa_lo[NB][2], qa_hi[NB][2];                   // [head block][span]
+        double gsc[NB][4];                                // for this lane's score head 4 hb + hq
 #pragma unroll
         for (int hb = 0; hb < NB; ++hb) {
-            const v4i zero = {0, 0, 0, 0};
-            double sc = 0.0;
-            const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
+            const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+                const int d0 = 64 * sp + 16 * kb;
+                double qc[16];
+                double gmax = 0.0;
 #pragma unroll
-                for (int gs = 0; gs < 2; ++gs) {
-                    const int g = 2 * sp + gs;
-                    const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(gs ? qa_hi[hb][sp] : qa_lo[hb][sp],
-                                                                         kbv, zero, 0, 0, 0);
-                    const int t1 = dsum[0] * 128 + dsum[1];
-                    const int t2 = dsum[2] * 128 + dsum[3];
-                    const double x = fma((double)t1, 16384.0, (double)t2);
-                    sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+                for (int t = 0; t < 16; ++t) qc[t] = 0.0;
+                if (hm < HPK) {
+                    const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4) {
+                        const float4 qv = *(const float4*)(qp + 4 * t4);
+                        float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
+                        if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
+                        qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
+                        qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
+                        qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
+                        qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
+                }
+                gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
+                int e = 0;
+                (void)frexp(gmax, &e);                         // gmax < 2^e
+                const double up = ldexp(1.0, 27 - e);
+                v4i pk = {0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    int x = (int)rint(qc[t] * up);             // |x| <= 2^27
+                    const int d3 = take_digit(x);
+                    const int d2 = take_digit(x);
+                    const int d1 = take_digit(x);
+                    const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
+                    pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
+                }
+                const v4i zero = {0, 0, 0, 0};
+                qa_lo[hb][sp] = first_half ? pk : zero;
+                qa_hi[hb][sp] = first_half ? zero : pk;
+#pragma unroll
+                for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
+                    const int es = __shfl(e, 4 * hq + 32 * gs, 64);
+                    gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
                 }
             }
-            const int h = 4 * hb + hq;
-            if (!valid || h >= HPK) sc = -INFINITY;
-            const float tmax = max16((float)sc);
-            float mnew = m[hb], alpha = 1.0f;
-            if (tmax > m[hb] + kLazy) {               // uniform over the head's 16 lanes
-                mnew = tmax;
-                alpha = fast_exp2(m[hb] - tmax);
-            }
-            rescale |= __any(alpha != 1.0f);
-            const float p = sc == -INFINITY ? 0.0f : fast_exp2((float)(sc - (double)mnew));
-            l[hb] = l[hb] * alpha + p;
-            m[hb] = mnew;
-            if (h < HPK) {
-                sm_pw[wave][buf][n][h] = p * t.vsn;
-                if (n == 0) sm_alpha[wave][buf][h] = alpha;
-            }
         }
-        wave_lds_sync();
 
-        // ---- V accumulation in the (row, channel) layout ----
-        if (rescale) {
+        float m[NB];
+        double l[NB];
+        float acc[HPK][kVDim];
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-                const float al = sm_alpha[wave][buf][h];
-#pragma unroll
-                for (int c = 0; c < kVDim; ++c) acc[h][c] *= al;
-            }
-        }
-        // The tile's rows are summed into a fresh register first and added to
-        // the running accumulator once per tile: the long f32 chain grows by
-        // one addition per tile instead of kVLoads (rounding error ~ sqrt(n)).
-        float ts[HPK][kVDim];
-#pragma unroll
-        for (int i = 0; i < kVLoads; ++i) {
-            float w[HPK];
-#pragma unroll
-            for (int h = 0; h < HPK; ++h) w[h] = sm_pw[wave][buf][ri + kVRows * i][h];
-            float vf[kVDim];
-            unpack(t.vx[i], vf);
-#pragma unroll
-            for (int h = 0; h < HPK; ++h)
-#pragma unroll
-                for (int c = 0; c < kVDim; ++c) ts[h][c] = i == 0 ? w[h] * vf[c] : fmaf(w[h], vf[c], ts[h][c]);
+        for (int hb = 0; hb < NB; ++hb) {
+            m[hb] = -INFINITY;
+            l[hb] = 0.0;
         }
 #pragma unroll
         for (int h = 0; h < HPK; ++h)
 #pragma unroll
-            for (int c = 0; c < kVDim; ++c) acc[h][c] += ts[h][c];
-        buf ^= 1;
-    };
+            for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
 
-    // Two register sets, ping-pong: the next step's loads are issued before
-    // this step's arithmetic.  Rows are clamped into the chunk, so a
-    // prefetch past the end re-reads the chunk's last row (and is unused).
-    auto load_step = [&](int r, Tile (&t)[kTiles]) {
+        // f64 accumulators of this lane: entries kOwn * ri + i of the seg's
+        // (head, channel) list e = kVDim * head + channel.
+        constexpr int kOwn = HPK * kVDim / kVRows;
+        auto cell = [&](int i) -> double& {
+            const int e = kOwn * ri + i;
+            return sm_v64[wave][e / kVDim][kVDim * seg + e % kVDim];
+        };
 #pragma unroll
-        for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
-    };
-    auto compute_step = [&](int r, const Tile (&t)[kTiles]) {
+        for (int i = 0; i < kOwn; ++i) cell(i) = 0.0;
+        // Sum acc over the four row groups (a transposing butterfly leaves lane
+        // ri with entries [kOwn ri, kOwn ri + kOwn)), add into f64, clear acc.
+        auto flush = [&]() {
+            constexpr int N = HPK * kVDim;
+            const bool b5 = ri & 2, b4 = ri & 1;
+            float y[N / 2], z[kOwn];
 #pragma unroll
-        for (int k = 0; k < kTiles; ++k)
-            if (r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
-    };
-    int r0 = it.row0 + 16 * kTiles * wave;
-    if (r0 < it.row1) {
-        Tile ta[kTiles], tb[kTiles];
-        load_step(r0, ta);
-        while (true) {
-            load_step(r0 + kStep, tb);
-            compute_step(r0, ta);
-            r0 += kStep;
-            if (r0 >= it.row1) break;
-            load_step(r0 + kStep, ta);
-            compute_step(r0, tb);
-            r0 += kStep;
-            if (r0 >= it.row1) break;
-        }
-    }
+            for (int i = 0; i < N / 2; ++i) {
+                const float lo = acc[i / kVDim][i % kVDim], hi = acc[(i + N / 2) / kVDim][(i + N / 2) % kVDim];
+                y[i] = (b5 ? hi : lo) + __shfl_xor(b5 ? lo : hi, 32, 64);
+            }
+#pragma unroll
+            for (int i = 0; i < kOwn; ++i)
+                z[i] = (b4 ? y[i + kOwn] : y[i]) + __shfl_xor(b4 ? y[i] : y[i + kOwn], 16, 64);
+#pragma unroll
+            for (int i = 0; i < kOwn; ++i) cell(i) += (double)z[i];
+#pragma unroll
+            for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
+        };
+        int since_flush = 0;
 
-    // ---- per-wave state -> LDS, then the 4-wave merge ----
+        // The piece's 16-row tiles, kTiles per step; the loads of the next step
+        // are issued before this step's arithmetic.
+        constexpr int kTiles = KVQ_Q8_TILES;
+        constexpr int kStep = 16 * kTiles;
+        struct Tile {
+            uint4 kb2[2];                                  // B operand: 16 channels of row n per span
+            float4 ks4;
+            float vsn;
+            uint2 vx[kVLoads];                             // rows ri + kVRows * i, channels of seg
+        };
+        auto load_tile = [&](int r0, Tile& t) {
+            const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
-    for (int hb = 0; hb < NB; ++hb) {
-        const float lt = sum16(l[hb]);
-        const int h = 4 * hb + hq;
-        if (n == 0 && h < HPK) {
-            sm_ml[wave][h][0] = m[hb];
-            sm_ml[wave][h][1] = lt;
+            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
+            t.ks4 = ld_stream(KS + rk * kKScales);
+            t.vsn = ld_stream1(VS + rk);
+#pragma unroll
+            for (int i = 0; i < kVLoads; ++i) {
+                const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
+                ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
+            }
+        };
+        int buf = 0;
+        auto compute_tile = [&](int r0, const Tile& t) {
+            const bool valid = r0 + n < it.row1;
+            // ---- scores (exact), softmax weights in the (head, row) layout ----
+            bool rescale = false;
+#pragma unroll
+            for (int hb = 0; hb < NB; ++hb) {
+                const v4i zero = {0, 0, 0, 0};
+                double sc = 0.0;
+                const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+#pragma unroll
+                    for (int gs = 0; gs < 2; ++gs) {
+                        const int g = 2 * sp + gs;
+                        const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(gs ? qa_hi[hb][sp] : qa_lo[hb][sp],
+                                                                             kbv, zero, 0, 0, 0);
+                        const int t1 = dsum[0] * 128 + dsum[1];
+                        const int t2 = dsum[2] * 128 + dsum[3];
+                        const double x = fma((double)t1, 16384.0, (double)t2);
+                        sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+                    }
+                }
+                const int h = 4 * hb + hq;
+                if (!valid || h >= HPK) sc = -INFINITY;
+                const float tmax = max16((float)sc);
+                float mnew = m[hb], alpha = 1.0f;
+                if (tmax > m[hb] + kLazy) {               // uniform over the head's 16 lanes
+                    mnew = tmax;
+                    alpha = fast_exp2(m[hb] - tmax);
+                }
+                rescale |= __any(alpha != 1.0f);
+                const float p = sc == -INFINITY ? 0.0f : fast_exp2((float)(sc - (double)mnew));
+                l[hb] = fma(l[hb], (double)alpha, (double)p);
+                m[hb] = mnew;
+                if (h < HPK) {
+                    sm_pw[wave][buf][n][h] = p * t.vsn;
+                    if (n == 0) sm_alpha[wave][buf][h] = alpha;
+                }
+            }
+            wave_lds_sync();
+
+            // ---- V accumulation in the (row, channel) layout ----
+            if (rescale) {
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) {
+                    const float al = sm_alpha[wave][buf][h];
+#pragma unroll
+                    for (int c = 0; c < kVDim; ++c) acc[h][c] *= al;
+                }
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) cell(i) *= (double)sm_alpha[wave][buf][(kOwn * ri + i) / kVDim];
+            }
+            // The tile's rows are summed into a fresh register first and added to
+            // the running accumulator once per tile: the long f32 chain grows by
+            // one addition per tile instead of kVLoads (rounding error ~ sqrt(n)).
+            float ts[HPK][kVDim];
+#pragma unroll
+            for (int i = 0; i < kVLoads; ++i) {
+                float w[HPK];
+#pragma unroll
+                for (int h = 0; h < HPK; ++h) w[h] = sm_pw[wave][buf][ri + kVRows * i][h];
+                float vf[kVDim];
+                unpack(t.vx[i], vf);
+#pragma unroll
+                for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                    for (int c = 0; c < kVDim; ++c) ts[h][c] = i == 0 ? w[h] * vf[c] : fmaf(w[h], vf[c], ts[h][c]);
+            }
+#pragma unroll
+            for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                for (int c = 0; c < kVDim; ++c) acc[h][c] += ts[h][c];
+            buf ^= 1;
+            if (++since_flush == KVQ_Q8_FLUSH) {
+                flush();
+                since_flush = 0;
+            }
+        };
+
+        // Two register sets, ping-pong: the next step's loads are issued before
+        // this step's arithmetic.  Rows are clamped into the piece, so a
+        // prefetch past its end re-reads its last row (and is unused).
+        auto load_step = [&](int r, Tile (&t)[kTiles]) {
+#pragma unroll
+            for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
+        };
+        auto compute_step = [&](int r, const Tile (&t)[kTiles]) {
+#pragma unroll
+            for (int k = 0; k < kTiles; ++k)
+                if (r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
+        };
+        int r0 = it.row0;
+        if (r0 < it.row1) {
+            Tile ta[kTiles], tb[kTiles];
+            load_step(r0, ta);
+            while (true) {
+                load_step(r0 + kStep, tb);
+                compute_step(r0, ta);
+                r0 += kStep;
+                if (r0 >= it.row1) break;
+                load_step(r0 + kStep, ta);
+                compute_step(r0, tb);
+                r0 += kStep;
+                if (r0 >= it.row1) break;
+            }
         }
-    }
+
+        // ---- the piece's partial: (max, sum) and the f64 accumulators per head ----
+        if (since_flush) flush();
 #pragma unroll
-    for (int h = 0; h < HPK; ++h) {
+        for (int hb = 0; hb < NB; ++hb) {
+            double lt = l[hb];
 #pragma unroll
-        for (int c = 0; c < kVDim; ++c) {
-            float x = acc[h][c];
-#pragma unroll
-            for (int msk = kVSeg; msk < 64; msk <<= 1) x += __shfl_xor(x, msk, 64);
-            acc[h][c] = x;
+            for (int msk = 1; msk < 16; msk <<= 1) lt += shfl_xor_f64(lt, msk);
+            const int h = 4 * hb + hq;
+            if (n == 0 && h < HPK) {
+                const size_t ix = (size_t)it.slot * HPK + h;
+                a.ws_ml[ix * 2] = m[hb];
+                a.ws_ml[ix * 2 + 1] = (float)lt;
+            }
         }
-        if (ri == 0) {
 #pragma unroll
-            for (int c4 = 0; c4 < kVDim / 4; ++c4)
-                *(float4*)&sm_acc[wave][h][kVDim * seg + 4 * c4] =
-                    make_float4(acc[h][4 * c4], acc[h][4 * c4 + 1], acc[h][4 * c4 + 2], acc[h][4 * c4 + 3]);
+        for (int i = 0; i < kOwn; ++i) {
+            const int e = kOwn * ri + i;
+            a.ws_acc[((size_t)it.slot * HPK + e / kVDim) * kHD + kVDim * seg + e % kVDim] = (float)cell(i);
         }
-    }
-    write_partials<HPK>(a, sm_acc, sm_ml);
+    });
 }
 
 // ---------------------------------------------------------------------------
-// Combine: per (sequence, Q head), merge the chunk partials with the same
-// rescaling as the fold ([P3] fold: accumulators are rescaled by
+// Combine: per (sequence, Q head), merge the partials of the segment with
+// the same rescaling as the fold ([P3] fold: accumulators are rescaled by
 // exp(old max - new max)), divide, and apply the V column field (q8 only).
-// Q heads of dead groups, and sequences with no rows, get zeros.
-// Up to 512 threads = 16 sub-groups of 32 lanes (a float4 of channels each),
-// sized to the number of chunks; a sub-group takes every ngroups-th chunk,
-// issuing the loads of up to 8 chunks at once and folding them with a
-// running max; the sub-groups then merge in LDS.
+// Empty partials (max -inf) weigh nothing.  Q heads of dead groups, and
+// sequences with no rows, get zeros.  Up to 512 threads = 16 sub-groups of
+// 32 lanes (a float4 of channels each), sized to the number of partials; a
+// sub-group takes every ngroups-th partial, issuing the loads of up to 8 at
+// once and folding them with a running max; the sub-groups then merge in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 512;
 constexpr int kCombineGroups = kCombineThreads / 32;
@@ -611,14 +631,18 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     const int g = h / a.hpk, hh = h - g * a.hpk;
     const int gl = a.live_slot[g];
     float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD;
-    if (gl < 0 || a.len[j] == 0) {
+    const int nt = a.ntile[j];
+    if (gl < 0 || nt == 0) {
         if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
-    const int nch = a.nchunk[j];
-    const size_t it0 = (size_t)a.item_base[j] + (size_t)gl * nch;
-    const float* ml = a.ws_ml + (it0 * a.hpk + hh) * 2;          // stride hpk*2 per chunk
-    const float* acc = a.ws_acc + (it0 * a.hpk + hh) * kHD;      // stride hpk*128 per chunk
+    // slots of the segment: its first..last share + segment index
+    const int sb = a.tile_base[j] + gl * nt;
+    const int first = tile_owner(sb, a.n_tiles, a.n_shares);
+    const int nch = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - first + 1;
+    const size_t it0 = (size_t)first + (size_t)j * a.n_live + gl;
+    const float* ml = a.ws_ml + (it0 * a.hpk + hh) * 2;          // stride hpk*2 per slot
+    const float* acc = a.ws_acc + (it0 * a.hpk + hh) * kHD;      // stride hpk*128 per slot
     const size_t mstride = (size_t)a.hpk * 2, astride = (size_t)a.hpk * kHD;
     const int sg = tid >> 5, lane = tid & 31;
     const int ngroups = (int)(blockDim.x >> 5);
@@ -639,7 +663,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
         float Mn = M;
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k) Mn = fmaxf(Mn, mv[k]);
-        const float r = fast_exp2(M - Mn);              // 0 while M is still -inf
+        const float r = M == Mn ? 1.0f : fast_exp2(M - Mn);   // 0 while M is still -inf
         L *= r;
         A.x *= r;
         A.y *= r;
@@ -647,7 +671,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
         A.w *= r;
 #pragma unroll
         for (int k = 0; k < kCombineBatch; ++k) {
-            const float e = fast_exp2(mv[k] - Mn);      // 0 for absent chunks
+            const float e = mv[k] == -INFINITY ? 0.0f : fast_exp2(mv[k] - Mn);   // empty partials
             L = fmaf(e, lv[k], L);
             A.x = fmaf(e, xv[k].x, A.x);
             A.y = fmaf(e, xv[k].y, A.y);
@@ -668,7 +692,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
         float Lt = 0.0f;
         float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k = 0; k < ngroups; ++k) {
-            const float e = fast_exp2(sm_m[k] - Mt);    // 0 for sub-groups without chunks
+            const float e = fast_exp2(sm_m[k] - Mt);    // 0 for sub-groups without rows
             Lt = fmaf(e, sm_l[k], Lt);
             At.x = fmaf(e, sm_acc[k][tid].x, At.x);
             At.y = fmaf(e, sm_acc[k][tid].y, At.y);
@@ -689,45 +713,81 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
 }
 
 // Threads per combine block: enough 32-lane sub-groups that each folds at
-// most one batch of chunks, between 1 and 16 sub-groups.
+// most one batch of partials, between 1 and 16 sub-groups.
 int combine_threads(const DecodeArgs& a) {
     int nmax = 1;
-    for (int j = 0; j < a.n_seq; ++j) nmax = a.nchunk[j] > nmax ? a.nchunk[j] : nmax;
+    for (int j = 0; j < a.n_seq; ++j) {
+        const int nt = a.ntile[j];
+        if (nt == 0) continue;
+        for (int gl = 0; gl < a.n_live; ++gl) {
+            const int sb = a.tile_base[j] + gl * nt;
+            const int cnt = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - tile_owner(sb, a.n_tiles, a.n_shares) + 1;
+            nmax = cnt > nmax ? cnt : nmax;
+        }
+    }
     int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
     groups = groups < 1 ? 1 : (groups > kCombineGroups ? kCombineGroups : groups);
     return 32 * groups;
 }
 
+// Waves of a decode kernel that are resident on the current device at once
+// (compute units x workgroups per unit x 4), at most kMaxWaves; cached per
+// device and kernel.  0 on a runtime error.
+constexpr int kMaxDevices = 64;
+int resident_waves(const void* kernel, int which) {
+    static int cache[kMaxDevices][8];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int& c = cache[dev][which];
+    if (c == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWaves * 64, 0) != hipSuccess) return 0;
+        const int64_t wv = (int64_t)cus * per_cu * kWaves;
+        c = (int)(wv < 1 ? 1 : (wv > kMaxWaves ? kMaxWaves : wv));
+    }
+    return c;
+}
+
+int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
+
+// Shares per launch: one per resident wave for the q8 kernel (a wave keeps
+// one 4.4-KB tile in flight beside the one it computes), one per four
+// resident waves for the f32 kernel: a wave's 16-KB tile keeps HBM busy with
+// one wave per SIMD, and fewer shares make the combine cheaper (measured on
+// MI355X, 4 x 10 heads x 32k rows: decode 52.0 vs 52.6 us, combine 9.1 vs
+// 5.0 us).
+constexpr int kF32WavesPerShare = 4;
+
+template <bool kQ8>
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
+    DecodeArgs a = args;
+    a.n_shares = 1;
+    if (a.n_tiles > 0) {
+        const void* fn = nullptr;
+        switch (a.hpk) {
+            case 1: fn = kQ8 ? (const void*)k_decode_q8<1> : (const void*)k_decode_f32<1>; break;
+            case 2: fn = kQ8 ? (const void*)k_decode_q8<2> : (const void*)k_decode_f32<2>; break;
+            case 4: fn = kQ8 ? (const void*)k_decode_q8<4> : (const void*)k_decode_f32<4>; break;
+            case 8: fn = kQ8 ? (const void*)k_decode_q8<8> : (const void*)k_decode_f32<8>; break;
+            default: return hipErrorInvalidValue;
+        }
+        const int wv = resident_waves(fn, 4 * kQ8 + hpk_index(a.hpk));
+        if (wv == 0) return hipErrorInvalidDevice;
+        const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
+        a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
+        const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
+        void* kargs[] = {&a};
+        const hipError_t e = hipLaunchKernel(fn, grid, block, kargs, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_combine<kQ8>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) {
-    if (a.n_items > 0) {
-        const dim3 grid(a.n_items), block(kWaves * 64);
-        switch (a.hpk) {
-            case 1: hipLaunchKernelGGL(k_decode_f32<1>, grid, block, 0, s, a); break;
-            case 2: hipLaunchKernelGGL(k_decode_f32<2>, grid, block, 0, s, a); break;
-            case 4: hipLaunchKernelGGL(k_decode_f32<4>, grid, block, 0, s, a); break;
-            case 8: hipLaunchKernelGGL(k_decode_f32<8>, grid, block, 0, s, a); break;
-            default: return hipErrorInvalidValue;
-        }
-    }
-    hipLaunchKernelGGL(k_combine<false>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) {
-    if (a.n_items > 0) {
-        const dim3 grid(a.n_items), block(kWaves * 64);
-        switch (a.hpk) {
-            case 1: hipLaunchKernelGGL(k_decode_q8<1>, grid, block, 0, s, a); break;
-            case 2: hipLaunchKernelGGL(k_decode_q8<2>, grid, block, 0, s, a); break;
-            case 4: hipLaunchKernelGGL(k_decode_q8<4>, grid, block, 0, s, a); break;
-            case 8: hipLaunchKernelGGL(k_decode_q8<8>, grid, block, 0, s, a); break;
-            default: return hipErrorInvalidValue;
-        }
-    }
-    hipLaunchKernelGGL(k_combine<true>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
-    return hipGetLastError();
-}
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<false>(a, s); }
+hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<true>(a, s); }
 
 }  // namespace kvq

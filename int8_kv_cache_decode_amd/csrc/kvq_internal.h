@@ -19,19 +19,17 @@ constexpr int kKGroup = KVQ_K_GROUP;        // K channels per scale
 constexpr int kKScales = kHD / kKGroup;     // K scales per row (4)
 constexpr int kSeqPerLaunch = 128;
 
-// Work split of the decode kernels: a (sequence, live KV head) row range is
-// cut into chunks of `chunk` rows, one workgroup per chunk.  The chunk is the
-// smallest multiple of kChunkAlign (and at least kChunkMin) that keeps the
-// number of chunks of a launch near kTargetItems.
-#ifndef KVQ_TARGET_ITEMS
-#define KVQ_TARGET_ITEMS 2048
-#endif
-#ifndef KVQ_CHUNK_MIN
-#define KVQ_CHUNK_MIN 64
-#endif
-constexpr int kTargetItems = KVQ_TARGET_ITEMS;
-constexpr int kChunkMin = KVQ_CHUNK_MIN;
-constexpr int kChunkAlign = 64;
+// Work split of the decode kernels (stream-K): the rows of every (sequence,
+// live KV head) of a launch are cut into 16-row tiles, laid end to end in
+// sequence-major, head-minor order, and the tile stream is divided into
+// n_shares contiguous, equal shares, one per wave of a grid that is resident
+// all at once.  A wave folds its share segment by segment and writes one
+// partial per segment its share touches, in slot share + segment; the
+// combine kernel merges the slots of a segment, a contiguous range.
+// kMaxWaves bounds n_shares (and so the workspace): 256 compute units x 32
+// wave slots.
+constexpr int kTileRows = 16;
+constexpr int kMaxWaves = 8192;
 
 // ---- codec ---------------------------------------------------------------
 struct AppendArgs {
@@ -88,8 +86,8 @@ struct DecodeArgs {
     const float* vs;
     const float* kcol;
     const float* vcol;
-    float* ws_acc;             // [items][hpk][128] partial weighted V sums
-    float* ws_ml;              // [items][hpk][2]   partial (max, sum) in log2 units
+    float* ws_acc;             // [slots][hpk][128] partial weighted V sums
+    float* ws_ml;              // [slots][hpk][2]   partial (max, sum) in log2 units
     const float* k_new;        // R-SWA step K/V [batch][n_kv_heads][128] (or null)
     const float* v_new;
     float* k_store;            // writable f32 storage for the ring write
@@ -99,18 +97,21 @@ struct DecodeArgs {
     int n_q_heads;
     int hpk;
     int capacity;
-    int chunk;                 // rows per work item
     int n_seq;                 // sequences in this launch
     int seq0;                  // first absolute sequence of this launch
-    int n_items;
+    int n_tiles;               // 16-row tiles of the launch over all (sequence, live head)
+    int n_shares;              // shares of the tile stream (set by the launcher, <= n_tiles)
     int8_t live_head[KVQ_MAX_KV_HEADS];      // KV head of live slot
     int8_t live_slot[KVQ_MAX_KV_HEADS];      // live slot of KV head, -1 dead
-    int32_t item_base[kSeqPerLaunch + 1];    // first item of each sequence
-    int32_t nchunk[kSeqPerLaunch];           // chunks per (sequence, live head)
+    int32_t tile_base[kSeqPerLaunch + 1];    // first tile of each sequence (its live heads in order)
+    int32_t ntile[kSeqPerLaunch];            // tiles per (sequence, live head) = ceil(len / 16)
     int32_t len[kSeqPerLaunch];              // rows attended
     int32_t wrow[kSeqPerLaunch];             // R-SWA row taken from k_new/v_new, -1 none
     uint8_t frozen[kSeqPerLaunch];           // q8: column fields hold the frozen RMS
 };
+
+// Partial slots a launch can use: n_shares + n_seq * n_live.
+inline size_t max_slots(int n_seq, int n_live) { return (size_t)kMaxWaves + (size_t)n_seq * n_live; }
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
