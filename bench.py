@@ -190,17 +190,23 @@ def main():
     value = positions / (ms_per_step / 1e3)
 
     # ---------------- per-part kernel timing with HIP events ----------------
-    def time_calls(fn, n):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        fn(0)
-        torch.cuda.synchronize()
-        s.record(stream)
-        for i in range(n):
+    # 5 untimed calls, then 5 repeats of n back-to-back calls, each bracketed
+    # by two events on the launch stream; the median repeat's average call.
+    def time_calls(fn, n, repeats=5):
+        for i in range(5):
             fn(i)
-        e.record(stream)
-        e.synchronize()
-        return s.elapsed_time(e) / n * 1e3      # us per call
+        torch.cuda.synchronize()
+        per_call = []
+        for _ in range(repeats):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for i in range(n):
+                fn(i)
+            e.record(stream)
+            e.synchronize()
+            per_call.append(s.elapsed_time(e) / n * 1e3)      # us per call
+        return float(np.median(per_call))
 
     parts = {}
     if do_rswa:
@@ -208,7 +214,7 @@ def main():
             c, rings, out = rswa[i % len(rswa)]
             q, kk, vv = pool[i % 16]
             K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
-        us = min(time_calls(rswa_call, 50) for _ in range(3))
+        us = time_calls(rswa_call, 100)
         nb = algorithmic_bytes_rswa(rs.prefill + rs.window, rs.n_heads)
         parts["rswa_decode_f32"] = {
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
@@ -217,7 +223,7 @@ def main():
     if do_q8:
         def q8_call(i):
             K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)
-        us = min(time_calls(q8_call, 20) for _ in range(3))
+        us = time_calls(q8_call, 50)
         nb = algorithmic_bytes_q8(cq.len, cq.n_live, bq.n_q_heads)
         parts["decode_attn_q8"] = {
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
@@ -227,7 +233,7 @@ def main():
         def app_call(i):
             K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
         if int(cq.len.max()) + 40 <= cq.capacity:
-            parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 10), 2)}
+            parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 5, repeats=1), 2)}
 
     dominant = "decode_attn_q8" if do_q8 else "rswa_decode_f32"
     kernel_tag = "k_decode_q8_batched_q8" if do_q8 else "k_decode_f32_rswa_long_f32"

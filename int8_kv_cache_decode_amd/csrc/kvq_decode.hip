@@ -351,6 +351,38 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         const bool frz = a.frozen[it.j] != 0;
         const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
+        // The piece's 16-row tiles, kTiles per step; the loads of the next step
+        // are issued before this step's arithmetic.
+        constexpr int kTiles = KVQ_Q8_TILES;
+        constexpr int kStep = 16 * kTiles;
+        struct Tile {
+            uint4 kb2[2];                                  // B operand: 16 channels of row n per span
+            float4 ks4;
+            float vsn;
+            uint2 vx[kVLoads];                             // rows ri + kVRows * i, channels of seg
+        };
+        auto load_tile = [&](int r0, Tile& t) {
+            const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
+            t.ks4 = ld_stream(KS + rk * kKScales);
+            t.vsn = ld_stream1(VS + rk);
+#pragma unroll
+            for (int i = 0; i < kVLoads; ++i) {
+                const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
+                ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
+            }
+        };
+        auto load_step = [&](int r, Tile (&t)[kTiles]) {
+#pragma unroll
+            for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
+        };
+        // The first step's loads go out before the query set-up below (a piece
+        // is never empty).
+        int r0 = it.row0;
+        Tile ta[kTiles], tb[kTiles];
+        load_step(r0, ta);
+
         // ---- query digits (MFMA A operand) and per-group scales ----
         // One v_mfma_i32_16x16x64_i8 spans 64 channels = two K groups.  A[m][k]:
         // m = lane & 15 = 4 * head + digit, k = 16 * (lane >> 4) + t of the span,
@@ -455,28 +487,6 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         };
         int since_flush = 0;
 
-        // The piece's 16-row tiles, kTiles per step; the loads of the next step
-        // are issued before this step's arithmetic.
-        constexpr int kTiles = KVQ_Q8_TILES;
-        constexpr int kStep = 16 * kTiles;
-        struct Tile {
-            uint4 kb2[2];                                  // B operand: 16 channels of row n per span
-            float4 ks4;
-            float vsn;
-            uint2 vx[kVLoads];                             // rows ri + kVRows * i, channels of seg
-        };
-        auto load_tile = [&](int r0, Tile& t) {
-            const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
-            t.ks4 = ld_stream(KS + rk * kKScales);
-            t.vsn = ld_stream1(VS + rk);
-#pragma unroll
-            for (int i = 0; i < kVLoads; ++i) {
-                const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
-                ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
-            }
-        };
         int buf = 0;
         auto compute_tile = [&](int r0, const Tile& t) {
             const bool valid = r0 + n < it.row1;
@@ -561,29 +571,20 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         // Two register sets, ping-pong: the next step's loads are issued before
         // this step's arithmetic.  Rows are clamped into the piece, so a
         // prefetch past its end re-reads its last row (and is unused).
-        auto load_step = [&](int r, Tile (&t)[kTiles]) {
-#pragma unroll
-            for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
-        };
         auto compute_step = [&](int r, const Tile (&t)[kTiles]) {
 #pragma unroll
             for (int k = 0; k < kTiles; ++k)
                 if (r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
         };
-        int r0 = it.row0;
-        if (r0 < it.row1) {
-            Tile ta[kTiles], tb[kTiles];
-            load_step(r0, ta);
-            while (true) {
-                load_step(r0 + kStep, tb);
-                compute_step(r0, ta);
-                r0 += kStep;
-                if (r0 >= it.row1) break;
-                load_step(r0 + kStep, ta);
-                compute_step(r0, tb);
-                r0 += kStep;
-                if (r0 >= it.row1) break;
-            }
+        while (true) {
+            load_step(r0 + kStep, tb);
+            compute_step(r0, ta);
+            r0 += kStep;
+            if (r0 >= it.row1) break;
+            load_step(r0 + kStep, ta);
+            compute_step(r0, tb);
+            r0 += kStep;
+            if (r0 >= it.row1) break;
         }
 
         // ---- the piece's partial: (max, sum) and the f64 accumulators per head ----
