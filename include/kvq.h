@@ -47,6 +47,7 @@ extern "C" {
 #define KVQ_COL_WARMUP    64    /* rows before the column field freezes ([P1] const KV_COL_WARMUP) */
 #define KVQ_RING_WINDOW   128   /* R-SWA ring slots ([P3] const RING_WINDOW) */
 #define KVQ_MAX_KV_HEADS  64
+#define KVQ_MAX_CAPACITY  (1 << 24)   /* rows per (sequence, head): 32-bit offsets */
 #define KVQ_ALL_SEQS      (-1)  /* `seq` value: one row for every sequence */
 
 #define KVQ_OK         0
@@ -131,8 +132,8 @@ typedef struct kvq_ring {
  * `alive` (host [n_kv_heads], nonzero = live; NULL = all live), len[] = 0,
  * frozen[] = 0, device pointers NULL.  `len_host` and `frozen_host` are
  * caller-owned host arrays of `batch` entries and must outlive the cache.
- * Errors: KVQ_EINVAL (kind, head_dim != 128, batch/capacity < 1,
- * n_kv_heads outside 1..64, null arrays).
+ * Errors: KVQ_EINVAL (kind, head_dim != 128, batch < 1, capacity outside
+ * 1..KVQ_MAX_CAPACITY, n_kv_heads outside 1..64, null arrays).
  */
 int kvq_cache_init(kvq_cache* c, int kind, int batch, int n_kv_heads, int head_dim,
                    int capacity, const uint8_t* alive, int32_t* len_host,

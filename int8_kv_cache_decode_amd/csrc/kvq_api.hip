@@ -35,7 +35,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_cache(const kvq_cache* c, int kind, const char* fn) {
     if (!c) return fail(KVQ_EINVAL, "%s: null cache", fn);
     if (c->head_dim != KVQ_HEAD_DIM) return fail(KVQ_EINVAL, "%s: head_dim %d != 128", fn, c->head_dim);
-    if (c->batch < 1 || c->capacity < 1) return fail(KVQ_EINVAL, "%s: batch %d / capacity %d must be >= 1", fn, c->batch, c->capacity);
+    if (c->batch < 1 || c->capacity < 1 || c->capacity > KVQ_MAX_CAPACITY)
+        return fail(KVQ_EINVAL, "%s: batch %d must be >= 1, capacity %d within 1..%d", fn, c->batch, c->capacity,
+                    KVQ_MAX_CAPACITY);
     if (c->n_kv_heads < 1 || c->n_kv_heads > KVQ_MAX_KV_HEADS)
         return fail(KVQ_EINVAL, "%s: n_kv_heads %d outside 1..%d", fn, c->n_kv_heads, KVQ_MAX_KV_HEADS);
     int live = 0;
@@ -264,7 +266,8 @@ int kvq_cache_init(kvq_cache* c, int kind, int batch, int n_kv_heads, int head_d
     if (!c) return fail(KVQ_EINVAL, "%s: null cache", fn);
     if (kind != KVQ_KIND_F32 && kind != KVQ_KIND_Q8) return fail(KVQ_EINVAL, "%s: unknown kind %d", fn, kind);
     if (head_dim != KVQ_HEAD_DIM) return fail(KVQ_EINVAL, "%s: head_dim %d != 128", fn, head_dim);
-    if (batch < 1 || capacity < 1) return fail(KVQ_EINVAL, "%s: batch/capacity must be >= 1", fn);
+    if (batch < 1 || capacity < 1 || capacity > KVQ_MAX_CAPACITY)
+        return fail(KVQ_EINVAL, "%s: batch must be >= 1 and capacity within 1..%d", fn, KVQ_MAX_CAPACITY);
     if (n_kv_heads < 1 || n_kv_heads > KVQ_MAX_KV_HEADS)
         return fail(KVQ_EINVAL, "%s: n_kv_heads %d outside 1..%d", fn, n_kv_heads, KVQ_MAX_KV_HEADS);
     if (!len_host || !frozen_host) return fail(KVQ_EINVAL, "%s: null len/frozen host arrays", fn);

@@ -361,16 +361,18 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             float vsn;
             uint2 vx[kVLoads];                             // rows ri + kVRows * i, channels of seg
         };
+        // Offsets within the (sequence, head) block are 32-bit (capacity <=
+        // 2^24 rows), so the loads take the block's base from scalar registers.
         auto load_tile = [&](int r0, Tile& t) {
-            const size_t rk = (size_t)min(r0 + n, it.row1 - 1);
+            const uint32_t rk = (uint32_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + rk * kHD + 64 * sp + 16 * (lane >> 4));
+            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + (rk * kHD + 64 * sp + 16 * (lane >> 4)));
             t.ks4 = ld_stream(KS + rk * kKScales);
             t.vsn = ld_stream1(VS + rk);
 #pragma unroll
             for (int i = 0; i < kVLoads; ++i) {
-                const size_t rv = (size_t)min(r0 + ri + kVRows * i, it.row1 - 1);
-                ld_v(VQ + rv * kHD + kVDim * seg, t.vx[i]);
+                const uint32_t rv = (uint32_t)min(r0 + ri + kVRows * i, it.row1 - 1);
+                ld_v(VQ + (rv * kHD + kVDim * seg), t.vx[i]);
             }
         };
         auto load_step = [&](int r, Tile (&t)[kTiles]) {
@@ -541,10 +543,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #pragma unroll
                 for (int i = 0; i < kOwn; ++i) cell(i) *= (double)sm_alpha[wave][buf][(kOwn * ri + i) / kVDim];
             }
-            // The tile's rows are summed into a fresh register first and added to
-            // the running accumulator once per tile: the long f32 chain grows by
-            // one addition per tile instead of kVLoads (rounding error ~ sqrt(n)).
-            float ts[HPK][kVDim];
+            // f32 FMA chains of 4 rows per tile between two f64 flushes
 #pragma unroll
             for (int i = 0; i < kVLoads; ++i) {
                 float w[HPK];
@@ -555,12 +554,8 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #pragma unroll
                 for (int h = 0; h < HPK; ++h)
 #pragma unroll
-                    for (int c = 0; c < kVDim; ++c) ts[h][c] = i == 0 ? w[h] * vf[c] : fmaf(w[h], vf[c], ts[h][c]);
+                    for (int c = 0; c < kVDim; ++c) acc[h][c] = fmaf(w[h], vf[c], acc[h][c]);
             }
-#pragma unroll
-            for (int h = 0; h < HPK; ++h)
-#pragma unroll
-                for (int c = 0; c < kVDim; ++c) acc[h][c] += ts[h][c];
             buf ^= 1;
             if (++since_flush == KVQ_Q8_FLUSH) {
                 flush();

@@ -72,6 +72,11 @@ def test_cache_init_validation():
     assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 8, 64, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
     assert L.kvq_cache_init(ctypes.byref(c), 1, 0, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
     assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 65, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    # capacity 1..2^24 (offsets inside a head block are 32-bit)
+    assert L.kvq_cache_init(ctypes.byref(c), 2, 2, 8, 128, 0, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 2, 2, 8, 128, (1 << 24) + 1, None, ln.ctypes.data,
+                            fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 2, 1, 1, 128, 1 << 24, None, ln.ctypes.data, fr.ctypes.data) == K.OK
     assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 8, 128, 16, None, None, fr.ctypes.data) == K.EINVAL
     alive = np.array([1, 1, 0, 1, 1, 0, 1, 1], np.uint8)
     assert L.kvq_cache_init(ctypes.byref(c), 2, 2, 8, 128, 16, alive.ctypes.data,
