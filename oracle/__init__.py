@@ -69,6 +69,11 @@ def _load():
         L.orc_attend_f32.restype = None
         L.orc_attend_q8.argtypes = [i, i, i, P, P, P, P, P, P, P, P]
         L.orc_attend_q8.restype = None
+        d = ctypes.c_double
+        L.orc_attend_f32_ex.argtypes = [i, i, i, P, P, P, i, d, P, P]
+        L.orc_attend_f32_ex.restype = None
+        L.orc_attend_q8_ex.argtypes = [i, i, i, P, P, P, P, P, P, P, i, d, P, P]
+        L.orc_attend_q8_ex.restype = None
         L.orc_weights_f32.argtypes = [i, i, P, P, P]
         L.orc_weights_f32.restype = None
         _lib = L
@@ -168,8 +173,20 @@ class Q8Head:
 # --------------------------------------------------------------------------
 # Attention by definition (float64)
 # --------------------------------------------------------------------------
-def attend_f32(q, k, v) -> np.ndarray:
-    """q [hpk][hd] (or [hd]), k/v [n][hd] f32 -> out float64 like q."""
+def _sinks(sinks, hpk):
+    if sinks is None:
+        return None
+    z = np.ascontiguousarray(np.asarray(sinks, np.float32).reshape(-1))
+    assert z.shape[0] == hpk, "one sink logit per Q head of the group"
+    return z
+
+
+def attend_f32(q, k, v, first: int = 0, softcap: float = 0.0, sinks=None) -> np.ndarray:
+    """q [hpk][hd] (or [hd]), k/v [n][hd] f32 -> out float64 like q.
+
+    first / softcap / sinks: [P2] attend_group_upto's visible-row start,
+    Gemma-2 logit soft-cap (0 = off) and per-head learned sink logits
+    (None = no sinks)."""
     q = _f32(q)
     squeeze = q.ndim == 1
     q2 = q.reshape(1, -1) if squeeze else q
@@ -177,11 +194,12 @@ def attend_f32(q, k, v) -> np.ndarray:
     k, v = _f32(k).reshape(-1, hd), _f32(v).reshape(-1, hd)
     n = k.shape[0]
     out = np.zeros((hpk, hd), np.float64)
-    _load().orc_attend_f32(n, hd, hpk, _p(q2), _p(k), _p(v), _p(out))
+    z = _sinks(sinks, hpk)
+    _load().orc_attend_f32_ex(n, hd, hpk, _p(q2), _p(k), _p(v), int(first), float(softcap), _p(z), _p(out))
     return out[0] if squeeze else out
 
 
-def attend_q8(q, head: Q8Head) -> np.ndarray:
+def attend_q8(q, head: Q8Head, first: int = 0, softcap: float = 0.0, sinks=None) -> np.ndarray:
     q = _f32(q)
     squeeze = q.ndim == 1
     q2 = q.reshape(1, -1) if squeeze else q
@@ -189,8 +207,9 @@ def attend_q8(q, head: Q8Head) -> np.ndarray:
     out = np.zeros((hpk, hd), np.float64)
     kcol = head.kcol if head.frozen else None
     vcol = head.vcol if head.frozen else None
-    _load().orc_attend_q8(head.n, hd, hpk, _p(q2), _p(head.kq), _p(head.ks), _p(kcol),
-                          _p(head.vq), _p(head.vs), _p(vcol), _p(out))
+    z = _sinks(sinks, hpk)
+    _load().orc_attend_q8_ex(head.n, hd, hpk, _p(q2), _p(head.kq), _p(head.ks), _p(kcol),
+                             _p(head.vq), _p(head.vs), _p(vcol), int(first), float(softcap), _p(z), _p(out))
     return out[0] if squeeze else out
 
 
@@ -203,7 +222,8 @@ def weights_f32(q, k) -> np.ndarray:
     return w
 
 
-def decode(q, units, n_kv_heads: int, threads: int = 1, only=None) -> np.ndarray:
+def decode(q, units, n_kv_heads: int, threads: int = 1, only=None, first=None, softcap: float = 0.0,
+           sinks=None) -> np.ndarray:
     """Batched decode by definition.
 
     q      [B][Hq][hd] f32
@@ -212,6 +232,8 @@ def decode(q, units, n_kv_heads: int, threads: int = 1, only=None) -> np.ndarray
     Returns out [B][Hq][hd] float64; Q heads h of group g = h // (Hq/Hkv)
     ([P1] attend_group), zeros for dead/empty groups.
     only   optional iterable of (b, g) pairs to compute (others left 0).
+    first  optional [B] first visible row per sequence; softcap, sinks [Hq]
+           as attend_f32.
     """
     q = _f32(q)
     B, Hq, hd = q.shape
@@ -226,10 +248,12 @@ def decode(q, units, n_kv_heads: int, threads: int = 1, only=None) -> np.ndarray
         if u is None:
             return
         qg = np.ascontiguousarray(q[b, g * hpk:(g + 1) * hpk])
+        f = 0 if first is None else int(first[b])
+        z = None if sinks is None else np.asarray(sinks, np.float32)[g * hpk:(g + 1) * hpk]
         if u[0] == "f32":
-            out[b, g * hpk:(g + 1) * hpk] = attend_f32(qg, u[1], u[2])
+            out[b, g * hpk:(g + 1) * hpk] = attend_f32(qg, u[1], u[2], f, softcap, z)
         else:
-            out[b, g * hpk:(g + 1) * hpk] = attend_q8(qg, u[1])
+            out[b, g * hpk:(g + 1) * hpk] = attend_q8(qg, u[1], f, softcap, z)
 
     if threads <= 1:
         for bg in todo:

@@ -227,27 +227,41 @@ static double q8_elem(const void* ctx, int p, int d)
     return x;
 }
 
+/* Beyond the plain definition, [P2] LayerKvCache::attend_group_upto takes:
+ *   first    only rows [first, n) are visible; first is clamped to n - 1, so
+ *            at least one row is (rows before it get probability 0);
+ *   softcap  > 0: the scaled scores are soft-capped (Gemma-2),
+ *            s = softcap * tanh(s / softcap); 0 leaves them as they are;
+ *   sinks    NULL, or one learned logit per head that joins the softmax as a
+ *            column without a value row: it takes part in the max and adds
+ *            exp(sink - max) to the denominator; it is not capped.        */
 static void attend_generic(int n, int hd, int hpk, const float* q,
                            orc_elem_fn kf, const void* kctx,
-                           orc_elem_fn vf, const void* vctx, double* out)
+                           orc_elem_fn vf, const void* vctx,
+                           int first, double softcap, const float* sinks, double* out)
 {
     for (int i = 0; i < hpk * hd; ++i) out[i] = 0.0;
     if (n <= 0) return;
+    if (first > n - 1) first = n - 1;
+    if (first < 0) first = 0;
     double scale = 1.0 / sqrt((double)hd);
     double* s = (double*)malloc(sizeof(double) * (size_t)n);
     for (int h = 0; h < hpk; ++h) {
         const float* qh = q + (size_t)h * hd;
         double* oh = out + (size_t)h * hd;
-        for (int p = 0; p < n; ++p) {
+        for (int p = first; p < n; ++p) {
             double dot = 0.0;
             for (int d = 0; d < hd; ++d) dot += (double)qh[d] * kf(kctx, p, d);
             s[p] = dot * scale;
+            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);
         }
-        double m = s[0];
-        for (int p = 1; p < n; ++p) if (s[p] > m) m = s[p];
+        double m = s[first];
+        for (int p = first + 1; p < n; ++p) if (s[p] > m) m = s[p];
+        if (sinks != NULL && (double)sinks[h] > m) m = (double)sinks[h];
         double z = 0.0;
-        for (int p = 0; p < n; ++p) { s[p] = exp(s[p] - m); z += s[p]; }
-        for (int p = 0; p < n; ++p) {
+        for (int p = first; p < n; ++p) { s[p] = exp(s[p] - m); z += s[p]; }
+        if (sinks != NULL) z += exp((double)sinks[h] - m);
+        for (int p = first; p < n; ++p) {
             double w = s[p] / z;
             for (int d = 0; d < hd; ++d) oh[d] += w * vf(vctx, p, d);
         }
@@ -256,24 +270,39 @@ static void attend_generic(int n, int hd, int hpk, const float* q,
 }
 
 /* f32 rows: k[n][hd], v[n][hd]. */
-void orc_attend_f32(int n, int hd, int hpk, const float* q,
-                    const float* k, const float* v, double* out)
+void orc_attend_f32_ex(int n, int hd, int hpk, const float* q,
+                       const float* k, const float* v,
+                       int first, double softcap, const float* sinks, double* out)
 {
     orc_f32_rows kc = { k, hd };
     orc_f32_rows vc = { v, hd };
-    attend_generic(n, hd, hpk, q, f32_elem, &kc, f32_elem, &vc, out);
+    attend_generic(n, hd, hpk, q, f32_elem, &kc, f32_elem, &vc, first, softcap, sinks, out);
+}
+
+void orc_attend_f32(int n, int hd, int hpk, const float* q,
+                    const float* k, const float* v, double* out)
+{
+    orc_attend_f32_ex(n, hd, hpk, q, k, v, 0, 0.0, NULL, out);
 }
 
 /* q8 rows: kq[n][hd], ks[n][ceil(hd/32)], vq[n][hd], vs[n]; kcol/vcol [hd] or
  * NULL (not frozen). */
+void orc_attend_q8_ex(int n, int hd, int hpk, const float* q,
+                      const int8_t* kq, const float* ks, const float* kcol,
+                      const int8_t* vq, const float* vs, const float* vcol,
+                      int first, double softcap, const float* sinks, double* out)
+{
+    orc_q8_rows kc = { kq, ks, kcol, hd, ORC_K_GROUP, ceil_div(hd, ORC_K_GROUP) };
+    orc_q8_rows vc = { vq, vs, vcol, hd, hd, 1 };
+    attend_generic(n, hd, hpk, q, q8_elem, &kc, q8_elem, &vc, first, softcap, sinks, out);
+}
+
 void orc_attend_q8(int n, int hd, int hpk, const float* q,
                    const int8_t* kq, const float* ks, const float* kcol,
                    const int8_t* vq, const float* vs, const float* vcol,
                    double* out)
 {
-    orc_q8_rows kc = { kq, ks, kcol, hd, ORC_K_GROUP, ceil_div(hd, ORC_K_GROUP) };
-    orc_q8_rows vc = { vq, vs, vcol, hd, hd, 1 };
-    attend_generic(n, hd, hpk, q, q8_elem, &kc, q8_elem, &vc, out);
+    orc_attend_q8_ex(n, hd, hpk, q, kq, ks, kcol, vq, vs, vcol, 0, 0.0, NULL, out);
 }
 
 /* Attention weights alone (for the sum-to-one invariant): w[n] for one query

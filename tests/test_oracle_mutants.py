@@ -34,6 +34,15 @@ MUTANTS = {
                        "* (double)r->scales[(size_t)p * r->ns + (d / r->group) % 2];"),
     "fused_rms": ("float sq = x * x;\n            col[d] = col[d] + sq;", "col[d] = fmaf(x, x, col[d]);"),
     "requant_wrong_row": ("orc_quant_row(rows + (size_t)p * hd, col", "orc_quant_row(rows + 0 * (size_t)p * hd, col"),
+    "window_clamp_two_rows": ("if (first > n - 1) first = n - 1;", "if (first > n - 1) first = n - 2 < 0 ? 0 : n - 2;"),
+    "sink_not_in_denominator": ("if (sinks != NULL) z += exp((double)sinks[h] - m);", ""),
+    "sink_scaled": ("z += exp((double)sinks[h] - m);", "z += exp((double)sinks[h] * scale - m);"),
+    "sink_capped": ("z += exp((double)sinks[h] - m);",
+                    "z += exp((softcap > 0.0 ? softcap * tanh((double)sinks[h] / softcap) : (double)sinks[h]) - m);"),
+    "softcap_missing_factor": ("s[p] = softcap * tanh(s[p] / softcap);", "s[p] = tanh(s[p] / softcap);"),
+    "softcap_before_scale": ("s[p] = dot * scale;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);",
+                             "s[p] = dot;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);\n"
+                             "            s[p] = s[p] * scale;"),
 }
 
 RUNNER = r'''

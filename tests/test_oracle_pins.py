@@ -9,6 +9,7 @@ the f32 codec.
 
 Pages:
   [P1] cortiq-engine 0.3.4, src/cortiq_engine/kv_cache.rs
+  [P2] cortiq-engine 0.8.49, src/cortiq_engine/kv_cache.rs
   [P3] franken_ocr 0.8.0, src/native_engine/rswa.rs
 """
 import decimal
@@ -474,6 +475,154 @@ def test_q8_attention_equals_attention_on_dequantised_rows():
     tk = torch.from_numpy(kk)[None, None].expand(1, 4, 100, HD).contiguous()
     tv = torch.from_numpy(vv)[None, None].expand(1, 4, 100, HD).contiguous()
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# Visible-row start, logit soft-cap and learned sinks ([P2] attend_group_upto)
+# ---------------------------------------------------------------------------
+def sdpa_bias(q, k, v, bias):
+    """torch SDPA in float64 with an additive score bias [hpk][n] (-inf masks
+    a row); k, v [n][hd] shared by the hpk query heads."""
+    hpk, hd = q.shape
+    n = k.shape[0]
+    tq = torch.from_numpy(np.asarray(q, np.float64))[None, :, None, :]
+    tk = torch.from_numpy(np.asarray(k, np.float64))[None, None].expand(1, hpk, n, hd).contiguous()
+    tv = torch.from_numpy(np.asarray(v, np.float64))[None, None].expand(1, hpk, n, hd).contiguous()
+    tb = torch.from_numpy(np.asarray(bias, np.float64))[None, :, None, :]
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tb)[0, :, 0, :].numpy()
+
+
+def options_reference(q, k, v, first, softcap, sinks):
+    """The options through torch: rows before the (clamped) first are masked
+    with -inf, the cap enters as the bias cap*tanh(s/cap) - s on torch's own
+    scaled scores, and a sink is one extra key row of zeros (score 0) with a
+    zero value row and bias = the sink logit."""
+    hpk, hd = q.shape
+    n = k.shape[0]
+    f = min(max(first, 0), n - 1)
+    s = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) / math.sqrt(hd)
+    bias = np.zeros((hpk, n))
+    if softcap > 0:
+        bias = softcap * np.tanh(s / softcap) - s
+    bias[:, :f] = -np.inf
+    if sinks is None:
+        return sdpa_bias(q, k, v, bias)
+    k2 = np.concatenate([np.asarray(k, np.float64), np.zeros((1, hd))])
+    v2 = np.concatenate([np.asarray(v, np.float64), np.zeros((1, hd))])
+    bias2 = np.concatenate([bias, np.asarray(sinks, np.float64).reshape(hpk, 1)], axis=1)
+    return sdpa_bias(q, k2, v2, bias2)
+
+
+@pytest.mark.parametrize("n,first", [(1, 0), (9, 0), (9, 1), (9, 8), (9, 9), (9, 40), (300, 217)])
+def test_window_equals_masked_rows(n, first):
+    """[P2] attend_group_upto: only rows [first, stored) are scored, first is
+    clamped to stored - 1, and the result equals the softmax over the whole
+    row with -inf before first (page test windowed_attend_equals_masked_full_row)."""
+    r = rng(3000 + n + first)
+    q = r.standard_normal((3, HD)).astype(np.float32)
+    k = (r.standard_normal((n, HD)) * 2).astype(np.float32)
+    v = r.standard_normal((n, HD)).astype(np.float32)
+    got = oracle.attend_f32(q, k, v, first=first)
+    np.testing.assert_allclose(got, options_reference(q, k, v, first, 0.0, None), rtol=0, atol=1e-12)
+    if first >= n:                                    # one visible row: its value, exactly
+        assert np.array_equal(got, np.repeat(v[n - 1:n].astype(np.float64), 3, axis=0))
+
+
+@pytest.mark.parametrize("cap", [0.5, 4.0, 30.0])
+def test_softcap_matches_sdpa_with_tanh_bias(cap):
+    """[P2] attend_group_upto, Gemma-2 soft-capping of the scaled scores."""
+    r = rng(3100 + int(cap * 10))
+    q = (r.standard_normal((4, HD)) * 3).astype(np.float32)
+    k = (r.standard_normal((50, HD)) * 3).astype(np.float32)
+    v = r.standard_normal((50, HD)).astype(np.float32)
+    got = oracle.attend_f32(q, k, v, softcap=cap)
+    np.testing.assert_allclose(got, options_reference(q, k, v, 0, cap, None), rtol=0, atol=1e-12)
+
+
+def test_softcap_closed_forms():
+    """Two keys: weights 1 : exp(c tanh(s2/c) - c tanh(s1/c)); a huge cap is
+    no cap; a tiny cap squeezes every score into (-c, c), so the output tends
+    to the mean of the values."""
+    hd = 4
+    q = np.array([1.0, 0.0, 0.0, 0.0], np.float32)
+    k = np.array([[2.0, 0, 0, 0], [8.0, 0, 0, 0]], np.float32)          # scores 1 and 4
+    v = np.array([[1.0, 0, 0, 0], [0.0, 1, 0, 0]], np.float32)
+    c = 2.0
+    a = math.exp(c * math.tanh(1.0 / c))
+    b = math.exp(c * math.tanh(4.0 / c))
+    got = oracle.attend_f32(q, k, v, softcap=c)
+    np.testing.assert_allclose(got[:2], [a / (a + b), b / (a + b)], rtol=0, atol=1e-15)
+    r = rng(3200)
+    q2 = r.standard_normal((2, HD)).astype(np.float32)
+    k2 = r.standard_normal((30, HD)).astype(np.float32)
+    v2 = r.standard_normal((30, HD)).astype(np.float32)
+    np.testing.assert_allclose(oracle.attend_f32(q2, k2, v2, softcap=1e12), oracle.attend_f32(q2, k2, v2),
+                               rtol=0, atol=1e-12)
+    tiny = oracle.attend_f32(q2, k2, v2, softcap=1e-9)
+    np.testing.assert_allclose(tiny, np.repeat(v2.astype(np.float64).mean(0)[None], 2, 0), rtol=0, atol=1e-7)
+
+
+def test_sinks_match_value_less_column():
+    """[P2] attend_group_upto: a sink logit joins the max and the denominator
+    and has no value row -- a softmax over the rows plus one extra column of
+    value zero."""
+    r = rng(3300)
+    q = r.standard_normal((4, HD)).astype(np.float32)
+    k = (r.standard_normal((40, HD)) * 2).astype(np.float32)
+    v = r.standard_normal((40, HD)).astype(np.float32)
+    z = np.array([0.5, -3.0, 9.0, 2.0], np.float32)
+    got = oracle.attend_f32(q, k, v, sinks=z)
+    np.testing.assert_allclose(got, options_reference(q, k, v, 0, 0.0, z), rtol=0, atol=1e-12)
+    # a very negative sink takes no mass; a dominant one takes nearly all of it
+    np.testing.assert_allclose(oracle.attend_f32(q, k, v, sinks=np.full(4, -1e4, np.float32)),
+                               oracle.attend_f32(q, k, v), rtol=0, atol=0)
+    one = oracle.attend_f32(q[:1], k[:1], v[:1], sinks=np.array([0.0], np.float32))
+    s = float(q[0].astype(np.float64) @ k[0].astype(np.float64)) / math.sqrt(HD)
+    w = math.exp(s) / (math.exp(s) + 1.0)                 # one row and a sink at 0
+    np.testing.assert_allclose(one[0], w * v[0].astype(np.float64), rtol=0, atol=1e-15)
+
+
+def test_sinks_with_windows_page_example():
+    """[P2] test sink_attend_matches_explicit_sink_column: 2 KV heads x 8
+    channels, 3 Q heads per group, 9 rows of the page's modular pattern, sinks
+    (0.7, -1.3, 2.5, 0, -4, 6), prefixes of 1, 2, 5, 9 rows and windows of
+    all, 3 and 1 rows; the page checks against an explicit value-less sink
+    column computed in f64."""
+    nkv, hd, hpk, rows = 2, 8, 3, 9
+
+    def kv(r_, i, a, m):
+        return np.float32((((r_ * a + i * 7 + 3) % m) / m - 0.5) * 2.0)
+
+    K = np.array([[kv(r_, i, 31, 97) for i in range(nkv * hd)] for r_ in range(rows)], np.float32)
+    V = np.array([[kv(r_, i, 17, 89) for i in range(nkv * hd)] for r_ in range(rows)], np.float32)
+    q = np.array([(((i * 11 + 5) % 83) / 83.0 - 0.5) * 3.0 for i in range(nkv * hpk * hd)], np.float32)
+    sinks = np.array([0.7, -1.3, 2.5, 0.0, -4.0, 6.0], np.float32)
+    checked = 0
+    for upto in (1, 2, 5, 9):
+        for window in (None, 3, 1):
+            first = 0 if window is None else max(upto - window, 0)
+            for g in range(nkv):
+                qg = q[g * hpk * hd:(g + 1) * hpk * hd].reshape(hpk, hd)
+                kg, vg = K[:upto, g * hd:(g + 1) * hd], V[:upto, g * hd:(g + 1) * hd]
+                zg = sinks[g * hpk:(g + 1) * hpk]
+                got = oracle.attend_f32(qg, kg, vg, first=first, sinks=zg)
+                np.testing.assert_allclose(got, options_reference(qg, kg, vg, first, 0.0, zg), rtol=0, atol=1e-12)
+                checked += hpk
+    assert checked == 4 * 3 * nkv * hpk
+
+
+def test_all_options_on_q8_rows():
+    """Window + soft-cap + sinks on a q8 head: the same options over the
+    dequantised rows."""
+    r = rng(3400)
+    h = oracle.Q8Head(cap=200)
+    h.append((r.standard_normal((200, HD)) * 3).astype(np.float32),
+             (r.standard_normal((200, HD)) * 3).astype(np.float32))
+    q = r.standard_normal((4, HD)).astype(np.float32)
+    z = np.array([1.0, -2.0, 0.0, 5.0], np.float32)
+    got = oracle.attend_q8(q, h, first=70, softcap=20.0, sinks=z)
+    ref = options_reference(q, h.dequant_k(), h.dequant_v(), 70, 20.0, z)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
 
 
