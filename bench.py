@@ -230,6 +230,24 @@ def main():
             "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
             "kv_positions_per_s": round(int(cq.len.sum()) / us * 1e6, 1)}
 
+        # [P2] attend_group_upto options: soft-cap 30 and per-Q-head sinks over
+        # the full context, then also an 8192-row sliding window
+        sinks = t(workloads.normal_f32(workloads.key(bq.seed, 97), (bq.n_q_heads,)) * np.float32(3.0))
+        opt_full = K.DecodeOpts(softcap=30.0, sinks=sinks)
+        win_first = np.maximum(cq.len.astype(np.int64) - 8192, 0).astype(np.int32)
+        opt_win = K.DecodeOpts(first=win_first, softcap=30.0, sinks=sinks)
+        for name, o, rows in (("decode_attn_q8_ex_softcap_sinks", opt_full, cq.len),
+                              ("decode_attn_q8_ex_window8192_softcap_sinks", opt_win,
+                               np.minimum(cq.len, 8192))):
+            def ex_call(i, o=o):
+                K.decode_attn_q8_ex(cq, bq.n_q_heads, qq, qout, o, ws_q8)
+            us = time_calls(ex_call, 50)
+            nb = algorithmic_bytes_q8(rows, cq.n_live, bq.n_q_heads)
+            parts[name] = {
+                "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+                "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                "kv_positions_per_s": round(int(np.sum(rows)) / us * 1e6, 1)}
+
         def app_call(i):
             K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
         if int(cq.len.max()) + 40 <= cq.capacity:

@@ -245,6 +245,41 @@ int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Options of decode_attn_f32_ex / decode_attn_q8_ex: the visible-row start,
+ * logit soft-cap and learned sinks of [P2] LayerKvCache::attend_group_upto.
+ *
+ * first    host int32 [batch], or NULL for 0: sequence b attends rows
+ *          [first[b], len[b]) only (a sliding window is first = len - W);
+ *          first[b] >= len[b] is clamped to len[b] - 1, so at least one row
+ *          stays visible.  Rows before first get probability exactly 0.
+ * softcap  > 0: every scaled score s becomes softcap * tanh(s / softcap)
+ *          (Gemma-2 soft-capping) before the softmax; 0 = off.
+ * sinks    device float [n_q_heads], or NULL for none: one learned logit per
+ *          Q head (same for every sequence).  It joins the softmax max and
+ *          adds exp(sink - max) to the denominator; it has no value row and
+ *          is not soft-capped.  A sequence with no rows still gives zeros.
+ * The struct is read during the call only; `first` is copied into the
+ * launch, so the caller may reuse it once the call returns.
+ */
+typedef struct kvq_decode_opts {
+    const int32_t* first;
+    float softcap;
+    int32_t reserved;        /* 0 */
+    const float* sinks;
+} kvq_decode_opts;
+
+/*
+ * decode_attn_f32_ex / decode_attn_q8_ex -- decode_attn_f32 / decode_attn_q8
+ * with the options above (opts NULL = no options: identical to the plain
+ * calls).  Errors: as the plain calls, plus KVQ_EINVAL for a negative
+ * first[b], a softcap that is negative or not finite, or reserved != 0.
+ */
+int decode_attn_f32_ex(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                       const kvq_decode_opts* opts, void* ws, size_t ws_bytes, void* stream);
+int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                      const kvq_decode_opts* opts, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * rswa_record_prefill -- [P3] RingCache::record_prefill for sequence `seq`
  * of an f32 cache whose reference block has just been appended with
  * kv_append_f32: prefill_len = len[seq], ring_len = ring_pos = writes = 0.

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -200,11 +201,24 @@ int check_decode_args(const kvq_cache* c, int n_q_heads, const float* q, float* 
     return KVQ_OK;
 }
 
-// Partition and launch one decode over every sequence.  lens: rows attended
-// per sequence; wrows: R-SWA row fed from k_new/v_new (or null).
+// Options of the _ex calls: first[b] >= 0, softcap finite and >= 0.
+int check_decode_opts(const kvq_cache* c, const kvq_decode_opts* o, const char* fn) {
+    if (!o) return KVQ_OK;
+    if (o->reserved != 0) return fail(KVQ_EINVAL, "%s: opts.reserved must be 0", fn);
+    if (!(o->softcap >= 0.0f) || std::isinf(o->softcap))
+        return fail(KVQ_EINVAL, "%s: softcap %g must be finite and >= 0", fn, (double)o->softcap);
+    if (o->first)
+        for (int b = 0; b < c->batch; ++b)
+            if (o->first[b] < 0) return fail(KVQ_EINVAL, "%s: first[%d] = %d < 0", fn, b, o->first[b]);
+    return KVQ_OK;
+}
+
+// Partition and launch one decode over every sequence.  lens: rows stored
+// per sequence; wrows: R-SWA row fed from k_new/v_new (or null); opts: the
+// visible-row start, soft-cap and sinks (or null).
 int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float* out, void* ws,
                const int32_t* lens, const int32_t* wrows, const float* k_new, const float* v_new,
-               hipStream_t s, const char* fn) {
+               const kvq_decode_opts* opts, hipStream_t s, const char* fn) {
     DecodeArgs a;
     memset(&a, 0, sizeof a);
     a.q = q;
@@ -228,6 +242,8 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
     a.n_q_heads = n_q_heads;
     a.hpk = hpk;
     a.capacity = c->capacity;
+    a.softcap2 = (opts && opts->softcap > 0.0f) ? (double)opts->softcap * 1.4426950408889634 : 0.0;
+    a.sinks = opts ? opts->sinks : nullptr;
     fill_live(c, a.live_head);
     memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
     for (int s0 = 0; s0 < c->batch; s0 += kSeqPerLaunch) {
@@ -237,8 +253,11 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
         int64_t tiles = 0;
         for (int j = 0; j < ns; ++j) {
             const int L = lens[s0 + j];
+            // [P2] attend_group_upto: first clamped so that one row stays visible
+            const int f = (opts && opts->first && L > 0) ? std::min(opts->first[s0 + j], L - 1) : 0;
             a.len[j] = L;
-            a.ntile[j] = (L + kTileRows - 1) / kTileRows;
+            a.first[j] = f;
+            a.ntile[j] = (L - f + kTileRows - 1) / kTileRows;
             a.wrow[j] = wrows ? wrows[s0 + j] : -1;
             a.frozen[j] = c->frozen[s0 + j] ? 1 : 0;
             a.tile_base[j] = (int32_t)tiles;
@@ -414,7 +433,7 @@ int decode_attn_f32(const kvq_cache* c, int n_q_heads, const float* q, float* ou
     if (rc) return rc;
     int hpk = 0;
     if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
-    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr,
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, nullptr,
                       (hipStream_t)stream, fn);
 }
 
@@ -425,7 +444,31 @@ int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out
     if (rc) return rc;
     int hpk = 0;
     if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
-    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr,
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, nullptr,
+                      (hipStream_t)stream, fn);
+}
+
+int decode_attn_f32_ex(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                       const kvq_decode_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "decode_attn_f32_ex";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    if ((rc = check_decode_opts(c, opts, fn))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, opts,
+                      (hipStream_t)stream, fn);
+}
+
+int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                      const kvq_decode_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "decode_attn_q8_ex";
+    int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    if ((rc = check_decode_opts(c, opts, fn))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, opts,
                       (hipStream_t)stream, fn);
 }
 
@@ -482,7 +525,7 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
         wrows[b] = r.prefill_len + slot;
         lens[b] = r.prefill_len + r.ring_len;
     }
-    if ((rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new,
+    if ((rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new, nullptr,
                          (hipStream_t)stream, fn)))
         return rc;
     for (int b = 0; b < c->batch; ++b) {

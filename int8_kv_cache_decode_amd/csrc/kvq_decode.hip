@@ -62,6 +62,7 @@ __host__ __device__ inline int tile_owner(int t, int T, int W) {
 }
 
 // The part of one share that lies in one (sequence, live head) segment.
+// A segment's tiles start at the sequence's first visible row.
 struct Piece {
     int j, gl, b, g;
     int row0, row1;  // rows of the segment, [row0, row1)
@@ -92,8 +93,8 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, F&& f
         p.gl = gl;
         p.b = a.seq0 + j;
         p.g = a.live_head[gl];
-        p.row0 = kTileRows * (t - sb);
-        p.row1 = min(kTileRows * (pe - sb), a.len[j]);
+        p.row0 = a.first[j] + kTileRows * (t - sb);
+        p.row1 = min(a.first[j] + kTileRows * (pe - sb), a.len[j]);
         p.slot = w + j * a.n_live + gl;
         p.hrow = ((size_t)p.b * a.n_live + gl) * a.capacity;
         f(p);
@@ -139,12 +140,38 @@ __device__ __forceinline__ float reduce8_over32(const float (&v)[8], int seg) {
     return z;
 }
 
-template <int HPK>
+// Gemma-2 logit soft-cap in log2 units ([P2] attend_group_upto):
+// c2 * tanh(s / c2), c2 = softcap * log2 e, in f64 without a library call.
+// tanh|y| = (1 - e) / (1 + e) with e = exp(-2|y|) = 2^z, z = n + r, n =
+// rint(z), |r| <= 1/2, and 2^r = exp(r ln 2) from its Taylor polynomial of
+// degree 10 (truncation below 3e-13 for |r ln 2| <= 0.35): the capped score
+// carries a relative error near 1e-12, far below the f32 output's.
+__device__ __forceinline__ double soft_cap(double s, double c2, double inv_c2) {
+    const double z = -2.0 * 1.4426950408889634 * (fabs(s) * inv_c2);
+    const double n = rint(z);
+    const double r = (z - n) * 0.6931471805599453;
+    double p = 1.0 / 3628800.0;                        // 1/10!
+    p = fma(p, r, 1.0 / 362880.0);
+    p = fma(p, r, 1.0 / 40320.0);
+    p = fma(p, r, 1.0 / 5040.0);
+    p = fma(p, r, 1.0 / 720.0);
+    p = fma(p, r, 1.0 / 120.0);
+    p = fma(p, r, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p = fma(p, r, 1.0);
+    const double e = ldexp(p, (int)fmax(n, -2000.0));  // 0 once |y| is large: tanh = 1
+    return copysign(c2 * ((1.0 - e) / (1.0 + e)), s);
+}
+
+template <int HPK, bool kCap>
 __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5, seg = lane & 31;
+    const double inv_c2 = kCap ? 1.0 / a.softcap2 : 0.0;
     for_each_piece(a, w, [&](const Piece& it) {
         const float* K = a.k + it.hrow * kHD;
         const float* V = a.v + it.hrow * kHD;
@@ -196,6 +223,7 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
                     part[i] = d;
                 }
                 float sc = reduce8_over32(part, seg);
+                if (kCap) sc = (float)soft_cap((double)sc, a.softcap2, inv_c2);
                 if (myrow >= it.row1) sc = -INFINITY;
                 const float mnew = fmaxf(m[h], wave_max(sc));
                 const float alpha = fast_exp2(m[h] - mnew);
@@ -332,7 +360,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #ifndef KVQ_Q8_MIN_WAVES
 #define KVQ_Q8_MIN_WAVES 3
 #endif
-template <int HPK>
+template <int HPK, bool kCap>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
     __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
@@ -341,6 +369,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const double inv_c2 = kCap ? 1.0 / a.softcap2 : 0.0;
     const int hq = lane >> 4, n = lane & 15;          // score layout
     const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
     for_each_piece(a, w, [&](const Piece& it) {
@@ -514,6 +543,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
                     }
                 }
                 const int h = 4 * hb + hq;
+                if (kCap) sc = soft_cap(sc, a.softcap2, inv_c2);
                 if (!valid || h >= HPK) sc = -INFINITY;
                 const float tmax = max16((float)sc);
                 float mnew = m[hb], alpha = 1.0f;
@@ -683,9 +713,11 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     }
     __syncthreads();
     if (tid < 32) {
-        float Mt = sm_m[0];
+        // a learned sink joins the max and the denominator ([P2] attend_group_upto)
+        const float zs = a.sinks ? (float)((double)a.sinks[h] * 1.4426950408889634) : -INFINITY;
+        float Mt = fmaxf(sm_m[0], zs);
         for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
-        float Lt = 0.0f;
+        float Lt = a.sinks ? fast_exp2(zs - Mt) : 0.0f;
         float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k = 0; k < ngroups; ++k) {
             const float e = fast_exp2(sm_m[k] - Mt);    // 0 for sub-groups without rows
@@ -731,7 +763,7 @@ int combine_threads(const DecodeArgs& a) {
 // device and kernel.  0 on a runtime error.
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
-    static int cache[kMaxDevices][8];
+    static int cache[kMaxDevices][16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     int& c = cache[dev][which];
@@ -747,6 +779,13 @@ int resident_waves(const void* kernel, int which) {
 
 int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
 
+// The kernel instance for a group size, cache kind and soft-cap switch.
+template <int HPK, bool kQ8>
+const void* decode_kernel(bool cap) {
+    if (kQ8) return cap ? (const void*)k_decode_q8<HPK, true> : (const void*)k_decode_q8<HPK, false>;
+    return cap ? (const void*)k_decode_f32<HPK, true> : (const void*)k_decode_f32<HPK, false>;
+}
+
 // Shares per launch: one per resident wave for the q8 kernel (a wave keeps
 // one 4.4-KB tile in flight beside the one it computes), one per four
 // resident waves for the f32 kernel: a wave's 16-KB tile keeps HBM busy with
@@ -760,15 +799,16 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
     DecodeArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {
+        const bool cap = a.softcap2 > 0.0;
         const void* fn = nullptr;
         switch (a.hpk) {
-            case 1: fn = kQ8 ? (const void*)k_decode_q8<1> : (const void*)k_decode_f32<1>; break;
-            case 2: fn = kQ8 ? (const void*)k_decode_q8<2> : (const void*)k_decode_f32<2>; break;
-            case 4: fn = kQ8 ? (const void*)k_decode_q8<4> : (const void*)k_decode_f32<4>; break;
-            case 8: fn = kQ8 ? (const void*)k_decode_q8<8> : (const void*)k_decode_f32<8>; break;
+            case 1: fn = decode_kernel<1, kQ8>(cap); break;
+            case 2: fn = decode_kernel<2, kQ8>(cap); break;
+            case 4: fn = decode_kernel<4, kQ8>(cap); break;
+            case 8: fn = decode_kernel<8, kQ8>(cap); break;
             default: return hipErrorInvalidValue;
         }
-        const int wv = resident_waves(fn, 4 * kQ8 + hpk_index(a.hpk));
+        const int wv = resident_waves(fn, 8 * kQ8 + 4 * cap + hpk_index(a.hpk));
         if (wv == 0) return hipErrorInvalidDevice;
         const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;

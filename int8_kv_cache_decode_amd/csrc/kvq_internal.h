@@ -101,11 +101,14 @@ struct DecodeArgs {
     int seq0;                  // first absolute sequence of this launch
     int n_tiles;               // 16-row tiles of the launch over all (sequence, live head)
     int n_shares;              // shares of the tile stream (set by the launcher, <= n_tiles)
+    double softcap2;           // logit soft-cap in log2 units (softcap * log2 e), 0 = off
+    const float* sinks;        // [n_q_heads] learned sink logits (natural units), or null
     int8_t live_head[KVQ_MAX_KV_HEADS];      // KV head of live slot
     int8_t live_slot[KVQ_MAX_KV_HEADS];      // live slot of KV head, -1 dead
     int32_t tile_base[kSeqPerLaunch + 1];    // first tile of each sequence (its live heads in order)
-    int32_t ntile[kSeqPerLaunch];            // tiles per (sequence, live head) = ceil(len / 16)
-    int32_t len[kSeqPerLaunch];              // rows attended
+    int32_t ntile[kSeqPerLaunch];            // tiles per (sequence, live head) = ceil((len - first) / 16)
+    int32_t first[kSeqPerLaunch];            // first visible row (rows [first, len) are attended)
+    int32_t len[kSeqPerLaunch];              // rows stored
     int32_t wrow[kSeqPerLaunch];             // R-SWA row taken from k_new/v_new, -1 none
     uint8_t frozen[kSeqPerLaunch];           // q8: column fields hold the frozen RMS
 };

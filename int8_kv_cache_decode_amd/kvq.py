@@ -47,6 +47,10 @@ class kvq_ring(ctypes.Structure):
                 ("writes", ctypes.c_int64)]
 
 
+class kvq_decode_opts(ctypes.Structure):
+    _fields_ = [("first", _P), ("softcap", ctypes.c_float), ("reserved", ctypes.c_int32), ("sinks", _P)]
+
+
 _lib = None
 
 # (name, restype, argtypes) of every exported entry point
@@ -61,6 +65,8 @@ _SIGNATURES = [
     ("kvq_workspace_bytes", ctypes.c_size_t, [_P, ctypes.c_int]),
     ("decode_attn_f32", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
     ("decode_attn_q8", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("decode_attn_f32_ex", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("decode_attn_q8_ex", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("rswa_record_prefill", ctypes.c_int, [_P, _P, ctypes.c_int]),
     ("rswa_decode", ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("kvq_last_error", ctypes.c_char_p, []),
@@ -230,6 +236,41 @@ def decode_attn_q8(cache: KvCache, n_q_heads: int, q, out, ws=None, ws_bytes=Non
     ws = cache.workspace(n_q_heads) if ws is None else ws
     nb = ws.numel() if ws_bytes is None else ws_bytes
     _check(lib().decode_attn_q8(cache.ref, n_q_heads, _ptr(q), _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+class DecodeOpts:
+    """kvq_decode_opts: first (host int32 [batch] or None), softcap (0 = off),
+    sinks (device float [n_q_heads] tensor or None).  Keeps the host array
+    alive for the call."""
+
+    def __init__(self, first=None, softcap: float = 0.0, sinks=None):
+        self.first = None if first is None else np.ascontiguousarray(first, np.int32)
+        self.sinks = sinks
+        self.c = kvq_decode_opts()
+        self.c.first = None if self.first is None else self.first.ctypes.data
+        self.c.softcap = float(softcap)
+        self.c.reserved = 0
+        self.c.sinks = _ptr(sinks)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def decode_attn_f32_ex(cache: KvCache, n_q_heads: int, q, out, opts: Optional[DecodeOpts] = None,
+                       ws=None, ws_bytes=None, stream=None) -> None:
+    ws = cache.workspace(n_q_heads) if ws is None else ws
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().decode_attn_f32_ex(cache.ref, n_q_heads, _ptr(q), _ptr(out), None if opts is None else opts.ref,
+                                    _ptr(ws), nb, _stream(stream)))
+
+
+def decode_attn_q8_ex(cache: KvCache, n_q_heads: int, q, out, opts: Optional[DecodeOpts] = None,
+                      ws=None, ws_bytes=None, stream=None) -> None:
+    ws = cache.workspace(n_q_heads) if ws is None else ws
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().decode_attn_q8_ex(cache.ref, n_q_heads, _ptr(q), _ptr(out), None if opts is None else opts.ref,
+                                   _ptr(ws), nb, _stream(stream)))
 
 
 def rswa_record_prefill(cache: KvCache, rings: Rings, seq: int) -> None:

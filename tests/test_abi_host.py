@@ -141,6 +141,28 @@ def test_decode_refusals():
     expect(call("decode_attn_f32", c.ref, 32, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE, c, before)
 
 
+def test_decode_option_refusals():
+    """decode_attn_*_ex refuse bad options before any launch: a negative
+    first row, a negative or non-finite soft-cap, reserved != 0."""
+    for kind, fn in ((K.KIND_F32, "decode_attn_f32_ex"), (K.KIND_Q8, "decode_attn_q8_ex")):
+        c = fake_cache(kind)
+        c.len[:] = [10, 20]
+        need = K.kvq_workspace_bytes(c, 32)
+        before = snapshot(c)
+        for first, cap, res in (([0, -1], 0.0, 0), (None, -1.0, 0), (None, float("nan"), 0),
+                                (None, float("inf"), 0), (None, 0.0, 1)):
+            o = K.DecodeOpts(first=first, softcap=cap)
+            o.c.reserved = res
+            expect(call(fn, c.ref, 32, FAKE, FAKE, o.ref, FAKE, need, None), K.EINVAL, c, before)
+        # the usual argument checks come first and still apply
+        o = K.DecodeOpts(first=[0, 0], softcap=30.0)
+        expect(call(fn, c.ref, 30, FAKE, FAKE, o.ref, FAKE, need, None), K.EINVAL, c, before)
+        expect(call(fn, c.ref, 32, FAKE, FAKE, o.ref, FAKE, need - 1, None), K.EINVAL, c, before)
+    c = fake_cache(K.KIND_Q8)
+    before = snapshot(c)
+    expect(call("decode_attn_f32_ex", c.ref, 32, FAKE, FAKE, None, FAKE, 1 << 40, None), K.ESTATE, c, before)
+
+
 def test_rswa_refusals_leave_cache_and_rings_unchanged():
     c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=200)
     rings = K.Rings(2)

@@ -155,7 +155,9 @@ def test_q8_all_seqs_append_freezes_each_sequence_at_64():
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def run_decode_case(kind, lens, hkv, hpk, alive, seed, scale_rows=False):
+def run_decode_case(kind, lens, hkv, hpk, alive, seed, scale_rows=False, opts=None):
+    """opts: None, or dict(first=[B] or None, softcap=float, sinks=[Hq] or
+    None) for the _ex calls ([P2] attend_group_upto options)."""
     r = rng(seed)
     B = len(lens)
     cap = max(max(lens), 1)
@@ -182,14 +184,24 @@ def run_decode_case(kind, lens, hkv, hpk, alive, seed, scale_rows=False):
     q = r.standard_normal((B, hq, 128)).astype(np.float32)
     qd = dev(q)
     out = torch.full((B, hq, 128), np.nan, device="cuda")
-    fn = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
-    fn(c, hq, qd, out)
+    if opts is None:
+        fn = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
+        call = lambda o: fn(c, hq, qd, o)
+        ref_kw = {}
+    else:
+        fn = K.decode_attn_f32_ex if kind == K.KIND_F32 else K.decode_attn_q8_ex
+        z = opts.get("sinks")
+        zd = None if z is None else dev(np.asarray(z, np.float32))
+        o8 = K.DecodeOpts(first=opts.get("first"), softcap=opts.get("softcap", 0.0), sinks=zd)
+        call = lambda o: fn(c, hq, qd, o, o8)
+        ref_kw = dict(first=opts.get("first"), softcap=opts.get("softcap", 0.0), sinks=z)
+    call(out)
     out2 = torch.full_like(out, np.nan)
-    fn(c, hq, qd, out2)
+    call(out2)
     torch.cuda.synchronize()
     got, got2 = host(out), host(out2)
     assert np.array_equal(got.view(np.uint32), got2.view(np.uint32)), "decode is not deterministic"
-    ref = oracle.decode(q, units, hkv, threads=THREADS)
+    ref = oracle.decode(q, units, hkv, threads=THREADS, **ref_kw)
     err = max_err(got, ref)
     say("  max err %.3g" % err)
     assert err <= F32_TOL, err
@@ -209,6 +221,49 @@ def test_decode_small_shapes(kind, hpk):
     lens = [0, 1, 63, 64, 65, 700, 2500]
     run_decode_case(kind, lens, 4, hpk, np.array([1, 1, 0, 1], np.uint8), seed=10 + hpk + 7 * kind,
                     scale_rows=(kind == K.KIND_Q8))
+
+
+@pytest.mark.parametrize("variant", ["window", "cap_sinks", "all"])
+@pytest.mark.parametrize("hpk", [1, 4, 8])
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+def test_decode_options_small(kind, hpk, variant):
+    """[P2] attend_group_upto options through decode_attn_*_ex: visible-row
+    starts inside the first tile, on tile edges, at len - 1 and past len
+    (clamped), the soft-cap on scaled scores, and per-Q-head sinks, against
+    the oracle with the same options."""
+    say("case: decode_options kind", kind, "hpk", hpk, "variant", variant)
+    lens = [0, 1, 63, 64, 65, 700, 2500]
+    first = [0, 5, 10, 63, 64, 650, 100] if variant in ("window", "all") else None
+    r = rng(40 + hpk + 3 * kind)
+    hq = 4 * hpk
+    opts = dict(first=first,
+                softcap={"window": 0.0, "cap_sinks": 5.0, "all": 30.0}[variant],
+                sinks=None if variant == "window" else (r.standard_normal(hq) * 2).astype(np.float32))
+    run_decode_case(kind, lens, 4, hpk, np.array([1, 1, 0, 1], np.uint8), seed=50 + hpk + 7 * kind,
+                    scale_rows=(kind == K.KIND_Q8), opts=opts)
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+def test_decode_options_none_equal_plain_call(kind):
+    """opts = NULL, and options that change nothing (first 0, cap 0, no
+    sinks), give the plain call's bits."""
+    say("case: decode_options_neutral kind", kind)
+    r = rng(60)
+    c = K.KvCache(kind, 3, 2, 300)
+    lens = [300, 17, 129]
+    for b, n in enumerate(lens):
+        append_rows(c, b, r.standard_normal((n, 2, 128)).astype(np.float32),
+                    r.standard_normal((n, 2, 128)).astype(np.float32))
+    q = dev(r.standard_normal((3, 8, 128)).astype(np.float32))
+    outs = [torch.full((3, 8, 128), np.nan, device="cuda") for _ in range(3)]
+    plain = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
+    ex = K.decode_attn_f32_ex if kind == K.KIND_F32 else K.decode_attn_q8_ex
+    plain(c, 8, q, outs[0])
+    ex(c, 8, q, outs[1], None)
+    ex(c, 8, q, outs[2], K.DecodeOpts(first=[0, 0, 0], softcap=0.0))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(host(o).view(np.uint32), host(outs[0]).view(np.uint32))
 
 
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
@@ -389,7 +444,9 @@ def test_workload_rswa_long_f32():
     rswa_workload("rswa_long_f32", check_steps={0, 127, 128, 250, 499})
 
 
-def gqa_workload(name, sample_units=None):
+def gqa_workload(name, sample_units=None, window=None, softcap=0.0, sinks_seed=None):
+    """window: rows visible per sequence (first = len - window); softcap and
+    seeded per-Q-head sinks go through decode_attn_*_ex when given."""
     from concurrent.futures import ThreadPoolExecutor
     spec = workloads.get(name)
     lens = spec.lengths()
@@ -418,10 +475,18 @@ def gqa_workload(name, sample_units=None):
     say("  %s appended %d rows" % (name, int(lens.sum())))
     q = spec.query()
     out = torch.full((spec.batch, spec.n_q_heads, 128), np.nan, device="cuda")
-    (K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8)(c, spec.n_q_heads, dev(q), out)
+    if window is None and softcap == 0.0 and sinks_seed is None:
+        (K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8)(c, spec.n_q_heads, dev(q), out)
+        ref_kw = {}
+    else:
+        first = None if window is None else np.maximum(lens.astype(np.int64) - window, 0).astype(np.int32)
+        z = None if sinks_seed is None else (rng(sinks_seed).standard_normal(spec.n_q_heads) * 3).astype(np.float32)
+        o = K.DecodeOpts(first=first, softcap=softcap, sinks=None if z is None else dev(z))
+        (K.decode_attn_f32_ex if kind == K.KIND_F32 else K.decode_attn_q8_ex)(c, spec.n_q_heads, dev(q), out, o)
+        ref_kw = dict(first=first, softcap=softcap, sinks=z)
     torch.cuda.synchronize()
     got = host(out)
-    ref = oracle.decode(q, units, spec.n_kv_heads, threads=THREADS, only=sample_units)
+    ref = oracle.decode(q, units, spec.n_kv_heads, threads=THREADS, only=sample_units, **ref_kw)
     hpk = spec.n_q_heads // spec.n_kv_heads
     pairs = sample_units or [(b, g) for b in range(spec.batch) for g in range(spec.n_kv_heads)]
     err = 0.0
@@ -448,3 +513,23 @@ def test_workload_gqa_q8():
 def test_workload_batched_q8():
     say("case: workload batched_q8")
     gqa_workload("batched_q8")
+
+
+def test_workload_gqa_f32_options():
+    """gqa_f32 with a 1000-row window, soft-cap 20 and sinks."""
+    say("case: workload gqa_f32 + options")
+    gqa_workload("gqa_f32", window=1000, softcap=20.0, sinks_seed=70)
+
+
+def test_workload_gqa_q8_options():
+    """gqa_q8 with a 4096-row window, soft-cap 50 and sinks."""
+    say("case: workload gqa_q8 + options")
+    gqa_workload("gqa_q8", window=4096, softcap=50.0, sinks_seed=71)
+
+
+@pytest.mark.timeout(900)
+def test_workload_batched_q8_options():
+    """batched_q8 with an 8192-row window (shorter sequences see all rows),
+    soft-cap 30 and sinks."""
+    say("case: workload batched_q8 + options")
+    gqa_workload("batched_q8", window=8192, softcap=30.0, sinks_seed=72)
