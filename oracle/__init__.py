@@ -281,6 +281,7 @@ class RingModel:
         self.writes = 0
         self.slots: list = [None] * window   # slot -> token id held
         self.tokens: list = []               # every token id written, in order
+        self.epoch = 0                       # lineage: bumped by a rollback that discards writes
 
     def record_prefill(self, n: int) -> None:
         self.prefill_len = n
@@ -289,6 +290,7 @@ class RingModel:
         self.writes = 0
         self.slots = [None] * self.W
         self.tokens = []
+        self.epoch += 1
 
     def write(self, token) -> int:
         """Warm-up: append at ring_len (ring_pos follows ring_len mod W);
@@ -317,3 +319,52 @@ class RingModel:
 
     def effective_len(self) -> int:
         return (self.prefill_len or 0) + self.ring_len
+
+    # [P3] RingCache::checkpoint / rollback_to: a checkpoint holds the cursors
+    # only; a rollback restores them if that loses no live row, and starts a
+    # new lineage when it discards writes.
+    def checkpoint(self) -> dict:
+        return dict(prefill_len=self.prefill_len, ring_len=self.ring_len, ring_pos=self.ring_pos,
+                    writes=self.writes, epoch=self.epoch)
+
+    def rollback_to(self, cp: dict) -> None:
+        if cp["prefill_len"] != self.prefill_len:
+            raise ValueError("checkpoint of another prefill")
+        if cp["epoch"] != self.epoch:
+            raise ValueError("checkpoint of an abandoned lineage")
+        if cp["writes"] > self.writes:
+            raise ValueError("checkpoint from the future")
+        discarded = self.writes - cp["writes"]
+        if cp["ring_len"] > self.W or discarded > self.W - cp["ring_len"]:
+            raise ValueError("rollback would need overwritten rows")
+        self.ring_len, self.ring_pos, self.writes = cp["ring_len"], cp["ring_pos"], cp["writes"]
+        self.tokens = self.tokens[: cp["writes"]]
+        if discarded:
+            self.epoch += 1
+
+
+# --------------------------------------------------------------------------
+# Row management around the decode ([P2] LayerKvCache::truncate_last,
+# trim_window_anchored)
+# --------------------------------------------------------------------------
+def truncate_last(n: int, n_drop: int) -> int:
+    """Rows kept after dropping the last n_drop of n (never below 0)."""
+    return n - min(n_drop, n)
+
+
+def trim_window(base: int, n: int, w: int, slack: int, align: int, anchor: Optional[int] = None,
+                q8_unfrozen: bool = False) -> int:
+    """Rows a sliding-window trim drops from the front of a sequence whose
+    row 0 is absolute position `base` and which stores n rows: nothing while
+    n <= 2w (or w == 0, or a q8 field not frozen yet); otherwise the front is
+    cut so that w + slack rows (and, with an anchor, every row from
+    anchor - w - slack on) stay, the new base rounded down to a multiple of
+    align."""
+    if w == 0 or n <= 2 * w or q8_unfrozen:
+        return 0
+    align = max(align, 1)
+    keep_from = max(base + n - (w + slack), 0)
+    if anchor is not None:
+        keep_from = min(keep_from, max(anchor - (w + slack), 0))
+    new_base = keep_from // align * align
+    return new_base - base if new_base > base else 0

@@ -696,6 +696,128 @@ def test_ring_attention_equals_explicit_window():
                                    oracle.attend_f32(q, exp_k, exp_v), rtol=0, atol=1e-13)
 
 
+def test_ring_rollback_restores_cursors_page_example():
+    """[P3] tests checkpoint_rollback_restores_ring_rows_byte_identical and
+    rollback_noop_is_identity: 5 prefill rows, 9 accepted steps, a checkpoint
+    at ring_len = ring_pos = 9, 6 draft steps rolled back; the live window is
+    the accepted tokens again and the next write lands in slot 9."""
+    m = oracle.RingModel()
+    m.record_prefill(5)
+    for t in range(9):
+        m.write(("acc", t))
+    cp = m.checkpoint()
+    assert (cp["ring_len"], cp["ring_pos"], cp["prefill_len"]) == (9, 9, 5)
+    for t in range(6):
+        m.write(("draft", t))
+    assert m.ring_len == 15
+    m.rollback_to(cp)
+    assert (m.ring_len, m.ring_pos, m.writes, m.effective_len()) == (9, 9, 9, 14)
+    assert m.physical() == [("acc", t) for t in range(9)] == m.window()
+    assert m.slots[9] == ("draft", 0)                 # a dead slot keeps the discarded row
+    assert m.write(("acc", 9)) == 9
+    m2 = oracle.RingModel()
+    m2.record_prefill(4)
+    m2.write("a")
+    e0 = m2.epoch
+    m2.rollback_to(m2.checkpoint())                  # no-op rollback: identity, same lineage
+    assert (m2.ring_len, m2.ring_pos, m2.writes, m2.epoch) == (1, 1, 1, e0)
+
+
+def test_ring_rollback_refusals_page_examples():
+    """[P3] tests rollback_rejects_eviction_in_steady_state_without_mutation
+    and rollback_rejects_abandoned_branch_checkpoint_without_mutation, plus a
+    checkpoint from the future and one from before a re-prefill."""
+    m = oracle.RingModel()
+    m.record_prefill(3)
+    for _ in range(oracle.RING_W):
+        m.write("x")
+    cp = m.checkpoint()
+    m.write("y")                                     # steady state: overwrites slot 0
+    before = m.checkpoint()
+    with pytest.raises(ValueError):
+        m.rollback_to(cp)
+    assert m.checkpoint() == before
+    m = oracle.RingModel()
+    m.record_prefill(4)
+    m.write("accepted")
+    branch = m.checkpoint()
+    m.write("abandoned")
+    stale = m.checkpoint()
+    m.rollback_to(branch)
+    m.write("replacement")
+    assert (stale["ring_len"], stale["ring_pos"], stale["writes"]) == (m.ring_len, m.ring_pos, m.writes)
+    before = m.checkpoint()
+    with pytest.raises(ValueError):                  # same cursors, abandoned lineage
+        m.rollback_to(stale)
+    assert m.checkpoint() == before
+    future = dict(before, writes=before["writes"] + 1)
+    with pytest.raises(ValueError):
+        m.rollback_to(future)
+    old = m.checkpoint()
+    m.record_prefill(4)                              # a re-prefill starts a new lineage
+    with pytest.raises(ValueError):
+        m.rollback_to(old)
+    # a warm-up rollback may discard up to W - ring_len writes, no more
+    m = oracle.RingModel()
+    m.record_prefill(0)
+    for _ in range(100):
+        m.write(0)
+    cp = m.checkpoint()
+    for _ in range(oracle.RING_W - 100):
+        m.write(1)
+    m.rollback_to(cp)
+    for _ in range(oracle.RING_W - 99):
+        m.write(1)
+    with pytest.raises(ValueError):
+        m.rollback_to(cp)
+
+
+def test_trim_window_page_invariants():
+    """[P2] tests swa_trim_keeps_contiguous_tail and swa_gen_bumps: feeding
+    positions one by one with w = 6, slack 2, align 4, a trim leaves
+    w + slack .. w + slack + align - 1 rows, never more than 2w rows stay,
+    the base stays a multiple of align and base + rows is the position
+    count; with w = 10, 18 rows do not trim and 21 do."""
+    w, slack, align = 6, 2, 4
+    base, n, trims = 0, 0, 0
+    for p in range(100):
+        n += 1
+        d = oracle.trim_window(base, n, w, slack, align)
+        if d:
+            trims += 1
+            base, n = base + d, n - d
+            assert w + slack <= n < w + slack + align
+        assert n <= 2 * w and base % align == 0 and base + n == p + 1
+    assert trims > 5
+    assert oracle.trim_window(0, 18, 10, 2, 4) == 0
+    assert oracle.trim_window(0, 21, 10, 2, 4) > 0
+    assert oracle.trim_window(0, 500, 0, 2, 4) == 0                     # w = 0: never
+    assert oracle.trim_window(0, 500, 10, 2, 4, q8_unfrozen=True) == 0   # q8 field not frozen yet
+
+
+def test_trim_window_anchored_page_example():
+    """[P2] test swa_anchored_trim_keeps_the_rollback_window: with anchor 40
+    (w 6, slack 2, align 4) the base never passes anchor - slack + 1 - w, so
+    truncating back to anchor - slack leaves at least w - 1 rows; the plain
+    trim then drains again."""
+    w, slack, align, anchor = 6, 2, 4, 40
+    base, n = 0, 0
+    for p in range(100):
+        n += 1
+        d = oracle.trim_window(base, n, w, slack, align, anchor)
+        base, n = base + d, n - d
+        assert base + w <= anchor - slack + 1
+    back = anchor - slack
+    n = oracle.truncate_last(n, base + n - back)
+    assert base + n == back and n >= w - 1
+    for p in range(back, back + 3 * w):
+        n += 1
+        d = oracle.trim_window(base, n, w, slack, align)
+        base, n = base + d, n - d
+    assert n <= 2 * w
+    assert oracle.truncate_last(5, 7) == 0 and oracle.truncate_last(5, 2) == 3
+
+
 def test_workload_generators_are_deterministic():
     s = workloads.get("batched_q8")
     L = s.lengths()
