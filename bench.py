@@ -253,6 +253,24 @@ def main():
         if int(cq.len.max()) + 40 <= cq.capacity:
             parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 5, repeats=1), 2)}
 
+        # [P2] trim_window over every sequence (window 8192, slack 64, align 64):
+        # runs once, last, since it shortens the cache.  Bytes: each kept row
+        # of each live head read and written once.
+        lens_before = cq.len.copy()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s_ev.record(stream)
+        dropped = [K.kv_trim_window(cq, b, 0, 8192, 64, 64)[1] for b in range(bq.batch)]
+        e_ev.record(stream)
+        e_ev.synchronize()
+        moved = sum(int(lens_before[b]) - d for b, d in enumerate(dropped) if d > 0)
+        us = s_ev.elapsed_time(e_ev) * 1e3
+        nb = moved * cq.n_live * 276 * 2
+        parts["kv_trim_window_all_seqs"] = {
+            "us_per_call": round(us, 2), "sequences_trimmed": int(sum(d > 0 for d in dropped)),
+            "rows_moved_per_head": moved, "bytes_moved": nb, "GBps": round(nb / us / 1e3, 1),
+            "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
+
     dominant = "decode_attn_q8" if do_q8 else "rswa_decode_f32"
     kernel_tag = "k_decode_q8_batched_q8" if do_q8 else "k_decode_f32_rswa_long_f32"
     d = parts[dominant]

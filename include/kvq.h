@@ -115,17 +115,32 @@ typedef struct kvq_cache {
 
 /*
  * R-SWA cursors of one sequence ([P3] RingCache fields prefill_len,
- * ring_len, ring_pos, decode_writes).  The sequence's rows are the read-only
- * reference block [0, prefill_len) followed by a ring of KVQ_RING_WINDOW
- * slots stored at rows [prefill_len, prefill_len + 128).
+ * ring_len, ring_pos, decode_writes, lineage_epoch).  The sequence's rows are
+ * the read-only reference block [0, prefill_len) followed by a ring of
+ * KVQ_RING_WINDOW slots stored at rows [prefill_len, prefill_len + 128).
  */
 typedef struct kvq_ring {
     int32_t prefill_len;     /* -1 until recorded */
     int32_t ring_len;        /* live ring slots, 0..128 */
     int32_t ring_pos;        /* next slot to overwrite once the ring is full */
-    int32_t reserved;
+    int32_t epoch;           /* lineage: advanced by a prefill and by a rollback that discards writes */
     int64_t writes;          /* ring writes since the prefill was recorded */
 } kvq_ring;
+
+/*
+ * A checkpoint of one sequence's ring cursors ([P3] RingCheckpoint): the
+ * cache and sequence it belongs to, and the cursors.  No K/V is copied.
+ */
+typedef struct kvq_ring_checkpoint {
+    const kvq_cache* cache;
+    int32_t seq;
+    int32_t prefill_len;
+    int32_t ring_len;
+    int32_t ring_pos;
+    int32_t epoch;
+    int32_t reserved;
+    int64_t writes;
+} kvq_ring_checkpoint;
 
 /*
  * Fill `c` for a new, empty cache: geometry, live-slot numbering from
@@ -288,6 +303,60 @@ int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* 
  * KVQ_ECAPACITY (len[seq] + 128 > capacity: no room for the ring).
  */
 int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
+
+/*
+ * rswa_checkpoint -- [P3] RingCache::checkpoint for sequence `seq`: copy its
+ * cursors into *cp (host), taken before speculative decode steps.  O(1), no
+ * device work.  Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not
+ * an f32 cache).
+ */
+int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring_checkpoint* cp);
+
+/*
+ * rswa_rollback_to -- [P3] RingCache::rollback_to: discard every decode
+ * step of sequence `seq` written since *cp was taken, by restoring ring_len,
+ * ring_pos and writes (len[seq] = prefill_len + ring_len).  The dead slots
+ * keep the discarded K/V and are never read.  A rollback that discards
+ * writes advances the epoch, so checkpoints of the abandoned branch stop
+ * matching.  Refused, with nothing changed, when the checkpoint belongs to
+ * another cache or sequence, another prefill or epoch, is from the future,
+ * or when the discarded writes overwrote a slot that was live at the
+ * checkpoint (cp->ring_len + discarded > 128).  No device work.
+ * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not an f32 cache,
+ * or any refusal above).
+ */
+int rswa_rollback_to(kvq_cache* c, kvq_ring* rings, int seq, const kvq_ring_checkpoint* cp);
+
+/*
+ * kv_truncate_last -- [P1]/[P2] LayerKvCache::truncate_last for sequence
+ * `seq` (or KVQ_ALL_SEQS): drop its last min(n_drop, len) rows, e.g. the
+ * rejected tokens of a speculative step.  Host cursor only: the rows stay in
+ * place and the next append overwrites them.  A q8 sequence keeps its frozen
+ * column field, as the page keeps the fields.  Not for R-SWA sequences,
+ * whose cursors rswa_rollback_to moves.
+ * Errors: KVQ_EINVAL (null, seq out of range, n_drop < 0).
+ */
+int kv_truncate_last(kvq_cache* c, int seq, int n_drop);
+
+/*
+ * kv_trim_window -- [P2] LayerKvCache::trim_window_anchored for sequence
+ * `seq`: drop the front rows a sliding-window layer of window w can never
+ * read again.  *base (host, in/out) is the absolute position of the
+ * sequence's row 0.  Nothing happens while len <= 2w, for w == 0, or on a q8
+ * sequence whose column field is not frozen yet (the freeze reads every
+ * row).  Otherwise the rows from
+ *   keep_from = min(base + len - (w + slack), anchor - (w + slack))  (>= 0)
+ * on stay, the cut rounded down to a multiple of max(align, 1):
+ *   d = (keep_from / align) * align - base   rows are dropped if d > 0,
+ * the remaining rows move to the front of the sequence's storage in order
+ * (one kernel on `stream`), len -= d, *base += d.  anchor < 0 means none.
+ * *dropped (may be NULL) receives d.  Windowed decodes of the trimmed
+ * sequence (first = len - w) see the same rows as before.
+ * Errors: KVQ_EINVAL (null cache/base, seq out of range, *base, w, slack or
+ * align < 0), KVQ_EDEVICE (launch failure).
+ */
+int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int align, int64_t anchor,
+                   int* dropped, void* stream);
 
 /*
  * rswa_decode -- one R-SWA decode step for every sequence of an f32 cache:

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -481,11 +482,115 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq) {
     if ((int64_t)c->len[seq] + KVQ_RING_WINDOW > c->capacity)
         return fail(KVQ_ECAPACITY, "%s: prefill %d + ring %d exceeds capacity %d", fn, c->len[seq],
                     KVQ_RING_WINDOW, c->capacity);
+    // a new prefill starts a new lineage ([P3] record_prefill)
+    if (rings[seq].epoch == INT32_MAX) return fail(KVQ_ESTATE, "%s: lineage epoch exhausted", fn);
     rings[seq].prefill_len = c->len[seq];
     rings[seq].ring_len = 0;
     rings[seq].ring_pos = 0;
-    rings[seq].reserved = 0;
+    rings[seq].epoch += 1;
     rings[seq].writes = 0;
+    return KVQ_OK;
+}
+
+int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring_checkpoint* cp) {
+    const char* fn = "rswa_checkpoint";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    const kvq_ring& r = rings[seq];
+    cp->cache = c;
+    cp->seq = seq;
+    cp->prefill_len = r.prefill_len;
+    cp->ring_len = r.ring_len;
+    cp->ring_pos = r.ring_pos;
+    cp->epoch = r.epoch;
+    cp->reserved = 0;
+    cp->writes = r.writes;
+    return KVQ_OK;
+}
+
+int rswa_rollback_to(kvq_cache* c, kvq_ring* rings, int seq, const kvq_ring_checkpoint* cp) {
+    const char* fn = "rswa_rollback_to";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    kvq_ring& r = rings[seq];
+    // [P3] rollback_to: the refusals, in the page's order, before any change
+    if (cp->cache != c || cp->seq != seq)
+        return fail(KVQ_ESTATE, "%s: checkpoint belongs to another cache or sequence", fn);
+    if (cp->prefill_len != r.prefill_len)
+        return fail(KVQ_ESTATE, "%s: checkpoint prefill_len %d != %d", fn, cp->prefill_len, r.prefill_len);
+    if (cp->epoch != r.epoch)
+        return fail(KVQ_ESTATE, "%s: stale checkpoint lineage (epoch %d != %d)", fn, cp->epoch, r.epoch);
+    if (cp->writes > r.writes)
+        return fail(KVQ_ESTATE, "%s: checkpoint is from the future (writes %lld > %lld)", fn, (long long)cp->writes,
+                    (long long)r.writes);
+    const int64_t discarded = r.writes - cp->writes;
+    if (cp->ring_len < 0 || cp->ring_len > KVQ_RING_WINDOW || discarded > KVQ_RING_WINDOW - cp->ring_len)
+        return fail(KVQ_ESTATE, "%s: not lossless: %lld discarded writes wrapped the ring past ring_len %d", fn,
+                    (long long)discarded, cp->ring_len);
+    if (discarded > 0 && r.epoch == INT32_MAX) return fail(KVQ_ESTATE, "%s: lineage epoch exhausted", fn);
+    r.ring_len = cp->ring_len;
+    r.ring_pos = cp->ring_pos;
+    r.writes = cp->writes;
+    if (discarded > 0) r.epoch += 1;
+    c->len[seq] = r.prefill_len + r.ring_len;
+    return KVQ_OK;
+}
+
+int kv_truncate_last(kvq_cache* c, int seq, int n_drop) {
+    const char* fn = "kv_truncate_last";
+    int rc = check_cache(c, 0, fn);
+    if (rc) return rc;
+    if (n_drop < 0) return fail(KVQ_EINVAL, "%s: n_drop %d < 0", fn, n_drop);
+    if (seq != KVQ_ALL_SEQS && (seq < 0 || seq >= c->batch))
+        return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    const int b0 = seq == KVQ_ALL_SEQS ? 0 : seq, b1 = seq == KVQ_ALL_SEQS ? c->batch : seq + 1;
+    for (int b = b0; b < b1; ++b) c->len[b] -= std::min(n_drop, c->len[b]);
+    return KVQ_OK;
+}
+
+int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int align, int64_t anchor,
+                   int* dropped, void* stream) {
+    const char* fn = "kv_trim_window";
+    int rc = check_cache(c, 0, fn);
+    if (rc) return rc;
+    if (!base) return fail(KVQ_EINVAL, "%s: null base", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if (*base < 0 || w < 0 || slack < 0 || align < 0)
+        return fail(KVQ_EINVAL, "%s: base %lld, w %d, slack %d, align %d must be >= 0", fn, (long long)*base, w, slack,
+                    align);
+    if (dropped) *dropped = 0;
+    const int64_t n = c->len[seq];
+    // [P2] trim_window_anchored, step by step
+    if (w == 0 || n <= 2 * (int64_t)w) return KVQ_OK;
+    if (c->kind == KVQ_KIND_Q8 && !c->frozen[seq]) return KVQ_OK;
+    const int64_t al = std::max(align, 1);
+    int64_t keep_from = std::max<int64_t>(*base + n - (w + slack), 0);
+    if (anchor >= 0) keep_from = std::min(keep_from, std::max<int64_t>(anchor - (w + slack), 0));
+    const int64_t new_base = keep_from / al * al;
+    if (new_base <= *base) return KVQ_OK;
+    const int d = (int)(new_base - *base);            // < n: new_base <= keep_from < base + n
+    MoveArgs m;
+    memset(&m, 0, sizeof m);
+    m.k = c->k;
+    m.v = c->v;
+    m.kq = c->kq;
+    m.ks = c->ks;
+    m.vq = c->vq;
+    m.vs = c->vs;
+    m.n_live = c->n_live;
+    m.capacity = c->capacity;
+    m.q8 = c->kind == KVQ_KIND_Q8;
+    m.seq = seq;
+    m.d = d;
+    m.keep = (int)(n - d);
+    if (c->n_live > 0 && (rc = device_status(launch_move_rows(m, (hipStream_t)stream), fn))) return rc;
+    c->len[seq] = (int32_t)(n - d);
+    *base = new_base;
+    if (dropped) *dropped = d;
     return KVQ_OK;
 }
 

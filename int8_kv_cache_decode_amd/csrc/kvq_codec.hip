@@ -134,7 +134,47 @@ __global__ __launch_bounds__(128) void k_freeze(const FreezeArgs a) {
     }
 }
 
+// Front-trim move ([P2] trim_window: the rows that stay keep their order and
+// values), one chunk of m <= d rows per launch: rows [src, src + m) go to
+// [dst, dst + m) with src - dst = d >= m, so a launch's source and
+// destination never overlap, and consecutive launches on the stream order a
+// chunk's reads before the next chunk's writes.  grid (blocks, live head,
+// buffer), block 256, a grid-stride loop of 16-byte (vs: 4-byte) copies.
+template <class T>
+__device__ __forceinline__ void copy_rows(T* base, int units_per_row, int src, int dst, int m) {
+    const T* s = base + (size_t)src * units_per_row;
+    T* d = base + (size_t)dst * units_per_row;
+    const size_t n = (size_t)m * units_per_row;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        d[i] = s[i];
+}
+
+__global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, int dst, int m) {
+    const size_t row0 = ((size_t)a.seq * a.n_live + blockIdx.y) * a.capacity;
+    switch (a.q8 ? blockIdx.z : 4 + blockIdx.z) {
+        case 0: copy_rows(reinterpret_cast<uint4*>(a.kq + row0 * kHD), kHD / 16, src, dst, m); break;
+        case 1: copy_rows(reinterpret_cast<uint4*>(a.ks + row0 * kKScales), 1, src, dst, m); break;
+        case 2: copy_rows(reinterpret_cast<uint4*>(a.vq + row0 * kHD), kHD / 16, src, dst, m); break;
+        case 3: copy_rows(reinterpret_cast<uint32_t*>(a.vs + row0), 1, src, dst, m); break;
+        case 4: copy_rows(reinterpret_cast<uint4*>(a.k + row0 * kHD), kHD / 4, src, dst, m); break;
+        default: copy_rows(reinterpret_cast<uint4*>(a.v + row0 * kHD), kHD / 4, src, dst, m); break;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s) {
+    for (int r = 0; r < a.keep; r += a.d) {
+        const int m = min(a.d, a.keep - r);
+        const size_t units = (size_t)m * (a.q8 ? kHD / 16 : kHD / 4);     // largest buffer, 16-byte units
+        const size_t want = (units + 1023) / 1024;
+        const int blocks = (int)(want < 128 ? want : 128);
+        hipLaunchKernelGGL(k_move_chunk, dim3(blocks, a.n_live, a.q8 ? 4 : 2), dim3(256), 0, s, a, a.d + r, r, m);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s) {
     hipLaunchKernelGGL(k_append_f32, dim3(n_rows, a.n_seq, a.n_live), dim3(64), 0, s, a);

@@ -68,11 +68,30 @@ struct FreezeArgs {
     int32_t n[kSeqPerLaunch];                // rows to freeze over
 };
 
+// Front-trim move of one sequence: rows [d, d + keep) of every live head go
+// to rows [0, keep), in order.
+struct MoveArgs {
+    float* k;
+    float* v;
+    int8_t* kq;
+    float* ks;
+    int8_t* vq;
+    float* vs;
+    int n_live;
+    int capacity;
+    int q8;
+    int seq;
+    int d;
+    int keep;
+};
+
 // grid (n_rows, n_seq, n_live)
 hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s);
 hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s);
 // grid (n_live, n_seq)
 hipError_t launch_freeze(const FreezeArgs& a, hipStream_t s);
+// one launch per chunk of d rows
+hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s);
 
 // ---- decode --------------------------------------------------------------
 struct DecodeArgs {

@@ -43,8 +43,14 @@ class kvq_cache(ctypes.Structure):
 
 class kvq_ring(ctypes.Structure):
     _fields_ = [("prefill_len", ctypes.c_int32), ("ring_len", ctypes.c_int32),
-                ("ring_pos", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ring_pos", ctypes.c_int32), ("epoch", ctypes.c_int32),
                 ("writes", ctypes.c_int64)]
+
+
+class kvq_ring_checkpoint(ctypes.Structure):
+    _fields_ = [("cache", _P), ("seq", ctypes.c_int32), ("prefill_len", ctypes.c_int32),
+                ("ring_len", ctypes.c_int32), ("ring_pos", ctypes.c_int32), ("epoch", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("writes", ctypes.c_int64)]
 
 
 class kvq_decode_opts(ctypes.Structure):
@@ -69,6 +75,11 @@ _SIGNATURES = [
     ("decode_attn_q8_ex", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("rswa_record_prefill", ctypes.c_int, [_P, _P, ctypes.c_int]),
     ("rswa_decode", ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("rswa_checkpoint", ctypes.c_int, [_P, _P, ctypes.c_int, _P]),
+    ("rswa_rollback_to", ctypes.c_int, [_P, _P, ctypes.c_int, _P]),
+    ("kv_truncate_last", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
+    ("kv_trim_window", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int64, _P, _P]),
     ("kvq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -283,3 +294,27 @@ def rswa_decode(cache: KvCache, rings: Rings, n_q_heads: int, q, k_new, v_new, o
     nb = ws.numel() if ws_bytes is None else ws_bytes
     _check(lib().rswa_decode(cache.ref, rings.ref, n_q_heads, _ptr(q), _ptr(k_new), _ptr(v_new),
                              _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def rswa_checkpoint(cache: KvCache, rings: Rings, seq: int) -> kvq_ring_checkpoint:
+    cp = kvq_ring_checkpoint()
+    _check(lib().rswa_checkpoint(cache.ref, rings.ref, seq, ctypes.byref(cp)))
+    return cp
+
+
+def rswa_rollback_to(cache: KvCache, rings: Rings, seq: int, cp: kvq_ring_checkpoint) -> None:
+    _check(lib().rswa_rollback_to(cache.ref, rings.ref, seq, ctypes.byref(cp)))
+
+
+def kv_truncate_last(cache: KvCache, seq: int, n_drop: int) -> None:
+    _check(lib().kv_truncate_last(cache.ref, seq, n_drop))
+
+
+def kv_trim_window(cache: KvCache, seq: int, base: int, w: int, slack: int, align: int, anchor: int = -1,
+                   stream=None):
+    """Returns (new base, rows dropped)."""
+    b = ctypes.c_int64(base)
+    d = ctypes.c_int(0)
+    _check(lib().kv_trim_window(cache.ref, seq, ctypes.byref(b), w, slack, align, anchor, ctypes.byref(d),
+                                _stream(stream)))
+    return b.value, d.value

@@ -163,6 +163,105 @@ def test_decode_option_refusals():
     expect(call("decode_attn_f32_ex", c.ref, 32, FAKE, FAKE, None, FAKE, 1 << 40, None), K.ESTATE, c, before)
 
 
+def test_truncate_last_moves_the_cursor_only():
+    """[P1]/[P2] truncate_last: drop the last min(n_drop, len) rows."""
+    c = fake_cache(K.KIND_Q8, batch=3)
+    c.len[:] = [10, 3, 0]
+    c.frozen[:] = [1, 0, 0]
+    K.kv_truncate_last(c, 0, 4)
+    assert list(c.len) == [6, 3, 0] and list(c.frozen) == [1, 0, 0]
+    K.kv_truncate_last(c, K.ALL_SEQS, 5)
+    assert list(c.len) == [1, 0, 0]
+    before = snapshot(c)
+    expect(call("kv_truncate_last", c.ref, 0, -1), K.EINVAL, c, before)
+    expect(call("kv_truncate_last", c.ref, 3, 1), K.EINVAL, c, before)
+
+
+def test_trim_window_no_op_cases_and_refusals():
+    """[P2] trim_window: nothing while len <= 2w, for w == 0, on a q8
+    sequence whose field is not frozen, or when the rounded cut does not pass
+    the base; bad arguments are refused with nothing changed.  (Trims that
+    move rows run on the GPU.)"""
+    c = fake_cache(K.KIND_F32, batch=2, cap=256)
+    c.len[:] = [20, 21]
+    assert K.kv_trim_window(c, 0, 0, 10, 2, 4, stream=0) == (0, 0)          # 20 <= 2w
+    assert K.kv_trim_window(c, 1, 0, 0, 2, 4, stream=0) == (0, 0)           # w == 0
+    assert K.kv_trim_window(c, 1, 12, 10, 2, 32, stream=0) == (12, 0)       # cut rounds down to 0 <= base
+    q = fake_cache(K.KIND_Q8, batch=1, cap=256)
+    q.len[:] = [200]
+    assert K.kv_trim_window(q, 0, 0, 10, 2, 4, stream=0) == (0, 0)          # field not frozen
+    assert list(c.len) == [20, 21] and list(q.len) == [200]
+    base = ctypes.c_int64(0)
+    before = snapshot(c)
+    expect(call("kv_trim_window", c.ref, 0, None, 5, 1, 1, -1, None, 0), K.EINVAL, c, before)
+    expect(call("kv_trim_window", c.ref, 2, ctypes.byref(base), 5, 1, 1, -1, None, 0), K.EINVAL, c, before)
+    for w, sl, al in ((-1, 1, 1), (5, -1, 1), (5, 1, -1)):
+        expect(call("kv_trim_window", c.ref, 0, ctypes.byref(base), w, sl, al, -1, None, 0), K.EINVAL, c, before)
+    base = ctypes.c_int64(-3)
+    expect(call("kv_trim_window", c.ref, 0, ctypes.byref(base), 5, 1, 1, -1, None, 0), K.EINVAL, c, before)
+
+
+def test_ring_checkpoint_and_rollback_cursors():
+    """[P3] checkpoint / rollback_to on the host cursors, the page's 9-accept,
+    6-draft example; a no-op rollback keeps the lineage; a re-prefill starts
+    a new one."""
+    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=400)
+    rings = K.Rings(2)
+    c.len[:] = [5, 0]
+    K.rswa_record_prefill(c, rings, 0)
+    e0 = rings[0].epoch
+    r = rings[0]
+    r.ring_len, r.ring_pos, r.writes = 9, 9, 9              # 9 accepted steps
+    c.len[0] = 14
+    cp = K.rswa_checkpoint(c, rings, 0)
+    assert (cp.prefill_len, cp.ring_len, cp.ring_pos, cp.writes, cp.epoch, cp.seq) == (5, 9, 9, 9, e0, 0)
+    r.ring_len, r.ring_pos, r.writes = 15, 15, 15           # 6 draft steps
+    c.len[0] = 20
+    K.rswa_rollback_to(c, rings, 0, cp)
+    assert (r.ring_len, r.ring_pos, r.writes, c.len[0]) == (9, 9, 9, 14) and r.epoch == e0 + 1
+    cp2 = K.rswa_checkpoint(c, rings, 0)
+    K.rswa_rollback_to(c, rings, 0, cp2)                    # nothing discarded: identity
+    assert (r.ring_len, r.writes, r.epoch, c.len[0]) == (9, 9, e0 + 1, 14)
+    K.rswa_record_prefill(c, rings, 1)
+    assert rings[1].epoch == 1
+
+
+def test_ring_rollback_refusals_leave_everything_unchanged():
+    """[P3] rollback_to refusals: another cache, another sequence, a stale
+    lineage, a checkpoint from the future, and discarded writes that wrapped
+    onto slots live at the checkpoint (steady state)."""
+    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=400)
+    other = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=400)
+    rings, orings = K.Rings(2), K.Rings(2)
+    c.len[:] = [3, 3]
+    other.len[:] = [3, 3]
+    for b in range(2):
+        K.rswa_record_prefill(c, rings, b)
+        K.rswa_record_prefill(other, orings, b)
+    r = rings[0]
+    r.ring_len, r.ring_pos, r.writes = 128, 0, 128          # ring just full
+    c.len[0] = 131
+    cp_full = K.rswa_checkpoint(c, rings, 0)
+    r.ring_pos, r.writes = 1, 129                           # one steady-state write
+    before = snapshot(c, rings)
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(cp_full)), K.ESTATE, c, before, rings)
+    foreign = K.rswa_checkpoint(other, orings, 0)
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(foreign)), K.ESTATE, c, before, rings)
+    seq1 = K.rswa_checkpoint(c, rings, 1)
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(seq1)), K.ESTATE, c, before, rings)
+    cp = K.rswa_checkpoint(c, rings, 0)
+    fut = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+    fut.writes += 1
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(fut)), K.ESTATE, c, before, rings)
+    stale = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+    stale.epoch -= 1
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(stale)), K.ESTATE, c, before, rings)
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, None), K.EINVAL, c, before, rings)
+    q = fake_cache(K.KIND_Q8)
+    bq = snapshot(q)
+    expect(call("rswa_checkpoint", q.ref, rings.ref, 0, ctypes.byref(cp)), K.ESTATE, q, bq)
+
+
 def test_rswa_refusals_leave_cache_and_rings_unchanged():
     c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=200)
     rings = K.Rings(2)

@@ -1,0 +1,179 @@
+"""GPU: row management around the decode ([P2] LayerKvCache::truncate_last,
+trim_window_anchored; [P3] RingCache::checkpoint / rollback_to) through the
+C ABI.  Moved rows, codes and scales are compared bit for bit with the rows
+they came from; decodes after a trim, a truncate or a rollback are compared
+with the oracle over the rows the pages say stay visible, or bit for bit
+with a control cache that never took the detour."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_kv_cache_decode_amd import kvq as K
+from gpu_cases import F32_TOL, THREADS, append_rows, assert_codes_equal, dev, host, max_err, oracle_q8_heads, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.lib()
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+BUFS = {K.KIND_F32: ("k", "v"), K.KIND_Q8: ("kq", "ks", "vq", "vs")}
+
+
+# (lens, w, slack, align, anchor): overlapping moves (keep > d), disjoint
+# ones (keep <= d), many chunks, an anchored cut, and a no-op.
+TRIMS = [([3000, 2001], 1400, 150, 16, -1),
+         ([2001, 700], 1000, 0, 4, -1),
+         ([900, 2500], 300, 2, 64, -1),
+         ([1500, 1500], 200, 10, 8, 900),
+         ([300, 100], 200, 10, 8, -1)]
+
+
+@pytest.mark.parametrize("case", range(len(TRIMS)))
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
+    lens, w, slack, align, anchor = TRIMS[case]
+    say("case: trim kind", kind, "lens", lens, "w", w, "slack", slack, "align", align, "anchor", anchor)
+    r = rng(100 + case + 10 * kind)
+    hkv, hpk = 3, 2
+    alive = np.array([1, 0, 1], np.uint8)
+    cap = max(lens)
+    c = K.KvCache(kind, len(lens), hkv, cap, alive=alive)
+    rows = []
+    for b, n in enumerate(lens):
+        k = (r.standard_normal((n, hkv, 128)) * 2).astype(np.float32)
+        v = (r.standard_normal((n, hkv, 128)) * 2).astype(np.float32)
+        append_rows(c, b, k, v)
+        rows.append((k, v))
+    torch.cuda.synchronize()
+    before = {nm: host(c.view(nm)).copy() for nm in BUFS[kind]}
+    q = r.standard_normal((len(lens), hkv * hpk, 128)).astype(np.float32)
+    bases = []
+    for b, n in enumerate(lens):
+        want = oracle.trim_window(0, n, w, slack, align, None if anchor < 0 else anchor,
+                                  q8_unfrozen=(kind == K.KIND_Q8 and n < 64))
+        base, d = K.kv_trim_window(c, b, 0, w, slack, align, anchor)
+        assert d == want and base == d and c.len[b] == n - d
+        bases.append(base)
+    torch.cuda.synchronize()
+    # every live head's rows [d, n) now sit at [0, n - d), bit for bit
+    for nm in BUFS[kind]:
+        after = host(c.view(nm))
+        for b, n in enumerate(lens):
+            d = bases[b]
+            assert np.array_equal(after[b, :, : n - d].view(np.uint8), before[nm][b, :, d:n].view(np.uint8)), (nm, b)
+    # the windowed decode (first = len - w) of the trimmed cache sees the rows
+    # the untrimmed cache's window sees
+    first = np.maximum(c.len.astype(np.int64) - w, 0).astype(np.int32)
+    out = torch.full((len(lens), hkv * hpk, 128), np.nan, device="cuda")
+    fn = K.decode_attn_f32_ex if kind == K.KIND_F32 else K.decode_attn_q8_ex
+    fn(c, hkv * hpk, dev(q), out, K.DecodeOpts(first=first))
+    torch.cuda.synchronize()
+    units = [[None] * hkv for _ in lens]
+    full_first = []
+    for b, n in enumerate(lens):
+        k, v = rows[b]
+        full_first.append(max(n - w, 0))
+        if kind == K.KIND_Q8:
+            heads = oracle_q8_heads(k, v, alive, cap=n)
+            for g in range(hkv):
+                units[b][g] = ("q8", heads[g]) if alive[g] else None
+        else:
+            for g in range(hkv):
+                units[b][g] = ("f32", np.ascontiguousarray(k[:, g]), np.ascontiguousarray(v[:, g])) if alive[g] else None
+    ref = oracle.decode(q, units, hkv, threads=THREADS, first=full_first)
+    err = max_err(host(out), ref)
+    say("  max err %.3g" % err)
+    assert err <= F32_TOL, err
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+def test_truncate_then_append_equals_never_appended(kind):
+    """[P2] truncate_last after a speculative append: the replacement rows
+    land where the rejected ones were; storage and decode equal a cache that
+    only ever saw the accepted rows (a q8 field frozen before keeps its
+    values)."""
+    say("case: truncate kind", kind)
+    r = rng(200 + kind)
+    hkv, hpk, n0 = 2, 4, 150
+    base_k = (r.standard_normal((n0, hkv, 128)) * 2).astype(np.float32)
+    base_v = (r.standard_normal((n0, hkv, 128)) * 2).astype(np.float32)
+    draft = [(r.standard_normal((5, hkv, 128)) * 2).astype(np.float32) for _ in range(2)]
+    final = [(r.standard_normal((3, hkv, 128)) * 2).astype(np.float32) for _ in range(2)]
+    test = K.KvCache(kind, 1, hkv, 200)
+    ctrl = K.KvCache(kind, 1, hkv, 200)
+    for cc in (test, ctrl):
+        append_rows(cc, 0, base_k, base_v)
+    append_rows(test, 0, *draft)
+    K.kv_truncate_last(test, 0, 5)
+    assert test.len[0] == n0
+    for cc in (test, ctrl):
+        append_rows(cc, 0, *final)
+    torch.cuda.synchronize()
+    n = n0 + 3
+    for nm in BUFS[kind]:
+        a, b = host(test.view(nm)), host(ctrl.view(nm))
+        assert np.array_equal(a[:, :, :n].view(np.uint8), b[:, :, :n].view(np.uint8)), nm
+    q = dev(r.standard_normal((1, hkv * hpk, 128)).astype(np.float32))
+    o1, o2 = (torch.full((1, hkv * hpk, 128), np.nan, device="cuda") for _ in range(2))
+    fn = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
+    fn(test, hkv * hpk, q, o1)
+    fn(ctrl, hkv * hpk, q, o2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o1).view(np.uint32), host(o2).view(np.uint32))
+
+
+def test_rswa_rollback_restores_the_accepted_path():
+    """[P3] test checkpoint_rollback_restores_ring_rows_byte_identical at the
+    decode level: 5 reference rows, 9 accepted steps, checkpoint, 6 draft
+    steps, rollback, then more accepted steps: every output and every live
+    row equals a control cache that never speculated, and the first dead
+    slot still holds a draft row."""
+    say("case: rswa rollback")
+    r = rng(300)
+    nh, pf = 4, 5
+    test = K.KvCache(K.KIND_F32, 1, nh, pf + 128)
+    ctrl = K.KvCache(K.KIND_F32, 1, nh, pf + 128)
+    rt, rc = K.Rings(1), K.Rings(1)
+    ref = (r.standard_normal((2, pf, nh, 128))).astype(np.float32)
+    for cc, rr in ((test, rt), (ctrl, rc)):
+        append_rows(cc, 0, ref[0], ref[1])
+        K.rswa_record_prefill(cc, rr, 0)
+    acc = [tuple(dev(r.standard_normal((1, nh, 128)).astype(np.float32)) for _ in range(3)) for _ in range(14)]
+    drafts = [tuple(dev(r.standard_normal((1, nh, 128)).astype(np.float32) + 3) for _ in range(3)) for _ in range(6)]
+    ot, oc = (torch.zeros((1, nh, 128), device="cuda") for _ in range(2))
+    for t in range(9):
+        q, k, v = acc[t]
+        K.rswa_decode(test, rt, nh, q, k, v, ot)
+        K.rswa_decode(ctrl, rc, nh, q, k, v, oc)
+    cp = K.rswa_checkpoint(test, rt, 0)
+    assert (cp.ring_len, cp.ring_pos, cp.prefill_len) == (9, 9, pf)
+    for q, k, v in drafts:
+        K.rswa_decode(test, rt, nh, q, k, v, ot)
+    assert rt[0].ring_len == 15
+    K.rswa_rollback_to(test, rt, 0, cp)
+    assert (rt[0].ring_len, rt[0].ring_pos, rt[0].writes, test.len[0]) == (9, 9, 9, pf + 9)
+    torch.cuda.synchronize()
+    kt = host(test.view("k"))[0]
+    assert np.array_equal(kt[:, pf + 9], host(drafts[0][1])[0])          # stale, never read
+    for t in range(9, 14):
+        q, k, v = acc[t]
+        K.rswa_decode(test, rt, nh, q, k, v, ot)
+        K.rswa_decode(ctrl, rc, nh, q, k, v, oc)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ot).view(np.uint32), host(oc).view(np.uint32)), t
+    n = pf + 14
+    for nm in ("k", "v"):
+        assert np.array_equal(host(test.view(nm))[:, :, :n], host(ctrl.view(nm))[:, :, :n])
+    # the abandoned branch's checkpoint no longer matches
+    with pytest.raises(K.KvqError):
+        K.rswa_rollback_to(test, rt, 0, cp)
