@@ -344,6 +344,37 @@ class RingModel:
 
 
 # --------------------------------------------------------------------------
+# Query-batched verify ([P3] verify_attention)
+# --------------------------------------------------------------------------
+def rswa_verify(q, ref_k, ref_v, history_k, history_v, draft_k, draft_v, window: int = RING_W):
+    """K-token verify by definition: draft query i attends, with no mask, to
+    the reference rows plus the ring as it would stand after the draft
+    tokens 0..i were written in order -- the last min(window, n + i + 1)
+    tokens of (history ++ draft[0..i]) -- i.e. the i-th of K sequential
+    decode steps; nothing is written.
+
+    q        [K][Hq][hd] f32 draft queries
+    ref_k/v  [Hkv][P][hd] f32 reference rows
+    history  [Hkv][n][hd] f32: every ring token written since the prefill,
+             oldest first (only the last `window` are live)
+    draft    [K][Hkv][hd] f32
+    Returns out [K][Hq][hd] float64."""
+    q = _f32(q)
+    K_, Hq, hd = q.shape
+    Hkv = ref_k.shape[0]
+    hpk = Hq // Hkv
+    out = np.zeros((K_, Hq, hd), np.float64)
+    for i in range(K_):
+        for g in range(Hkv):
+            toks_k = np.concatenate([history_k[g], draft_k[: i + 1, g]])
+            toks_v = np.concatenate([history_v[g], draft_v[: i + 1, g]])
+            rows_k = np.concatenate([ref_k[g], toks_k[-window:]])
+            rows_v = np.concatenate([ref_v[g], toks_v[-window:]])
+            out[i, g * hpk:(g + 1) * hpk] = attend_f32(q[i, g * hpk:(g + 1) * hpk], rows_k, rows_v)
+    return out
+
+
+# --------------------------------------------------------------------------
 # Row management around the decode ([P2] LayerKvCache::truncate_last,
 # trim_window_anchored)
 # --------------------------------------------------------------------------

@@ -818,6 +818,45 @@ def test_trim_window_anchored_page_example():
     assert oracle.truncate_last(5, 7) == 0 and oracle.truncate_last(5, 2) == 3
 
 
+@pytest.mark.parametrize("prefill,n_hist,K", [(7, 5, 4), (7, 126, 5), (3, 300, 6), (0, 0, 3)])
+def test_verify_equals_sequential_ring_steps(prefill, n_hist, K):
+    """[P3] verify_attention: draft i's context is the i-th of K sequential
+    decode steps -- computed here on the physical ring of a RingModel
+    (pinned by the ring tests), written slot by slot, warm-up, crossing the
+    window and in steady state; query i never sees drafts after i."""
+    r = rng(4000 + prefill + n_hist + K)
+    hkv, hpk, W = 2, 2, oracle.RING_W
+    ref_k = r.standard_normal((hkv, prefill, HD)).astype(np.float32)
+    ref_v = r.standard_normal((hkv, prefill, HD)).astype(np.float32)
+    hist_k = r.standard_normal((hkv, n_hist, HD)).astype(np.float32)
+    hist_v = r.standard_normal((hkv, n_hist, HD)).astype(np.float32)
+    dk = r.standard_normal((K, hkv, HD)).astype(np.float32)
+    dv = r.standard_normal((K, hkv, HD)).astype(np.float32)
+    q = r.standard_normal((K, hkv * hpk, HD)).astype(np.float32)
+    got = oracle.rswa_verify(q, ref_k, ref_v, hist_k, hist_v, dk, dv)
+    m = oracle.RingModel(W)
+    m.record_prefill(prefill)
+    ring_k = np.zeros((hkv, W, HD), np.float32)
+    ring_v = np.zeros((hkv, W, HD), np.float32)
+    for t in range(n_hist):
+        s_ = m.write(t)
+        ring_k[:, s_], ring_v[:, s_] = hist_k[:, t], hist_v[:, t]
+    for i in range(K):
+        s_ = m.write(n_hist + i)
+        ring_k[:, s_], ring_v[:, s_] = dk[i], dv[i]
+        for g in range(hkv):
+            rows_k = np.concatenate([ref_k[g], ring_k[g, : m.ring_len]])
+            rows_v = np.concatenate([ref_v[g], ring_v[g, : m.ring_len]])
+            want = oracle.attend_f32(q[i, g * hpk:(g + 1) * hpk], rows_k, rows_v)
+            np.testing.assert_allclose(got[i, g * hpk:(g + 1) * hpk], want, rtol=0, atol=1e-13)
+    # a later draft token does not reach an earlier query
+    dk2, dv2 = dk.copy(), dv.copy()
+    dk2[-1] += 5.0
+    dv2[-1] -= 3.0
+    got2 = oracle.rswa_verify(q, ref_k, ref_v, hist_k, hist_v, dk2, dv2)
+    assert np.array_equal(got2[:-1], got[:-1]) and not np.array_equal(got2[-1], got[-1])
+
+
 def test_workload_generators_are_deterministic():
     s = workloads.get("batched_q8")
     L = s.lengths()
