@@ -220,6 +220,30 @@ def main():
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
             "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
             "kv_positions_per_s": round((rs.prefill + rs.window) / us * 1e6, 1)}
+
+        # [P3] verify_attention: 8 draft tokens checked against the same
+        # replicas, nothing written; bytes as the decode (each row read once
+        # for all 8 queries) plus the drafts, queries and outputs
+        n_draft = 8
+        vq_ = t(workloads.normal_f32(workloads.key(rs.seed, 91), (1, n_draft, rs.n_heads, 128)))
+        vk_ = t(workloads.normal_f32(workloads.key(rs.seed, 92), (1, n_draft, rs.n_heads, 128)))
+        vv_ = t(workloads.normal_f32(workloads.key(rs.seed, 93), (1, n_draft, rs.n_heads, 128)))
+        vout = torch.zeros((1, n_draft, rs.n_heads, 128), device=dev)
+        vws = torch.empty(K.kvq_verify_workspace_bytes(rswa[0][0], rs.n_heads, n_draft), dtype=torch.uint8,
+                          device=dev)
+
+        def verify_call(i):
+            c, rings, _ = rswa[i % len(rswa)]
+            K.rswa_verify(c, rings, rs.n_heads, n_draft, vq_, vk_, vv_, vout, vws)
+        us = time_calls(verify_call, 100)
+        rows = rs.prefill + rs.window
+        nb = rows * rs.n_heads * 1024 + n_draft * rs.n_heads * 512 * 4
+        flops = 4 * 128 * n_draft * rs.n_heads * (rows + n_draft)
+        parts["rswa_verify_f32_k8"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "mfma_TFLOPs": round(flops / us / 1e6, 2),
+            "draft_positions_per_s": round(n_draft * rows / us * 1e6, 1)}
     if do_q8:
         def q8_call(i):
             K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)

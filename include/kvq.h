@@ -305,6 +305,31 @@ int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* 
 int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
 
 /*
+ * rswa_verify -- [P3] verify_attention: the query-batched verify of
+ * speculative decoding.  For every sequence b and draft i < n_draft, out[b][i]
+ * is what the i-th of n_draft sequential rswa_decode steps fed with the draft
+ * tokens 0..i would return: each Q head attends, with no mask, to the
+ * reference rows, the ring as it would stand after draft tokens 0..i were
+ * written (the oldest live slots evicted once it is full), and those draft
+ * tokens.  Nothing is written: the cache and the ring cursors are unchanged
+ * (accepting drafts is then rswa_decode, or a checkpoint / rollback).
+ *
+ * q        device float [batch][n_draft][n_q_heads][128]
+ * k_draft, v_draft  device float [batch][n_draft][n_kv_heads][128]
+ * out      device float [batch][n_draft][n_q_heads][128]
+ * ws/ws_bytes  device workspace of at least kvq_verify_workspace_bytes().
+ * n_draft x (n_q_heads / n_kv_heads) must be within 1..16.
+ * Errors: KVQ_EINVAL (null, unaligned, bad counts, workspace too small),
+ * KVQ_ESTATE (not an f32 cache, a prefill not recorded, or a len that no
+ * longer matches the cursors).
+ */
+int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_draft, const float* q,
+                const float* k_draft, const float* v_draft, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes rswa_verify needs (0 on invalid arguments). */
+size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft);
+
+/*
  * rswa_checkpoint -- [P3] RingCache::checkpoint for sequence `seq`: copy its
  * cursors into *cp (host), taken before speculative decode steps.  O(1), no
  * device work.  Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not

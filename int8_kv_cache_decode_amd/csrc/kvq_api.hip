@@ -640,6 +640,78 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
     return KVQ_OK;
 }
 
+size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft) {
+    if (!c || c->n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % c->n_kv_heads || n_draft < 1) return 0;
+    const int nq = n_draft * (n_q_heads / c->n_kv_heads);
+    return nq > kVerifyMaxQ ? 0 : ws_need(c, nq);
+}
+
+int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_draft, const float* q,
+                const float* k_draft, const float* v_draft, float* out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "rswa_verify";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "%s: n_q_heads %d is not a multiple of n_kv_heads %d", fn, n_q_heads, c->n_kv_heads);
+    const int hpk = n_q_heads / c->n_kv_heads;
+    if (n_draft < 1 || n_draft * hpk > kVerifyMaxQ)
+        return fail(KVQ_EINVAL, "%s: n_draft %d x group %d must be within 1..%d", fn, n_draft, hpk, kVerifyMaxQ);
+    if (!rings || !q || !k_draft || !v_draft || !out || !ws) return fail(KVQ_EINVAL, "%s: null argument", fn);
+    if (!aligned16(q) || !aligned16(k_draft) || !aligned16(v_draft) || !aligned16(out) || !aligned16(ws))
+        return fail(KVQ_EINVAL, "%s: q/k_draft/v_draft/out/workspace not 16-byte aligned", fn);
+    const size_t need = ws_need(c, n_draft * hpk);
+    if (ws_bytes < need) return fail(KVQ_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    for (int b = 0; b < c->batch; ++b) {
+        const kvq_ring& r = rings[b];
+        if (r.prefill_len < 0) return fail(KVQ_ESTATE, "%s: sequence %d: verify before record_prefill", fn, b);
+        if (r.ring_len < 0 || r.ring_len > KVQ_RING_WINDOW || r.ring_pos < 0 || r.ring_pos >= KVQ_RING_WINDOW)
+            return fail(KVQ_ESTATE, "%s: sequence %d: corrupt ring cursors", fn, b);
+        if (c->len[b] != r.prefill_len + r.ring_len)
+            return fail(KVQ_ESTATE, "%s: sequence %d: len %d != prefill %d + ring %d", fn, b, c->len[b], r.prefill_len,
+                        r.ring_len);
+    }
+    VerifyArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.out = out;
+    a.k = c->k;
+    a.v = c->v;
+    a.kd = k_draft;
+    a.vd = v_draft;
+    a.ws_acc = (float*)ws;
+    a.ws_ml = (float*)ws + ws_slots(c) * (size_t)(n_draft * hpk) * kHD;
+    a.n_kv_heads = c->n_kv_heads;
+    a.n_live = c->n_live;
+    a.n_q_heads = n_q_heads;
+    a.hpk = hpk;
+    a.capacity = c->capacity;
+    a.n_draft = n_draft;
+    a.nq = n_draft * hpk;
+    fill_live(c, a.live_head);
+    memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
+    for (int s0 = 0; s0 < c->batch; s0 += kSeqPerLaunch) {
+        const int ns = std::min(kSeqPerLaunch, c->batch - s0);
+        a.seq0 = s0;
+        a.n_seq = ns;
+        int64_t tiles = 0;
+        for (int j = 0; j < ns; ++j) {
+            const kvq_ring& r = rings[s0 + j];
+            a.prefill[j] = r.prefill_len;
+            a.ring_len[j] = r.ring_len;
+            a.ring_oldest[j] = r.ring_len < KVQ_RING_WINDOW ? 0 : r.ring_pos;
+            a.len[j] = r.prefill_len + r.ring_len + n_draft;
+            a.ntile[j] = (a.len[j] + kTileRows - 1) / kTileRows;
+            a.tile_base[j] = (int32_t)tiles;
+            tiles += (int64_t)a.ntile[j] * c->n_live;
+            if (tiles >= ((int64_t)1 << 31)) return fail(KVQ_EINVAL, "%s: more than 2^31 tiles in one launch", fn);
+        }
+        a.tile_base[ns] = (int32_t)tiles;
+        a.n_tiles = (int)tiles;
+        if ((rc = device_status(launch_verify_f32(a, (hipStream_t)stream), fn))) return rc;
+    }
+    return KVQ_OK;
+}
+
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -70,9 +70,14 @@ struct Piece {
     size_t hrow;     // first storage row of the (sequence, live head)
 };
 
+// First row of a segment's tile stream: the visible-row start of a decode,
+// row 0 of a verify.
+__device__ __forceinline__ int seg_first(const DecodeArgs& a, int j) { return a.first[j]; }
+__device__ __forceinline__ int seg_first(const VerifyArgs&, int) { return 0; }
+
 // Calls f(piece) for each piece of share w, in stream order.
-template <class F>
-__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, F&& f) {
+template <class Args, class F>
+__device__ __forceinline__ void for_each_piece(const Args& a, int w, F&& f) {
     const int T = a.n_tiles, W = a.n_shares;
     int t = (int)((int64_t)w * T / W);
     const int t1 = (int)((int64_t)(w + 1) * T / W);
@@ -93,8 +98,8 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, int w, F&& f
         p.gl = gl;
         p.b = a.seq0 + j;
         p.g = a.live_head[gl];
-        p.row0 = a.first[j] + kTileRows * (t - sb);
-        p.row1 = min(a.first[j] + kTileRows * (pe - sb), a.len[j]);
+        p.row0 = seg_first(a, j) + kTileRows * (t - sb);
+        p.row1 = min(seg_first(a, j) + kTileRows * (pe - sb), a.len[j]);
         p.slot = w + j * a.n_live + gl;
         p.hrow = ((size_t)p.b * a.n_live + gl) * a.capacity;
         f(p);
@@ -293,6 +298,7 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
 // in the combine ([P1] attend: acc (.) vcol at the end).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr float kLazy = 8.0f;
 
 // V layout of the q8 kernel: lane (ri = lane / 16, seg = lane % 16) owns
@@ -648,28 +654,15 @@ constexpr int kCombineThreads = 512;
 constexpr int kCombineGroups = kCombineThreads / 32;
 constexpr int kCombineBatch = 8;
 
-template <bool kQ8>
-__global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a) {
+// Folds the nch partials at ml / acc (strides mstride / astride floats)
+// with a sink logit zs in log2 units (-inf: none) and leaves, for tid < 32,
+// the normalised channels 4 tid .. 4 tid + 3 in *res.  Block-wide: every
+// thread of the block calls it.
+__device__ __forceinline__ bool combine_partials(const float* ml, const float* acc, size_t mstride, size_t astride,
+                                                 int nch, float zs, float4* res) {
     __shared__ float4 sm_acc[kCombineGroups][32];
     __shared__ float sm_m[kCombineGroups], sm_l[kCombineGroups];
-    const int h = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-    const int b = a.seq0 + j;
-    const int g = h / a.hpk, hh = h - g * a.hpk;
-    const int gl = a.live_slot[g];
-    float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD;
-    const int nt = a.ntile[j];
-    if (gl < 0 || nt == 0) {
-        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
-        return;
-    }
-    // slots of the segment: its first..last share + segment index
-    const int sb = a.tile_base[j] + gl * nt;
-    const int first = tile_owner(sb, a.n_tiles, a.n_shares);
-    const int nch = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - first + 1;
-    const size_t it0 = (size_t)first + (size_t)j * a.n_live + gl;
-    const float* ml = a.ws_ml + (it0 * a.hpk + hh) * 2;          // stride hpk*2 per slot
-    const float* acc = a.ws_acc + (it0 * a.hpk + hh) * kHD;      // stride hpk*128 per slot
-    const size_t mstride = (size_t)a.hpk * 2, astride = (size_t)a.hpk * kHD;
+    const int tid = threadIdx.x;
     const int sg = tid >> 5, lane = tid & 31;
     const int ngroups = (int)(blockDim.x >> 5);
 
@@ -712,32 +705,229 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
         sm_l[sg] = L;
     }
     __syncthreads();
-    if (tid < 32) {
-        // a learned sink joins the max and the denominator ([P2] attend_group_upto)
-        const float zs = a.sinks ? (float)((double)a.sinks[h] * 1.4426950408889634) : -INFINITY;
-        float Mt = fmaxf(sm_m[0], zs);
-        for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
-        float Lt = a.sinks ? fast_exp2(zs - Mt) : 0.0f;
-        float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k = 0; k < ngroups; ++k) {
-            const float e = fast_exp2(sm_m[k] - Mt);    // 0 for sub-groups without rows
-            Lt = fmaf(e, sm_l[k], Lt);
-            At.x = fmaf(e, sm_acc[k][tid].x, At.x);
-            At.y = fmaf(e, sm_acc[k][tid].y, At.y);
-            At.z = fmaf(e, sm_acc[k][tid].z, At.z);
-            At.w = fmaf(e, sm_acc[k][tid].w, At.w);
-        }
-        const float inv = 1.0f / Lt;
-        float4 rr = make_float4(At.x * inv, At.y * inv, At.z * inv, At.w * inv);
-        if (kQ8 && a.frozen[j]) {
-            const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + 4 * tid);
-            rr.x *= vc.x;
-            rr.y *= vc.y;
-            rr.z *= vc.z;
-            rr.w *= vc.w;
-        }
-        *(float4*)(o + 4 * tid) = rr;
+    if (tid >= 32) return false;
+    // a learned sink joins the max and the denominator ([P2] attend_group_upto)
+    float Mt = fmaxf(sm_m[0], zs);
+    for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
+    float Lt = zs == -INFINITY ? 0.0f : fast_exp2(zs - Mt);
+    float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < ngroups; ++k) {
+        const float e = sm_m[k] == -INFINITY ? 0.0f : fast_exp2(sm_m[k] - Mt);   // sub-groups without rows
+        Lt = fmaf(e, sm_l[k], Lt);
+        At.x = fmaf(e, sm_acc[k][tid].x, At.x);
+        At.y = fmaf(e, sm_acc[k][tid].y, At.y);
+        At.z = fmaf(e, sm_acc[k][tid].z, At.z);
+        At.w = fmaf(e, sm_acc[k][tid].w, At.w);
     }
+    const float inv = 1.0f / Lt;
+    *res = make_float4(At.x * inv, At.y * inv, At.z * inv, At.w * inv);
+    return true;
+}
+
+template <bool kQ8>
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a) {
+    const int h = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int b = a.seq0 + j;
+    const int g = h / a.hpk, hh = h - g * a.hpk;
+    const int gl = a.live_slot[g];
+    float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD;
+    const int nt = a.ntile[j];
+    if (gl < 0 || nt == 0) {
+        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    // slots of the segment: its first..last share + segment index
+    const int sb = a.tile_base[j] + gl * nt;
+    const int first = tile_owner(sb, a.n_tiles, a.n_shares);
+    const int nch = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - first + 1;
+    const size_t it0 = (size_t)first + (size_t)j * a.n_live + gl;
+    const float zs = a.sinks ? (float)((double)a.sinks[h] * 1.4426950408889634) : -INFINITY;
+    float4 rr;
+    if (!combine_partials(a.ws_ml + (it0 * a.hpk + hh) * 2, a.ws_acc + (it0 * a.hpk + hh) * kHD,
+                          (size_t)a.hpk * 2, (size_t)a.hpk * kHD, nch, zs, &rr))
+        return;
+    if (kQ8 && a.frozen[j]) {
+        const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + 4 * tid);
+        rr.x *= vc.x;
+        rr.y *= vc.y;
+        rr.z *= vc.z;
+        rr.w *= vc.w;
+    }
+    *(float4*)(o + 4 * tid) = rr;
+}
+
+// ---------------------------------------------------------------------------
+// K-token R-SWA verify ([P3] verify_attention): every draft query attends
+// the reference rows, the ring as it would stand after the drafts up to its
+// own were written, and those drafts; nothing is written.  Up to 16 queries
+// per KV head (n_draft x hpk) share each K and V row read, which makes the
+// score and value passes dense contractions on the matrix cores
+// (v_mfma_f32_16x16x4f32, f32 in and out):
+//   scores  S^T[16 rows x 16 queries] = K[16 x 128] Q^T: A = K (lane l: row
+//           l % 16, channels 16 u + 4 (l / 16) + e, u < 8, e < 4, so the four
+//           lanes of a row read 64 contiguous bytes per load), B = Q^T (lane
+//           l: query l % 16, the same channels), 32 steps; lane l receives the
+//           scores of query l % 16 for rows 4 (l / 16) + r, r < 4;
+//   values  (P V)^T[channels x queries] = V^T P^T per 16-channel block cb:
+//           step s takes row 4 (l / 16) + s from each lane, so the B operand
+//           is the lane's own weight p[s] and the A operand is V[row][c] with
+//           c = 4 (l % 16) + (cb & 3) + 64 (cb >> 2) (16 lanes read 256
+//           contiguous bytes); lane l accumulates query l % 16's channels
+//           16 (l / 16) + 4 r + (cb & 3) + 64 (cb >> 2) -- one query per lane,
+//           so the online-softmax rescale is per lane.
+// Visibility of row p to draft query i (the ring after i + 1 more writes):
+// reference rows always; a ring slot unless it is among the e_i = max(0,
+// ring_len + i + 1 - 128) oldest live slots; draft row d iff d <= i.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
+    const int w = share_index();
+    if (w >= a.n_shares) return;
+    const int lane = threadIdx.x & 63;
+    const int qi = lane & 15, kb = lane >> 4;
+    for_each_piece(a, w, [&](const Piece& it) {
+        const int j = it.j;
+        const int L = a.prefill[j] + a.ring_len[j];                  // cache rows; drafts follow
+        const float* K = a.k + it.hrow * kHD;
+        const float* V = a.v + it.hrow * kHD;
+        const size_t dstride = (size_t)a.n_kv_heads * kHD;
+        const float* KD = a.kd + ((size_t)it.b * a.n_draft * a.n_kv_heads + it.g) * kHD;
+        const float* VD = a.vd + ((size_t)it.b * a.n_draft * a.n_kv_heads + it.g) * kHD;
+        auto row_ptr = [&](const float* C, const float* D, int p) {
+            return p < L ? C + (size_t)p * kHD : D + (size_t)(p - L) * dstride;
+        };
+        // this lane's query (MFMA column): draft di, head hh of the group
+        const bool qvalid = qi < a.nq;
+        const int di = qvalid ? qi / a.hpk : 0, hh = qvalid ? qi - di * a.hpk : 0;
+        float qb[32];
+        {
+            const float* qp = a.q + (((size_t)it.b * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 4 * kb;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float4 x = qvalid ? *(const float4*)(qp + 16 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+                qb[4 * t + 0] = x.x * kQScale;
+                qb[4 * t + 1] = x.y * kQScale;
+                qb[4 * t + 2] = x.z * kQScale;
+                qb[4 * t + 3] = x.w * kQScale;
+            }
+        }
+        const int pre = a.prefill[j], rl = a.ring_len[j], old = a.ring_oldest[j];
+        const int evict = max(0, rl + di + 1 - KVQ_RING_WINDOW);
+        auto visible = [&](int p) {
+            if (p < pre) return true;
+            if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
+            return p - L <= di;
+        };
+
+        struct Tile {
+            float4 kt[8];      // K row r0 + qi, channels 16 u + 4 kb ..
+            float4 vt[4][2];   // V rows r0 + 4 kb + s, channels 4 qi .. and 64 + 4 qi ..
+        };
+        auto load_tile = [&](int r0, Tile& t) {
+            const float* kr = row_ptr(K, KD, min(r0 + qi, it.row1 - 1)) + 4 * kb;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t.kt[u] = ld_stream(kr + 16 * u);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const float* vr = row_ptr(V, VD, min(r0 + 4 * kb + s2, it.row1 - 1)) + 4 * qi;
+                t.vt[s2][0] = ld_stream(vr);
+                t.vt[s2][1] = ld_stream(vr + 64);
+            }
+        };
+        float m = -INFINITY, l = 0.0f;
+        v4f acc[8];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+        auto compute_tile = [&](int r0, const Tile& t) {
+            v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(t.kt[u].x, qb[4 * u + 0], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(t.kt[u].y, qb[4 * u + 1], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(t.kt[u].z, qb[4 * u + 2], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x4f32(t.kt[u].w, qb[4 * u + 3], c, 0, 0, 0);
+            }
+            float sc[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = r0 + 4 * kb + r;
+                sc[r] = (qvalid && p < it.row1 && visible(p)) ? c[r] : -INFINITY;
+                tmax = fmaxf(tmax, sc[r]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mnew = fmaxf(m, tmax);
+            const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(m - mnew);
+            float pw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pw[r] = sc[r] == -INFINITY ? 0.0f : fast_exp2(sc[r] - mnew);
+            l = l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+            m = mnew;
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const float vv[8] = {t.vt[s2][0].x, t.vt[s2][0].y, t.vt[s2][0].z, t.vt[s2][0].w,
+                                     t.vt[s2][1].x, t.vt[s2][1].y, t.vt[s2][1].z, t.vt[s2][1].w};
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[cb], pw[s2], acc[cb], 0, 0, 0);
+            }
+        };
+        int r0 = it.row0;
+        Tile ta, tb;
+        load_tile(r0, ta);
+        while (true) {
+            load_tile(r0 + kTileRows, tb);
+            compute_tile(r0, ta);
+            r0 += kTileRows;
+            if (r0 >= it.row1) break;
+            load_tile(r0 + kTileRows, ta);
+            compute_tile(r0, tb);
+            r0 += kTileRows;
+            if (r0 >= it.row1) break;
+        }
+        // the piece's partial for each valid query
+        float lt = l + __shfl_xor(l, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (qvalid) {
+            const size_t ix = (size_t)it.slot * a.nq + qi;
+            if (kb == 0) {
+                a.ws_ml[ix * 2] = m;
+                a.ws_ml[ix * 2 + 1] = lt;
+            }
+            float* dst = a.ws_acc + ix * kHD + 16 * kb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *(float4*)(dst + 4 * r) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+                *(float4*)(dst + 64 + 4 * r) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+            }
+        }
+    });
+}
+
+// Combine of the verify: block (draft i x Q head h, sequence).
+__global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const VerifyArgs a) {
+    const int x = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int i = x / a.n_q_heads, h = x - i * a.n_q_heads;
+    const int b = a.seq0 + j;
+    const int g = h / a.hpk, hh = h - g * a.hpk;
+    const int gl = a.live_slot[g];
+    float* o = a.out + (((size_t)b * a.n_draft + i) * a.n_q_heads + h) * kHD;
+    const int nt = a.ntile[j];
+    if (gl < 0 || nt == 0) {
+        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
+        return;
+    }
+    const int sb = a.tile_base[j] + gl * nt;
+    const int first = tile_owner(sb, a.n_tiles, a.n_shares);
+    const int nch = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - first + 1;
+    const size_t it0 = (size_t)first + (size_t)j * a.n_live + gl;
+    const int vq = i * a.hpk + hh;
+    float4 rr;
+    if (combine_partials(a.ws_ml + (it0 * a.nq + vq) * 2, a.ws_acc + (it0 * a.nq + vq) * kHD, (size_t)a.nq * 2,
+                         (size_t)a.nq * kHD, nch, -INFINITY, &rr))
+        *(float4*)(o + 4 * tid) = rr;
 }
 
 // Threads per combine block: enough 32-lane sub-groups that each folds at
@@ -763,7 +953,7 @@ int combine_threads(const DecodeArgs& a) {
 // device and kernel.  0 on a runtime error.
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
-    static int cache[kMaxDevices][16];
+    static int cache[kMaxDevices][17];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     int& c = cache[dev][which];
@@ -824,6 +1014,32 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<false>(a, s); }
+
+hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
+    VerifyArgs a = args;
+    a.n_shares = 1;
+    if (a.n_tiles > 0) {                          // zero only when every group is dead
+        const int wv = resident_waves(reinterpret_cast<const void*>(k_verify_f32), 16);
+        if (wv == 0) return hipErrorInvalidDevice;
+        // one share per resident wave: up to 16 queries per row make the waves
+        // compute-heavy, unlike the single-query f32 decode
+        a.n_shares = wv < a.n_tiles ? wv : a.n_tiles;
+        const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
+        hipLaunchKernelGGL(k_verify_f32, grid, block, 0, s, a);
+    }
+    int nmax = 1;
+    for (int j = 0; j < a.n_seq; ++j)
+        for (int gl = 0; gl < a.n_live; ++gl) {
+            const int sb = a.tile_base[j] + gl * a.ntile[j];
+            const int cnt = tile_owner(sb + a.ntile[j] - 1, a.n_tiles, a.n_shares) -
+                            tile_owner(sb, a.n_tiles, a.n_shares) + 1;
+            nmax = cnt > nmax ? cnt : nmax;
+        }
+    int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
+    groups = groups < 1 ? 1 : (groups > kCombineGroups ? kCombineGroups : groups);
+    hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads, a.n_seq), dim3(32 * groups), 0, s, a);
+    return hipGetLastError();
+}
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<true>(a, s); }
 
 }  // namespace kvq

@@ -135,7 +135,42 @@ struct DecodeArgs {
 // Partial slots a launch can use: n_shares + n_seq * n_live.
 inline size_t max_slots(int n_seq, int n_live) { return (size_t)kMaxWaves + (size_t)n_seq * n_live; }
 
+// K-token R-SWA verify ([P3] verify_attention): per sequence, the segment
+// of a live head is its cache rows [0, prefill + ring_len) followed by the
+// n_draft draft rows, read from kd/vd.
+struct VerifyArgs {
+    const float* q;            // [batch][n_draft][n_q_heads][128]
+    float* out;                // [batch][n_draft][n_q_heads][128]
+    const float* k;            // f32 storage
+    const float* v;
+    const float* kd;           // draft K/V [batch][n_draft][n_kv_heads][128]
+    const float* vd;
+    float* ws_acc;             // [slots][nq][128]
+    float* ws_ml;              // [slots][nq][2]
+    int n_kv_heads;
+    int n_live;
+    int n_q_heads;
+    int hpk;
+    int capacity;
+    int n_seq;
+    int seq0;
+    int n_tiles;
+    int n_shares;
+    int n_draft;
+    int nq;                    // n_draft * hpk queries per KV head (<= 16)
+    int8_t live_head[KVQ_MAX_KV_HEADS];
+    int8_t live_slot[KVQ_MAX_KV_HEADS];
+    int32_t tile_base[kSeqPerLaunch + 1];
+    int32_t ntile[kSeqPerLaunch];
+    int32_t len[kSeqPerLaunch];              // prefill + ring_len + n_draft
+    int32_t prefill[kSeqPerLaunch];
+    int32_t ring_len[kSeqPerLaunch];
+    int32_t ring_oldest[kSeqPerLaunch];      // slot of the oldest live ring token
+};
+constexpr int kVerifyMaxQ = 16;
+
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -80,6 +80,8 @@ _SIGNATURES = [
     ("kv_truncate_last", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int]),
     ("kv_trim_window", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int64, _P, _P]),
+    ("rswa_verify", ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("kvq_verify_workspace_bytes", ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int]),
     ("kvq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -318,3 +320,18 @@ def kv_trim_window(cache: KvCache, seq: int, base: int, w: int, slack: int, alig
     _check(lib().kv_trim_window(cache.ref, seq, ctypes.byref(b), w, slack, align, anchor, ctypes.byref(d),
                                 _stream(stream)))
     return b.value, d.value
+
+
+def kvq_verify_workspace_bytes(cache: KvCache, n_q_heads: int, n_draft: int) -> int:
+    return lib().kvq_verify_workspace_bytes(cache.ref, n_q_heads, n_draft)
+
+
+def rswa_verify(cache: KvCache, rings: Rings, n_q_heads: int, n_draft: int, q, k_draft, v_draft, out,
+                ws=None, ws_bytes=None, stream=None) -> None:
+    if ws is None:
+        import torch
+        need = kvq_verify_workspace_bytes(cache, n_q_heads, n_draft)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().rswa_verify(cache.ref, rings.ref, n_q_heads, n_draft, _ptr(q), _ptr(k_draft), _ptr(v_draft),
+                             _ptr(out), _ptr(ws), nb, _stream(stream)))

@@ -163,6 +163,34 @@ def test_decode_option_refusals():
     expect(call("decode_attn_f32_ex", c.ref, 32, FAKE, FAKE, None, FAKE, 1 << 40, None), K.ESTATE, c, before)
 
 
+def test_verify_refusals():
+    """rswa_verify refuses before any launch: bad counts, too many queries
+    per KV head, a small workspace, an unrecorded prefill, a q8 cache."""
+    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=400)
+    rings = K.Rings(2)
+    c.len[:] = [5, 5]
+    need = K.kvq_verify_workspace_bytes(c, 10, 4)
+    assert need > 0 and K.kvq_verify_workspace_bytes(c, 10, 17) == 0 and K.kvq_verify_workspace_bytes(c, 20, 9) == 0
+    before = snapshot(c, rings)
+    expect(call("rswa_verify", c.ref, rings.ref, 10, 4, FAKE, FAKE, FAKE, FAKE, FAKE, need, None), K.ESTATE,
+           c, before, rings)                                            # prefill not recorded
+    K.rswa_record_prefill(c, rings, 0)
+    K.rswa_record_prefill(c, rings, 1)
+    before = snapshot(c, rings)
+    for n_q, n_d, ws in ((10, 0, need), (10, 17, 1 << 40), (20, 9, 1 << 40), (15, 1, 1 << 40), (10, 4, need - 1)):
+        expect(call("rswa_verify", c.ref, rings.ref, n_q, n_d, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None), K.EINVAL,
+               c, before, rings)
+    expect(call("rswa_verify", c.ref, rings.ref, 10, 4, None, FAKE, FAKE, FAKE, FAKE, need, None), K.EINVAL,
+           c, before, rings)
+    c.len[1] = 6                                                        # appended since the record
+    before = snapshot(c, rings)
+    expect(call("rswa_verify", c.ref, rings.ref, 10, 4, FAKE, FAKE, FAKE, FAKE, FAKE, need, None), K.ESTATE,
+           c, before, rings)
+    q = fake_cache(K.KIND_Q8)
+    bq = snapshot(q)
+    expect(call("rswa_verify", q.ref, rings.ref, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE, q, bq)
+
+
 def test_truncate_last_moves_the_cursor_only():
     """[P1]/[P2] truncate_last: drop the last min(n_drop, len) rows."""
     c = fake_cache(K.KIND_Q8, batch=3)
