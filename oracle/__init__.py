@@ -74,6 +74,10 @@ def _load():
         L.orc_attend_f32_ex.restype = None
         L.orc_attend_q8_ex.argtypes = [i, i, i, P, P, P, P, P, P, P, i, d, P, P]
         L.orc_attend_q8_ex.restype = None
+        L.orc_quant_row_i8.argtypes = [P, i, P]
+        L.orc_quant_row_i8.restype = ctypes.c_float
+        L.orc_attend_i8.argtypes = [i, i, i, P, P, P, P, P, P]
+        L.orc_attend_i8.restype = None
         L.orc_weights_f32.argtypes = [i, i, P, P, P]
         L.orc_weights_f32.restype = None
         _lib = L
@@ -170,6 +174,43 @@ class Q8Head:
         return self.vq[:n].astype(np.float64) * self.vs[:n, None].astype(np.float64) * col
 
 
+def quant_row_i8(x):
+    """[P3] quantize_row_i8 of one f32 row -> (codes int8 [hd], scale f32)."""
+    x = _f32(x)
+    q = np.zeros(x.shape[0], np.int8)
+    sc = _load().orc_quant_row_i8(_p(x), x.shape[0], _p(q))
+    return q, np.float32(sc)
+
+
+class I8Head:
+    """Per-row int8 storage of ONE live KV head ([P3] Int8Kv: codes and one
+    f32 scale per row, for K and for V)."""
+
+    def __init__(self, cap: int, hd: int = 128):
+        self.cap, self.hd, self.n = cap, hd, 0
+        self.kq = np.zeros((cap, hd), np.int8)
+        self.ks = np.zeros(cap, np.float32)
+        self.vq = np.zeros((cap, hd), np.int8)
+        self.vs = np.zeros(cap, np.float32)
+
+    def append(self, k_rows, v_rows) -> None:
+        k_rows, v_rows = _f32(k_rows), _f32(v_rows)
+        n_new = k_rows.shape[0]
+        if self.n + n_new > self.cap:
+            raise ValueError("oracle i8 append: capacity exceeded")
+        for r in range(n_new):
+            p = self.n + r
+            self.kq[p], self.ks[p] = quant_row_i8(k_rows[r])
+            self.vq[p], self.vs[p] = quant_row_i8(v_rows[r])
+        self.n += n_new
+
+    def dequant_k(self) -> np.ndarray:
+        return self.kq[: self.n].astype(np.float64) * self.ks[: self.n, None].astype(np.float64)
+
+    def dequant_v(self) -> np.ndarray:
+        return self.vq[: self.n].astype(np.float64) * self.vs[: self.n, None].astype(np.float64)
+
+
 # --------------------------------------------------------------------------
 # Attention by definition (float64)
 # --------------------------------------------------------------------------
@@ -213,6 +254,19 @@ def attend_q8(q, head: Q8Head, first: int = 0, softcap: float = 0.0, sinks=None)
     return out[0] if squeeze else out
 
 
+def attend_i8(q, head: I8Head) -> np.ndarray:
+    """[P3] decode_attention_int8 for one KV head: q [hpk][hd] quantised per
+    head, exact integer dots scaled by qscale * kscale / sqrt(hd), softmax,
+    V dequantised per row; float64."""
+    q = _f32(q)
+    squeeze = q.ndim == 1
+    q2 = q.reshape(1, -1) if squeeze else q
+    hpk, hd = q2.shape
+    out = np.zeros((hpk, hd), np.float64)
+    _load().orc_attend_i8(head.n, hd, hpk, _p(q2), _p(head.kq), _p(head.ks), _p(head.vq), _p(head.vs), _p(out))
+    return out[0] if squeeze else out
+
+
 def weights_f32(q, k) -> np.ndarray:
     q, k = _f32(q), _f32(k)
     hd = q.shape[0]
@@ -228,7 +282,7 @@ def decode(q, units, n_kv_heads: int, threads: int = 1, only=None, first=None, s
 
     q      [B][Hq][hd] f32
     units  units[b][g] -> None (dead group or nothing stored) or
-           ("f32", k [n][hd], v [n][hd]) or ("q8", Q8Head)
+           ("f32", k [n][hd], v [n][hd]) or ("q8", Q8Head) or ("i8", I8Head)
     Returns out [B][Hq][hd] float64; Q heads h of group g = h // (Hq/Hkv)
     ([P1] attend_group), zeros for dead/empty groups.
     only   optional iterable of (b, g) pairs to compute (others left 0).
@@ -252,6 +306,8 @@ def decode(q, units, n_kv_heads: int, threads: int = 1, only=None, first=None, s
         z = None if sinks is None else np.asarray(sinks, np.float32)[g * hpk:(g + 1) * hpk]
         if u[0] == "f32":
             out[b, g * hpk:(g + 1) * hpk] = attend_f32(qg, u[1], u[2], f, softcap, z)
+        elif u[0] == "i8":
+            out[b, g * hpk:(g + 1) * hpk] = attend_i8(qg, u[1])
         else:
             out[b, g * hpk:(g + 1) * hpk] = attend_q8(qg, u[1], f, softcap, z)
 

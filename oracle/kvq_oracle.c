@@ -305,6 +305,65 @@ void orc_attend_q8(int n, int hd, int hpk, const float* q,
     orc_attend_q8_ex(n, hd, hpk, q, kq, ks, kcol, vq, vs, vcol, 0, 0.0, NULL, out);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Per-row int8 route: [P3] quantize_row_i8 and decode_attention_int8.       */
+/*                                                                            */
+/* quantize_row_i8: maxabs = max |x| over the row (f32); scale = maxabs / 127 */
+/* (correctly rounded division), or 1 for an all-zero row; code = clamp(      */
+/* round_ties_even(x / scale), -127, 127).  Returns the scale.                */
+/* ------------------------------------------------------------------------ */
+float orc_quant_row_i8(const float* x, int hd, int8_t* q)
+{
+    float maxabs = 0.0f;
+    for (int d = 0; d < hd; ++d) {
+        float a = fabsf(x[d]);
+        if (a > maxabs) maxabs = a;
+    }
+    float scale = maxabs > 0.0f ? maxabs / 127.0f : 1.0f;
+    for (int d = 0; d < hd; ++d) {
+        float r = rintf(x[d] / scale);          /* default rounding mode: ties to even */
+        if (r < -127.0f) r = -127.0f;
+        if (r > 127.0f) r = 127.0f;
+        q[d] = (int8_t)r;
+    }
+    return scale;
+}
+
+/* decode_attention_int8 for one KV head: every query head is quantised with
+ * quantize_row_i8; its score against row p is the exact integer dot of the
+ * codes times qscale * kscale[p] / sqrt(hd); weights by the softmax; the
+ * output sums weight * vscale[p] * vcode[p][d] (all in double).
+ *   kq[n][hd], ks[n], vq[n][hd], vs[n];  q[hpk][hd];  out[hpk][hd]           */
+void orc_attend_i8(int n, int hd, int hpk, const float* q,
+                   const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
+                   double* out)
+{
+    for (int i = 0; i < hpk * hd; ++i) out[i] = 0.0;
+    if (n <= 0) return;
+    int8_t* qc = (int8_t*)malloc((size_t)hd);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double scale = 1.0 / sqrt((double)hd);
+    for (int h = 0; h < hpk; ++h) {
+        float qs = orc_quant_row_i8(q + (size_t)h * hd, hd, qc);
+        double* oh = out + (size_t)h * hd;
+        for (int p = 0; p < n; ++p) {
+            long dot = 0;
+            for (int d = 0; d < hd; ++d) dot += (long)qc[d] * (long)kq[(size_t)p * hd + d];
+            s[p] = (double)dot * (double)qs * (double)ks[p] * scale;
+        }
+        double m = s[0];
+        for (int p = 1; p < n; ++p) if (s[p] > m) m = s[p];
+        double z = 0.0;
+        for (int p = 0; p < n; ++p) { s[p] = exp(s[p] - m); z += s[p]; }
+        for (int p = 0; p < n; ++p) {
+            double w = s[p] / z * (double)vs[p];
+            for (int d = 0; d < hd; ++d) oh[d] += w * (double)vq[(size_t)p * hd + d];
+        }
+    }
+    free(s);
+    free(qc);
+}
+
 /* Attention weights alone (for the sum-to-one invariant): w[n] for one query
  * head over f32 rows. */
 void orc_weights_f32(int n, int hd, const float* q, const float* k, double* w)

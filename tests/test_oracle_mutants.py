@@ -39,6 +39,13 @@ MUTANTS = {
     "sink_scaled": ("z += exp((double)sinks[h] - m);", "z += exp((double)sinks[h] * scale - m);"),
     "sink_capped": ("z += exp((double)sinks[h] - m);",
                     "z += exp((softcap > 0.0 ? softcap * tanh((double)sinks[h] / softcap) : (double)sinks[h]) - m);"),
+    "i8_half_away": ("float r = rintf(x[d] / scale);", "float r = roundf(x[d] / scale);"),
+    "i8_reciprocal": ("float r = rintf(x[d] / scale);", "float r = rintf(x[d] * (1.0f / scale));"),
+    "i8_zero_row_scale": ("float scale = maxabs > 0.0f ? maxabs / 127.0f : 1.0f;",
+                          "float scale = maxabs > 0.0f ? maxabs / 127.0f : 1e-12f;"),
+    "i8_drops_vscale": ("double w = s[p] / z * (double)vs[p];", "double w = s[p] / z;"),
+    "i8_drops_qscale": ("s[p] = (double)dot * (double)qs * (double)ks[p] * scale;",
+                        "s[p] = (double)dot * (double)ks[p] * scale;"),
     "softcap_missing_factor": ("s[p] = softcap * tanh(s[p] / softcap);", "s[p] = tanh(s[p] / softcap);"),
     "softcap_before_scale": ("s[p] = dot * scale;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);",
                              "s[p] = dot;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);\n"

@@ -857,6 +857,69 @@ def test_verify_equals_sequential_ring_steps(prefill, n_hist, K):
     assert np.array_equal(got2[:-1], got[:-1]) and not np.array_equal(got2[-1], got[-1])
 
 
+# ---------------------------------------------------------------------------
+# Per-row int8 route ([P3] quantize_row_i8, decode_attention_int8)
+# ---------------------------------------------------------------------------
+def test_int8_row_fixtures_from_page(golden_dir):
+    """[P3] tests: ties to even ([127, .5, 1.5, ...] -> [127, 0, 2, 2, 4, 0,
+    -2, -2, -4], scale 1) and division, not the reciprocal (-124, where
+    the reciprocal route gives -125)."""
+    fx = json.load(open(os.path.join(golden_dir, "int8_row_fixtures.json")))
+    row = np.zeros(HD, np.float32)
+    row[:9] = fx["ties_to_even"]["row_prefix"]
+    q, sc = oracle.quant_row_i8(row)
+    assert q[:9].tolist() == fx["ties_to_even"]["codes_prefix"] and not q[9:].any()
+    assert struct.pack("<f", sc).hex() == struct.pack("<I", int(fx["ties_to_even"]["scale_bits"], 16)).hex()
+    row = np.zeros(HD, np.float32)
+    row[:2] = [bits_f32(h) for h in fx["divides"]["row_prefix_bits"]]
+    q, sc = oracle.quant_row_i8(row)
+    assert q[:2].tolist() == fx["divides"]["codes_prefix"]
+    recip = half_away(float(np.float32(row[1] * np.float32(np.float32(1.0) / sc))))
+    assert recip == fx["divides"]["reciprocal_route_code_1"]
+
+
+def test_int8_row_against_exact_rationals():
+    """scale = f32(maxabs / 127) and code = round_ties_even(f32(x / scale))
+    recomputed with exact rationals over rows of magnitudes 2^-20 .. 2^20
+    (the page's scalar-contract test spans the same range); an all-zero row
+    has scale 1 and codes 0."""
+    r = rng(5000)
+    for case in range(60):
+        mag = 2.0 ** ((case % 41) - 20)
+        x = ((r.random(HD) * 2 - 1) * mag).astype(np.float32)
+        if case == 0:
+            x[:] = 0
+        q, sc = oracle.quant_row_i8(x)
+        amax = max(abs(Fraction(float(v))) for v in x)
+        want_sc = f32_round(amax / 127) if amax > 0 else 1.0
+        assert float(sc) == want_sc
+        for d in range(HD):
+            t = f32_round(Fraction(float(x[d])) / Fraction(want_sc))
+            want = max(-127, min(127, round(t)))          # Python rounds ties to even
+            assert q[d] == want, (case, d)
+
+
+def test_int8_attention_matches_sdpa_on_dequantised_rows():
+    """decode_attention_int8 is attention of the dequantised query q^ =
+    code * qscale over K^ = code * kscale, V^ = code * vscale (torch SDPA,
+    float64)."""
+    r = rng(5100)
+    h = oracle.I8Head(cap=90)
+    h.append((r.standard_normal((90, HD)) * 3).astype(np.float32),
+             (r.standard_normal((90, HD)) * 3).astype(np.float32))
+    q = (r.standard_normal((4, HD)) * 2).astype(np.float32)
+    got = oracle.attend_i8(q, h)
+    qh = np.stack([oracle.quant_row_i8(q[i])[0].astype(np.float64) * float(oracle.quant_row_i8(q[i])[1])
+                   for i in range(4)])
+    tq = torch.from_numpy(qh)[None, :, None, :]
+    tk = torch.from_numpy(h.dequant_k())[None, None].expand(1, 4, 90, HD).contiguous()
+    tv = torch.from_numpy(h.dequant_v())[None, None].expand(1, 4, 90, HD).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[0, :, 0, :].numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    # the integer dot stays far inside i32: 127 * 127 * 128
+    assert 127 * 127 * HD == 2_064_512 < 2 ** 31
+
+
 def test_workload_generators_are_deterministic():
     s = workloads.get("batched_q8")
     L = s.lengths()
