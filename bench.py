@@ -70,6 +70,13 @@ def algorithmic_bytes_q8(lens, n_live, hq):
     return rows * 276 + len(lens) * n_live * 2 * 128 * 4 + len(lens) * hq * 128 * 4 * 2
 
 
+def algorithmic_bytes_i8(lens, n_live, hq):
+    # int8 K and V codes (2 x 128 B) and their two f32 row scales per row
+    # and live head, queries read, outputs written
+    rows = int(np.sum(lens)) * n_live
+    return rows * 264 + len(lens) * hq * 128 * 4 * 2
+
+
 def algorithmic_bytes_rswa(n_rows, heads):
     # K and V rows read once, q read, out written, the step's K/V read and written once
     return n_rows * heads * 1024 + heads * 512 * 2 + heads * 512 * 2 * 2
@@ -154,16 +161,21 @@ def main():
     if do_q8:
         from concurrent.futures import ThreadPoolExecutor
         cq = K.KvCache(K.KIND_Q8, bq.batch, bq.n_kv_heads, int(lens.max()) + total_steps + 64)
+        # the same rows also go through the per-row int8 codec ([P3])
+        ci8 = K.KvCache(K.KIND_I8, bq.batch, bq.n_kv_heads, int(lens.max()))
         with ThreadPoolExecutor(16) as ex:
             for b, (k, v) in enumerate(ex.map(bq.kv_rows, range(bq.batch))):
-                K.kv_append_q8(cq, b, int(lens[b]), t(k), t(v))
+                kd, vd = t(k), t(v)
+                K.kv_append_q8(cq, b, int(lens[b]), kd, vd)
+                K.kv_append_i8(ci8, b, int(lens[b]), kd, vd)
         qq = t(bq.query())
         qout = torch.zeros((bq.batch, bq.n_q_heads, 128), device=dev)
         newk = t(workloads.normal_f32(workloads.key(bq.seed, 99), (bq.batch, bq.n_kv_heads, 128)))
         newv = t(workloads.normal_f32(workloads.key(bq.seed, 98), (bq.batch, bq.n_kv_heads, 128)))
         ws_q8 = cq.workspace(bq.n_q_heads)
         torch.cuda.synchronize()
-        log("q8 cache ready: %d rows, %.2f GB stored" % (int(lens.sum()), cq.cache_bytes() / 1e9))
+        log("q8 cache ready: %d rows, %.2f GB stored (i8: %.2f GB)" % (
+            int(lens.sum()), cq.cache_bytes() / 1e9, ci8.cache_bytes() / 1e9))
 
     def step(i):
         if do_rswa:
@@ -254,6 +266,20 @@ def main():
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
             "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
             "kv_positions_per_s": round(int(cq.len.sum()) / us * 1e6, 1)}
+
+        # [P3] decode_attention_int8 over the same contexts (per-row int8 K
+        # and V, query quantised per head)
+        ws_i8 = ci8.workspace(bq.n_q_heads)
+
+        def i8_call(i):
+            K.decode_attn_i8(ci8, bq.n_q_heads, qq, qout, ws_i8)
+        us = time_calls(i8_call, 50)
+        nb = algorithmic_bytes_i8(ci8.len, ci8.n_live, bq.n_q_heads)
+        parts["decode_attn_i8"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "kv_positions_per_s": round(int(ci8.len.sum()) / us * 1e6, 1)}
+        del ci8, ws_i8
 
         # [P2] attend_group_upto options: soft-cap 30 and per-Q-head sinks over
         # the full context, then also an 8192-row sliding window

@@ -58,14 +58,16 @@ extern "C" {
 
 #define KVQ_KIND_F32  1
 #define KVQ_KIND_Q8   2
+#define KVQ_KIND_I8   3   /* per-row int8 ([P3] Int8Kv) */
 
 /* Device buffers of a cache, for kvq_buffer_bytes(). */
 #define KVQ_BUF_K     0   /* f32:  float [batch][n_live][capacity][128]            */
 #define KVQ_BUF_V     1   /* f32:  float [batch][n_live][capacity][128]            */
 #define KVQ_BUF_KQ    2   /* q8:   int8  [batch][n_live][capacity][128] (16 B rows) */
-#define KVQ_BUF_KS    3   /* q8:   float [batch][n_live][capacity][4]  (one 16 B record per row) */
+#define KVQ_BUF_KS    3   /* q8:   float [batch][n_live][capacity][4]  (one 16 B record per row);
+                             i8:   float [batch][n_live][capacity]                 */
 #define KVQ_BUF_VQ    4   /* q8:   int8  [batch][n_live][capacity][128]            */
-#define KVQ_BUF_VS    5   /* q8:   float [batch][n_live][capacity]                 */
+#define KVQ_BUF_VS    5   /* q8, i8: float [batch][n_live][capacity]              */
 #define KVQ_BUF_KCOL  6   /* q8:   float [batch][n_live][128]                      */
 #define KVQ_BUF_VCOL  7   /* q8:   float [batch][n_live][128]                      */
 
@@ -87,6 +89,9 @@ extern "C" {
  * freeze and the per-channel RMS afterwards.  A stored value is
  *   K^[p][d] = kq[p][d] * ks[p][d/32] * kcol[d],
  *   V^[p][d] = vq[p][d] * vs[p] * vcol[d].
+ * i8 kind ([P3] Int8Kv, the per-row int8 route): K and V rows as int8 codes
+ * with one f32 scale per row each (kq, ks, vq, vs; KVQ_BUF_KQ/VQ as for q8),
+ *   K^[p][d] = kq[p][d] * ks[p],  V^[p][d] = vq[p][d] * vs[p].
  *
  * Fill it with kvq_cache_init(), then set the device pointers of the kind's
  * buffers (sizes from kvq_buffer_bytes(); every base must be 16-byte
@@ -94,7 +99,7 @@ extern "C" {
  * entries that the library keeps up to date.
  */
 typedef struct kvq_cache {
-    int32_t kind;            /* KVQ_KIND_F32 or KVQ_KIND_Q8 */
+    int32_t kind;            /* KVQ_KIND_F32, KVQ_KIND_Q8 or KVQ_KIND_I8 */
     int32_t batch;           /* sequences */
     int32_t n_kv_heads;      /* KV heads, dead ones included */
     int32_t head_dim;        /* 128 */
@@ -257,6 +262,28 @@ int decode_attn_f32(const kvq_cache* c, int n_q_heads, const float* q, float* ou
  * errors as decode_attn_f32 (KVQ_ESTATE for a non-q8 cache).
  */
 int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kv_append_i8 -- kv_append_f32 for an i8 cache: each row of each live head
+ * is quantised as [P3] quantize_row_i8, separately for K and V:
+ *   scale = max|x| / 127 (correctly rounded f32 division), or 1 for an
+ *   all-zero row;  code = clamp(round_ties_even(x / scale), -127, 127)
+ * with x / scale correctly rounded.  Same arguments and errors as
+ * kv_append_f32 (KVQ_ESTATE for a cache of another kind).
+ */
+int kv_append_i8(kvq_cache* c, int seq, int n_rows, const float* k_new, const float* v_new, void* stream);
+
+/*
+ * decode_attn_i8 -- [P3] decode_attention_int8 over an i8 cache: each Q
+ * head is quantised with quantize_row_i8 (codes and qscale, in f32); its
+ * score against row p is (1/sqrt(128)) * qscale * ks[p] * <qcodes, kq[p]>
+ * with the integer dot exact (|dot| <= 127 * 127 * 128); the softmax and the
+ * value pass (weight * vs[p] * vq[p]) as decode_attn_f32.  Arguments,
+ * layout, workspace and errors as decode_attn_f32 (KVQ_ESTATE for a cache
+ * of another kind).
+ */
+int decode_attn_i8(const kvq_cache* c, int n_q_heads, const float* q, float* out,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*

@@ -62,6 +62,10 @@ int check_cache(const kvq_cache* c, int kind, const char* fn) {
         if (!aligned16(c->kq) || !aligned16(c->ks) || !aligned16(c->vq) || !aligned16(c->vs) ||
             !aligned16(c->kcol) || !aligned16(c->vcol))
             return fail(KVQ_EINVAL, "%s: q8 buffers not 16-byte aligned", fn);
+    } else if (c->kind == KVQ_KIND_I8) {
+        if (!c->kq || !c->ks || !c->vq || !c->vs) return fail(KVQ_EINVAL, "%s: i8 cache with a missing buffer", fn);
+        if (!aligned16(c->kq) || !aligned16(c->ks) || !aligned16(c->vq) || !aligned16(c->vs))
+            return fail(KVQ_EINVAL, "%s: i8 buffers not 16-byte aligned", fn);
     } else {
         return fail(KVQ_EINVAL, "%s: unknown cache kind %d", fn, c->kind);
     }
@@ -107,10 +111,15 @@ AppendArgs base_append(const kvq_cache* c, const float* k_new, const float* v_ne
     return a;
 }
 
-// Launch equal-length segments (same n) in batches of kSeqPerLaunch.
+// Launch equal-length segments (same n) in batches of kSeqPerLaunch, with
+// the append kernel of the cache's own kind (the caller has checked it, so
+// every buffer that kernel writes is present).
 int launch_segments(const kvq_cache* c, const float* k_new, const float* v_new,
-                    const std::vector<Seg>& segs, bool q8, hipStream_t s, const char* fn) {
+                    const std::vector<Seg>& segs, hipStream_t s, const char* fn) {
     if (c->n_live == 0) return KVQ_OK;
+    const int kind = c->kind;
+    if (kind != KVQ_KIND_F32 && kind != KVQ_KIND_Q8 && kind != KVQ_KIND_I8)
+        return fail(KVQ_EINVAL, "%s: unknown cache kind %d", fn, kind);
     size_t i = 0;
     while (i < segs.size()) {
         AppendArgs a = base_append(c, k_new, v_new);
@@ -126,7 +135,10 @@ int launch_segments(const kvq_cache* c, const float* k_new, const float* v_new,
         }
         a.n_seq = ns;
         if (n == 0) continue;
-        const int rc = device_status(q8 ? launch_append_q8(a, n, s) : launch_append_f32(a, n, s), fn);
+        const int rc = device_status(kind == KVQ_KIND_Q8   ? launch_append_q8(a, n, s)
+                                     : kind == KVQ_KIND_I8 ? launch_append_i8(a, n, s)
+                                                           : launch_append_f32(a, n, s),
+                                     fn);
         if (rc) return rc;
     }
     return KVQ_OK;
@@ -269,7 +281,9 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
         }
         a.tile_base[ns] = (int32_t)tiles;
         a.n_tiles = (int)tiles;
-        const hipError_t e = (c->kind == KVQ_KIND_Q8) ? launch_decode_q8(a, s) : launch_decode_f32(a, s);
+        const hipError_t e = c->kind == KVQ_KIND_Q8   ? launch_decode_q8(a, s)
+                             : c->kind == KVQ_KIND_I8 ? launch_decode_i8(a, s)
+                                                      : launch_decode_f32(a, s);
         const int rc = device_status(e, fn);
         if (rc) return rc;
     }
@@ -284,7 +298,8 @@ int kvq_cache_init(kvq_cache* c, int kind, int batch, int n_kv_heads, int head_d
                    const uint8_t* alive, int32_t* len_host, uint8_t* frozen_host) {
     const char* fn = "kvq_cache_init";
     if (!c) return fail(KVQ_EINVAL, "%s: null cache", fn);
-    if (kind != KVQ_KIND_F32 && kind != KVQ_KIND_Q8) return fail(KVQ_EINVAL, "%s: unknown kind %d", fn, kind);
+    if (kind != KVQ_KIND_F32 && kind != KVQ_KIND_Q8 && kind != KVQ_KIND_I8)
+        return fail(KVQ_EINVAL, "%s: unknown kind %d", fn, kind);
     if (head_dim != KVQ_HEAD_DIM) return fail(KVQ_EINVAL, "%s: head_dim %d != 128", fn, head_dim);
     if (batch < 1 || capacity < 1 || capacity > KVQ_MAX_CAPACITY)
         return fail(KVQ_EINVAL, "%s: batch must be >= 1 and capacity within 1..%d", fn, KVQ_MAX_CAPACITY);
@@ -315,14 +330,14 @@ size_t kvq_buffer_bytes(const kvq_cache* c, int which) {
     if (!c || c->head_dim != KVQ_HEAD_DIM || c->batch < 1 || c->capacity < 1) return 0;
     const size_t rows = (size_t)c->batch * c->n_live * c->capacity;
     const size_t heads = (size_t)c->batch * c->n_live;
-    const bool f32 = c->kind == KVQ_KIND_F32, q8 = c->kind == KVQ_KIND_Q8;
+    const bool f32 = c->kind == KVQ_KIND_F32, q8 = c->kind == KVQ_KIND_Q8, i8 = c->kind == KVQ_KIND_I8;
     switch (which) {
         case KVQ_BUF_K:
         case KVQ_BUF_V: return f32 ? rows * kHD * sizeof(float) : 0;
         case KVQ_BUF_KQ:
-        case KVQ_BUF_VQ: return q8 ? rows * kHD : 0;
-        case KVQ_BUF_KS: return q8 ? rows * kKScales * sizeof(float) : 0;
-        case KVQ_BUF_VS: return q8 ? rows * sizeof(float) : 0;
+        case KVQ_BUF_VQ: return (q8 || i8) ? rows * kHD : 0;
+        case KVQ_BUF_KS: return q8 ? rows * kKScales * sizeof(float) : i8 ? rows * sizeof(float) : 0;
+        case KVQ_BUF_VS: return (q8 || i8) ? rows * sizeof(float) : 0;
         case KVQ_BUF_KCOL:
         case KVQ_BUF_VCOL: return q8 ? heads * kHD * sizeof(float) : 0;
         default: return 0;
@@ -336,6 +351,8 @@ size_t kvq_cache_bytes(const kvq_cache* c) {
         const size_t rows = (size_t)c->len[b] * c->n_live;
         if (c->kind == KVQ_KIND_F32) {
             bytes += rows * 2 * kHD * sizeof(float);
+        } else if (c->kind == KVQ_KIND_I8) {
+            bytes += rows * 2 * (kHD + sizeof(float));
         } else {
             bytes += rows * (kHD + kKScales * sizeof(float) + kHD + sizeof(float));
             if (c->frozen[b]) bytes += (size_t)c->n_live * 2 * kHD * sizeof(float);
@@ -356,7 +373,23 @@ int kv_append_f32(kvq_cache* c, int seq, int n_rows, const float* k_new, const f
     } else if (n_rows > 0) {
         segs.push_back({seq, 0, c->len[seq], n_rows, false});
     }
-    if ((rc = launch_segments(c, k_new, v_new, segs, false, (hipStream_t)stream, fn))) return rc;
+    if ((rc = launch_segments(c, k_new, v_new, segs, (hipStream_t)stream, fn))) return rc;
+    for (const Seg& sg : segs) c->len[sg.seq] += sg.n;
+    return KVQ_OK;
+}
+
+int kv_append_i8(kvq_cache* c, int seq, int n_rows, const float* k_new, const float* v_new, void* stream) {
+    const char* fn = "kv_append_i8";
+    int rc = check_cache(c, KVQ_KIND_I8, fn);
+    if (rc) return rc;
+    if ((rc = check_append_args(c, seq, n_rows, k_new, v_new, fn))) return rc;
+    std::vector<Seg> segs;
+    if (seq == KVQ_ALL_SEQS) {
+        for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, c->len[b], 1, false});
+    } else if (n_rows > 0) {
+        segs.push_back({seq, 0, c->len[seq], n_rows, false});
+    }
+    if ((rc = launch_segments(c, k_new, v_new, segs, (hipStream_t)stream, fn))) return rc;
     for (const Seg& sg : segs) c->len[sg.seq] += sg.n;
     return KVQ_OK;
 }
@@ -377,7 +410,7 @@ int kv_append_q8(kvq_cache* c, int seq, int n_rows, const float* k_new, const fl
         for (auto& f : fl) c->frozen[f.first] = 1;
         std::vector<Seg> segs;
         for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, c->len[b], 1, c->frozen[b] != 0});
-        if ((rc = launch_segments(c, k_new, v_new, segs, true, s, fn))) return rc;
+        if ((rc = launch_segments(c, k_new, v_new, segs, s, fn))) return rc;
         for (int b = 0; b < c->batch; ++b) c->len[b] += 1;
         return KVQ_OK;
     }
@@ -385,7 +418,7 @@ int kv_append_q8(kvq_cache* c, int seq, int n_rows, const float* k_new, const fl
     const int L = c->len[seq];
     if (c->frozen[seq] || L + n_rows <= KVQ_COL_WARMUP) {
         std::vector<Seg> one{{seq, 0, L, n_rows, c->frozen[seq] != 0}};
-        if ((rc = launch_segments(c, k_new, v_new, one, true, s, fn))) return rc;
+        if ((rc = launch_segments(c, k_new, v_new, one, s, fn))) return rc;
         c->len[seq] = L + n_rows;
         return KVQ_OK;
     }
@@ -394,14 +427,14 @@ int kv_append_q8(kvq_cache* c, int seq, int n_rows, const float* k_new, const fl
     const int n1 = std::max(0, KVQ_COL_WARMUP - L);
     if (n1 > 0) {
         std::vector<Seg> first{{seq, 0, L, n1, false}};
-        if ((rc = launch_segments(c, k_new, v_new, first, true, s, fn))) return rc;
+        if ((rc = launch_segments(c, k_new, v_new, first, s, fn))) return rc;
         c->len[seq] = L + n1;
     }
     std::vector<std::pair<int, int>> fl{{seq, c->len[seq]}};
     if ((rc = launch_freeze_list(c, fl, s, fn))) return rc;
     c->frozen[seq] = 1;
     std::vector<Seg> rest{{seq, n1, c->len[seq], n_rows - n1, true}};
-    if ((rc = launch_segments(c, k_new, v_new, rest, true, s, fn))) return rc;
+    if ((rc = launch_segments(c, k_new, v_new, rest, s, fn))) return rc;
     c->len[seq] = L + n_rows;
     return KVQ_OK;
 }
@@ -442,6 +475,17 @@ int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out
                    size_t ws_bytes, void* stream) {
     const char* fn = "decode_attn_q8";
     int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    int hpk = 0;
+    if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, nullptr,
+                      (hipStream_t)stream, fn);
+}
+
+int decode_attn_i8(const kvq_cache* c, int n_q_heads, const float* q, float* out, void* ws, size_t ws_bytes,
+                   void* stream) {
+    const char* fn = "decode_attn_i8";
+    int rc = check_cache(c, KVQ_KIND_I8, fn);
     if (rc) return rc;
     int hpk = 0;
     if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
@@ -583,7 +627,7 @@ int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int a
     m.vs = c->vs;
     m.n_live = c->n_live;
     m.capacity = c->capacity;
-    m.q8 = c->kind == KVQ_KIND_Q8;
+    m.kind = c->kind;
     m.seq = seq;
     m.d = d;
     m.keep = (int)(n - d);

@@ -78,6 +78,28 @@ __global__ __launch_bounds__(128) void k_append_q8(const AppendArgs a) {
     }
 }
 
+// Per-row int8 append ([P3] quantize_row_i8).  block 128: wave 0 quantises
+// the K row, wave 1 the V row; lane holds 2 channels.  scale = max|x| / 127
+// (1 for a zero row), code = clamp(round_ties_even(x / scale), -127, 127).
+__global__ __launch_bounds__(128) void k_append_i8(const AppendArgs a) {
+    const int r = blockIdx.x, j = blockIdx.y, gl = blockIdx.z;
+    const int g = a.live_head[gl];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool is_k = (wave == 0);
+    const size_t src = ((size_t)(a.src_row0[j] + r) * a.n_kv_heads + g) * kHD + 2 * lane;
+    const size_t hrow = ((size_t)a.seq[j] * a.n_live + gl) * a.capacity + a.dst_row0[j] + r;
+    const float2 x = *(const float2*)((is_k ? a.k_new : a.v_new) + src);
+    const float am = group_max<64>(fmaxf(fabsf(x.x), fabsf(x.y)));
+    const float s = am > 0.0f ? __fdiv_rn(am, 127.0f) : 1.0f;
+    const float c0 = fminf(fmaxf(rintf(__fdiv_rn(x.x, s)), -127.0f), 127.0f);
+    const float c1 = fminf(fmaxf(rintf(__fdiv_rn(x.y, s)), -127.0f), 127.0f);
+    char2 c;
+    c.x = (int8_t)(int)c0;
+    c.y = (int8_t)(int)c1;
+    *(char2*)((is_k ? a.kq : a.vq) + hrow * kHD + 2 * lane) = c;
+    if (lane == 0) (is_k ? a.ks : a.vs)[hrow] = s;
+}
+
 // Freeze + requantise ([P1] freeze_cols) for one (sequence, live head).
 // block 128: thread d owns channel d.  The RMS sum runs over the rows in
 // order, multiply then add, exactly as the page's loop does per channel.
@@ -139,7 +161,8 @@ __global__ __launch_bounds__(128) void k_freeze(const FreezeArgs a) {
 // [dst, dst + m) with src - dst = d >= m, so a launch's source and
 // destination never overlap, and consecutive launches on the stream order a
 // chunk's reads before the next chunk's writes.  grid (blocks, live head,
-// buffer), block 256, a grid-stride loop of 16-byte (vs: 4-byte) copies.
+// buffer), block 256, a grid-stride loop of 16-byte copies (4-byte for the
+// one-per-row scales: vs, and ks of the per-row int8 kind).
 template <class T>
 __device__ __forceinline__ void copy_rows(T* base, int units_per_row, int src, int dst, int m) {
     const T* s = base + (size_t)src * units_per_row;
@@ -151,13 +174,16 @@ __device__ __forceinline__ void copy_rows(T* base, int units_per_row, int src, i
 
 __global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, int dst, int m) {
     const size_t row0 = ((size_t)a.seq * a.n_live + blockIdx.y) * a.capacity;
-    switch (a.q8 ? blockIdx.z : 4 + blockIdx.z) {
+    const int z = blockIdx.z;
+    const int which = a.kind == KVQ_KIND_F32 ? 4 + z : (a.kind == KVQ_KIND_I8 && z == 1) ? 6 : z;
+    switch (which) {
         case 0: copy_rows(reinterpret_cast<uint4*>(a.kq + row0 * kHD), kHD / 16, src, dst, m); break;
         case 1: copy_rows(reinterpret_cast<uint4*>(a.ks + row0 * kKScales), 1, src, dst, m); break;
         case 2: copy_rows(reinterpret_cast<uint4*>(a.vq + row0 * kHD), kHD / 16, src, dst, m); break;
         case 3: copy_rows(reinterpret_cast<uint32_t*>(a.vs + row0), 1, src, dst, m); break;
         case 4: copy_rows(reinterpret_cast<uint4*>(a.k + row0 * kHD), kHD / 4, src, dst, m); break;
-        default: copy_rows(reinterpret_cast<uint4*>(a.v + row0 * kHD), kHD / 4, src, dst, m); break;
+        case 5: copy_rows(reinterpret_cast<uint4*>(a.v + row0 * kHD), kHD / 4, src, dst, m); break;
+        default: copy_rows(reinterpret_cast<uint32_t*>(a.ks + row0), 1, src, dst, m); break;
     }
 }
 
@@ -166,10 +192,11 @@ __global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, i
 hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s) {
     for (int r = 0; r < a.keep; r += a.d) {
         const int m = min(a.d, a.keep - r);
-        const size_t units = (size_t)m * (a.q8 ? kHD / 16 : kHD / 4);     // largest buffer, 16-byte units
+        const bool f32 = a.kind == KVQ_KIND_F32;
+        const size_t units = (size_t)m * (f32 ? kHD / 4 : kHD / 16);     // largest buffer, 16-byte units
         const size_t want = (units + 1023) / 1024;
         const int blocks = (int)(want < 128 ? want : 128);
-        hipLaunchKernelGGL(k_move_chunk, dim3(blocks, a.n_live, a.q8 ? 4 : 2), dim3(256), 0, s, a, a.d + r, r, m);
+        hipLaunchKernelGGL(k_move_chunk, dim3(blocks, a.n_live, f32 ? 2 : 4), dim3(256), 0, s, a, a.d + r, r, m);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -183,6 +210,11 @@ hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s) {
 
 hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s) {
     hipLaunchKernelGGL(k_append_q8, dim3(n_rows, a.n_seq, a.n_live), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_i8(const AppendArgs& a, int n_rows, hipStream_t s) {
+    hipLaunchKernelGGL(k_append_i8, dim3(n_rows, a.n_seq, a.n_live), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

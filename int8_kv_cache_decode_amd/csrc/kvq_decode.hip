@@ -366,7 +366,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #ifndef KVQ_Q8_MIN_WAVES
 #define KVQ_Q8_MIN_WAVES 3
 #endif
-template <int HPK, bool kCap>
+template <int HPK, bool kCap, bool kI8>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
     __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
@@ -380,10 +380,10 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
     for_each_piece(a, w, [&](const Piece& it) {
         const int8_t* KQ = a.kq + it.hrow * kHD;
-        const float* KS = a.ks + it.hrow * kKScales;
+        const float* KS = a.ks + it.hrow * (kI8 ? 1 : kKScales);
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
-        const bool frz = a.frozen[it.j] != 0;
+        const bool frz = !kI8 && a.frozen[it.j] != 0;
         const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
         // The piece's 16-row tiles, kTiles per step; the loads of the next step
@@ -402,7 +402,10 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             const uint32_t rk = (uint32_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + (rk * kHD + 64 * sp + 16 * (lane >> 4)));
-            t.ks4 = ld_stream(KS + rk * kKScales);
+            if constexpr (kI8)
+                t.ks4.x = ld_stream1(KS + rk);
+            else
+                t.ks4 = ld_stream(KS + rk * kKScales);
             t.vsn = ld_stream1(VS + rk);
 #pragma unroll
             for (int i = 0; i < kVLoads; ++i) {
@@ -429,53 +432,98 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         const bool first_half = (lane >> 4) < 2;
         v4i qa_lo[NB][2], qa_hi[NB][2];                   // [head block][span]
         double gsc[NB][4];                                // for this lane's score head 4 hb + hq
+        if constexpr (!kI8) {
+    #pragma unroll
+            for (int hb = 0; hb < NB; ++hb) {
+                const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
 #pragma unroll
-        for (int hb = 0; hb < NB; ++hb) {
-            const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
+                for (int sp = 0; sp < 2; ++sp) {
+                    const int d0 = 64 * sp + 16 * kb;
+                    double qc[16];
+                    double gmax = 0.0;
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const int d0 = 64 * sp + 16 * kb;
-                double qc[16];
-                double gmax = 0.0;
+                    for (int t = 0; t < 16; ++t) qc[t] = 0.0;
+                    if (hm < HPK) {
+                        const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) qc[t] = 0.0;
-                if (hm < HPK) {
-                    const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
+                        for (int t4 = 0; t4 < 4; ++t4) {
+                            const float4 qv = *(const float4*)(qp + 4 * t4);
+                            float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
+                            if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
+                            qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
+                            qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
+                            qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
+                            qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
+                        }
+#pragma unroll
+                        for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
+                    }
+                    gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
+                    int e = 0;
+                    (void)frexp(gmax, &e);                         // gmax < 2^e
+                    const double up = ldexp(1.0, 27 - e);
+                    v4i pk = {0, 0, 0, 0};
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        int x = (int)rint(qc[t] * up);             // |x| <= 2^27
+                        const int d3 = take_digit(x);
+                        const int d2 = take_digit(x);
+                        const int d1 = take_digit(x);
+                        const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
+                        pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
+                    }
+                    const v4i zero = {0, 0, 0, 0};
+                    qa_lo[hb][sp] = first_half ? pk : zero;
+                    qa_hi[hb][sp] = first_half ? zero : pk;
+#pragma unroll
+                    for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
+                        const int es = __shfl(e, 4 * hq + 32 * gs, 64);
+                        gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
+                    }
+                }
+            }
+        } else {
+            // ---- query codes ([P3] quantize_row_i8 on each Q head, in f32) ----
+            // A rows m = 4 * head carry the head's codes over all 64 channels
+            // of a span (one K scale per row, so no group is zeroed); the rows
+            // of digits 1..3 are zero.  gsc[hb][0] = qscale * log2(e)/sqrt(128)
+            // of this lane's score head 4 hb + hq.
+#pragma unroll
+            for (int hb = 0; hb < NB; ++hb) {
+                const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
+                float xs[2][16];
+                float amax = 0.0f;
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
                     for (int t4 = 0; t4 < 4; ++t4) {
-                        const float4 qv = *(const float4*)(qp + 4 * t4);
-                        float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
-                        if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
-                        qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
-                        qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
-                        qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
-                        qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
+                        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (hm < HPK)
+                            qv = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD +
+                                                  64 * sp + 16 * kb + 4 * t4);
+                        xs[sp][4 * t4 + 0] = qv.x;
+                        xs[sp][4 * t4 + 1] = qv.y;
+                        xs[sp][4 * t4 + 2] = qv.z;
+                        xs[sp][4 * t4 + 3] = qv.w;
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(qv.x), fabsf(qv.y)), fmaxf(fabsf(qv.z), fabsf(qv.w))));
                     }
+                amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
 #pragma unroll
-                    for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
-                }
-                gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
-                int e = 0;
-                (void)frexp(gmax, &e);                         // gmax < 2^e
-                const double up = ldexp(1.0, 27 - e);
-                v4i pk = {0, 0, 0, 0};
+                for (int sp = 0; sp < 2; ++sp) {
+                    v4i pk = {0, 0, 0, 0};
+                    if (jm == 0 && hm < HPK) {
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    int x = (int)rint(qc[t] * up);             // |x| <= 2^27
-                    const int d3 = take_digit(x);
-                    const int d2 = take_digit(x);
-                    const int d1 = take_digit(x);
-                    const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
-                    pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
+                        for (int t = 0; t < 16; ++t) {
+                            const int c = (int)fminf(fmaxf(rintf(__fdiv_rn(xs[sp][t], qs)), -127.0f), 127.0f);
+                            pk[t >> 2] |= (c & 0xff) << (8 * (t & 3));
+                        }
+                    }
+                    qa_lo[hb][sp] = pk;
+                    qa_hi[hb][sp] = pk;
                 }
-                const v4i zero = {0, 0, 0, 0};
-                qa_lo[hb][sp] = first_half ? pk : zero;
-                qa_hi[hb][sp] = first_half ? zero : pk;
-#pragma unroll
-                for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
-                    const int es = __shfl(e, 4 * hq + 32 * gs, 64);
-                    gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
-                }
+                gsc[hb][0] = (double)__shfl(qs, 4 * hq, 64) * kQScale64;
             }
         }
 
@@ -533,19 +581,30 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             for (int hb = 0; hb < NB; ++hb) {
                 const v4i zero = {0, 0, 0, 0};
                 double sc = 0.0;
-                const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
+                if constexpr (kI8) {
+                    // exact integer dot of the codes over both spans
+                    v4i dsum = zero;
 #pragma unroll
-                for (int sp = 0; sp < 2; ++sp) {
-                    const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+                    for (int sp = 0; sp < 2; ++sp) {
+                        const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+                        dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa_lo[hb][sp], kbv, dsum, 0, 0, 0);
+                    }
+                    sc = (double)dsum[0] * (gsc[hb][0] * (double)t.ks4.x);
+                } else {
+                    const float ksg[4] = {t.ks4.x, t.ks4.y, t.ks4.z, t.ks4.w};
 #pragma unroll
-                    for (int gs = 0; gs < 2; ++gs) {
-                        const int g = 2 * sp + gs;
-                        const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(gs ? qa_hi[hb][sp] : qa_lo[hb][sp],
-                                                                             kbv, zero, 0, 0, 0);
-                        const int t1 = dsum[0] * 128 + dsum[1];
-                        const int t2 = dsum[2] * 128 + dsum[3];
-                        const double x = fma((double)t1, 16384.0, (double)t2);
-                        sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+                    for (int sp = 0; sp < 2; ++sp) {
+                        const v4i kbv = {(int)t.kb2[sp].x, (int)t.kb2[sp].y, (int)t.kb2[sp].z, (int)t.kb2[sp].w};
+#pragma unroll
+                        for (int gs = 0; gs < 2; ++gs) {
+                            const int g = 2 * sp + gs;
+                            const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(gs ? qa_hi[hb][sp] : qa_lo[hb][sp],
+                                                                                 kbv, zero, 0, 0, 0);
+                            const int t1 = dsum[0] * 128 + dsum[1];
+                            const int t2 = dsum[2] * 128 + dsum[3];
+                            const double x = fma((double)t1, 16384.0, (double)t2);
+                            sc = fma(x, (double)ksg[g] * gsc[hb][g], sc);
+                        }
                     }
                 }
                 const int h = 4 * hb + hq;
@@ -953,7 +1012,7 @@ int combine_threads(const DecodeArgs& a) {
 // device and kernel.  0 on a runtime error.
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
-    static int cache[kMaxDevices][17];
+    static int cache[kMaxDevices][25];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     int& c = cache[dev][which];
@@ -969,10 +1028,14 @@ int resident_waves(const void* kernel, int which) {
 
 int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
 
+// Cache kinds of the decode launcher.
+constexpr int kF32 = 0, kQ8k = 1, kI8k = 2;
+
 // The kernel instance for a group size, cache kind and soft-cap switch.
-template <int HPK, bool kQ8>
+template <int HPK, int kKind>
 const void* decode_kernel(bool cap) {
-    if (kQ8) return cap ? (const void*)k_decode_q8<HPK, true> : (const void*)k_decode_q8<HPK, false>;
+    if (kKind == kI8k) return (const void*)k_decode_q8<HPK, false, true>;
+    if (kKind == kQ8k) return cap ? (const void*)k_decode_q8<HPK, true, false> : (const void*)k_decode_q8<HPK, false, false>;
     return cap ? (const void*)k_decode_f32<HPK, true> : (const void*)k_decode_f32<HPK, false>;
 }
 
@@ -984,21 +1047,22 @@ const void* decode_kernel(bool cap) {
 // 5.0 us).
 constexpr int kF32WavesPerShare = 4;
 
-template <bool kQ8>
+template <int kKind>
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
+    constexpr bool kQ8 = kKind != kF32;
     DecodeArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {
         const bool cap = a.softcap2 > 0.0;
         const void* fn = nullptr;
         switch (a.hpk) {
-            case 1: fn = decode_kernel<1, kQ8>(cap); break;
-            case 2: fn = decode_kernel<2, kQ8>(cap); break;
-            case 4: fn = decode_kernel<4, kQ8>(cap); break;
-            case 8: fn = decode_kernel<8, kQ8>(cap); break;
+            case 1: fn = decode_kernel<1, kKind>(cap); break;
+            case 2: fn = decode_kernel<2, kKind>(cap); break;
+            case 4: fn = decode_kernel<4, kKind>(cap); break;
+            case 8: fn = decode_kernel<8, kKind>(cap); break;
             default: return hipErrorInvalidValue;
         }
-        const int wv = resident_waves(fn, 8 * kQ8 + 4 * cap + hpk_index(a.hpk));
+        const int wv = resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk));
         if (wv == 0) return hipErrorInvalidDevice;
         const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
@@ -1007,19 +1071,21 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
         const hipError_t e = hipLaunchKernel(fn, grid, block, kargs, 0, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_combine<kQ8>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
+    // the i8 kind has no column field to apply
+    hipLaunchKernelGGL(k_combine<kKind == kQ8k>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<false>(a, s); }
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<kF32>(a, s); }
+hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kI8k>(a, s); }
 
 hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
     VerifyArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {                          // zero only when every group is dead
-        const int wv = resident_waves(reinterpret_cast<const void*>(k_verify_f32), 16);
+        const int wv = resident_waves(reinterpret_cast<const void*>(k_verify_f32), 24);
         if (wv == 0) return hipErrorInvalidDevice;
         // one share per resident wave: up to 16 queries per row make the waves
         // compute-heavy, unlike the single-query f32 decode
@@ -1040,6 +1106,6 @@ hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
     hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads, a.n_seq), dim3(32 * groups), 0, s, a);
     return hipGetLastError();
 }
-hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<true>(a, s); }
+hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kQ8k>(a, s); }
 
 }  // namespace kvq

@@ -79,7 +79,7 @@ struct MoveArgs {
     float* vs;
     int n_live;
     int capacity;
-    int q8;
+    int kind;       // KVQ_KIND_*: which buffers move
     int seq;
     int d;
     int keep;
@@ -88,6 +88,7 @@ struct MoveArgs {
 // grid (n_rows, n_seq, n_live)
 hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s);
 hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s);
+hipError_t launch_append_i8(const AppendArgs& a, int n_rows, hipStream_t s);
 // grid (n_live, n_seq)
 hipError_t launch_freeze(const FreezeArgs& a, hipStream_t s);
 // one launch per chunk of d rows
@@ -172,5 +173,6 @@ constexpr int kVerifyMaxQ = 16;
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace kvq

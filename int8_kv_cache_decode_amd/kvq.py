@@ -24,7 +24,7 @@ MAX_KV_HEADS = 64
 ALL_SEQS = -1
 
 OK, EINVAL, ECAPACITY, ESTATE, EDEVICE = 0, -1, -2, -3, -4
-KIND_F32, KIND_Q8 = 1, 2
+KIND_F32, KIND_Q8, KIND_I8 = 1, 2, 3
 BUF_K, BUF_V, BUF_KQ, BUF_KS, BUF_VQ, BUF_VS, BUF_KCOL, BUF_VCOL = range(8)
 
 _P = ctypes.c_void_p
@@ -68,6 +68,8 @@ _SIGNATURES = [
     ("kv_append_f32", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]),
     ("kv_append_q8", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]),
     ("kv_freeze_col_and_requant", ctypes.c_int, [_P, ctypes.c_int, _P]),
+    ("kv_append_i8", ctypes.c_int, [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]),
+    ("decode_attn_i8", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
     ("kvq_workspace_bytes", ctypes.c_size_t, [_P, ctypes.c_int]),
     ("decode_attn_f32", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
     ("decode_attn_q8", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -157,7 +159,8 @@ class KvCache:
         self._ws = None
         if allocate:
             import torch
-            names = ("k", "v") if kind == KIND_F32 else ("kq", "ks", "vq", "vs", "kcol", "vcol")
+            names = {KIND_F32: ("k", "v"), KIND_Q8: ("kq", "ks", "vq", "vs", "kcol", "vcol"),
+                     KIND_I8: ("kq", "ks", "vq", "vs")}[kind]
             ids = {"k": BUF_K, "v": BUF_V, "kq": BUF_KQ, "ks": BUF_KS, "vq": BUF_VQ, "vs": BUF_VS,
                    "kcol": BUF_KCOL, "vcol": BUF_VCOL}
             for n in names:
@@ -179,6 +182,8 @@ class KvCache:
             return t[: B * H * C * HEAD_DIM * 4].view(torch.float32).view(B, H, C, HEAD_DIM)
         if name in ("kq", "vq"):
             return t[: B * H * C * HEAD_DIM].view(torch.int8).view(B, H, C, HEAD_DIM)
+        if name == "ks" and self.kind == KIND_I8:
+            return t[: B * H * C * 4].view(torch.float32).view(B, H, C)
         if name == "ks":
             return t[: B * H * C * 16].view(torch.float32).view(B, H, C, 4)
         if name == "vs":
@@ -233,6 +238,16 @@ def kv_append_f32(cache: KvCache, seq: int, n_rows: int, k_new, v_new, stream=No
 
 def kv_append_q8(cache: KvCache, seq: int, n_rows: int, k_new, v_new, stream=None) -> None:
     _check(lib().kv_append_q8(cache.ref, seq, n_rows, _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def kv_append_i8(cache: KvCache, seq: int, n_rows: int, k_new, v_new, stream=None) -> None:
+    _check(lib().kv_append_i8(cache.ref, seq, n_rows, _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def decode_attn_i8(cache: KvCache, n_q_heads: int, q, out, ws=None, ws_bytes=None, stream=None) -> None:
+    ws = cache.workspace(n_q_heads) if ws is None else ws
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().decode_attn_i8(cache.ref, n_q_heads, _ptr(q), _ptr(out), _ptr(ws), nb, _stream(stream)))
 
 
 def kv_freeze_col_and_requant(cache: KvCache, seq: int, stream=None) -> None:

@@ -76,6 +76,8 @@ def _load():
         L.orc_attend_q8_ex.restype = None
         L.orc_quant_row_i8.argtypes = [P, i, P]
         L.orc_quant_row_i8.restype = ctypes.c_float
+        L.orc_quant_rows_i8.argtypes = [i, i, P, P, P]
+        L.orc_quant_rows_i8.restype = None
         L.orc_attend_i8.argtypes = [i, i, i, P, P, P, P, P, P]
         L.orc_attend_i8.restype = None
         L.orc_weights_f32.argtypes = [i, i, P, P, P]
@@ -198,10 +200,12 @@ class I8Head:
         n_new = k_rows.shape[0]
         if self.n + n_new > self.cap:
             raise ValueError("oracle i8 append: capacity exceeded")
-        for r in range(n_new):
-            p = self.n + r
-            self.kq[p], self.ks[p] = quant_row_i8(k_rows[r])
-            self.vq[p], self.vs[p] = quant_row_i8(v_rows[r])
+        n0 = self.n
+        for src, q, sc in ((k_rows, self.kq, self.ks), (v_rows, self.vq, self.vs)):
+            qq = np.zeros((n_new, self.hd), np.int8)
+            ss = np.zeros(n_new, np.float32)
+            _load().orc_quant_rows_i8(n_new, self.hd, _p(np.ascontiguousarray(src)), _p(qq), _p(ss))
+            q[n0:n0 + n_new], sc[n0:n0 + n_new] = qq, ss
         self.n += n_new
 
     def dequant_k(self) -> np.ndarray:

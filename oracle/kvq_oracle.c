@@ -329,6 +329,13 @@ float orc_quant_row_i8(const float* x, int hd, int8_t* q)
     return scale;
 }
 
+/* quantize_row_i8 over n rows x[n][hd] -> q[n][hd], s[n]. */
+void orc_quant_rows_i8(int n, int hd, const float* x, int8_t* q, float* s)
+{
+    for (int p = 0; p < n; ++p)
+        s[p] = orc_quant_row_i8(x + (size_t)p * hd, hd, q + (size_t)p * hd);
+}
+
 /* decode_attention_int8 for one KV head: every query head is quantised with
  * quantize_row_i8; its score against row p is the exact integer dot of the
  * codes times qscale * kscale[p] / sqrt(hd); weights by the softmax; the

@@ -33,7 +33,7 @@ def host(t: torch.Tensor) -> np.ndarray:
 def append_rows(cache: K.KvCache, seq: int, k: np.ndarray, v: np.ndarray, chunks=None):
     """Append rows [n][Hkv][128] through the ABI, optionally in chunks."""
     n = k.shape[0]
-    fn = K.kv_append_f32 if cache.kind == K.KIND_F32 else K.kv_append_q8
+    fn = {K.KIND_F32: K.kv_append_f32, K.KIND_Q8: K.kv_append_q8, K.KIND_I8: K.kv_append_i8}[cache.kind]
     bounds = [0] + list(chunks or []) + [n]
     for lo, hi in zip(bounds[:-1], bounds[1:]):
         if hi > lo:

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 def fake_cache(kind, batch=2, hkv=8, cap=256, alive=None):
     c = K.KvCache(kind, batch, hkv, cap, alive=alive, allocate=False)
-    names = ("k", "v") if kind == K.KIND_F32 else ("kq", "ks", "vq", "vs", "kcol", "vcol")
+    names = {K.KIND_F32: ("k", "v"), K.KIND_Q8: ("kq", "ks", "vq", "vs", "kcol", "vcol"),
+             K.KIND_I8: ("kq", "ks", "vq", "vs")}[kind]
     for i, n in enumerate(names):
         setattr(c.c, n, FAKE + 4096 * i)
     return c
@@ -68,7 +69,7 @@ def test_cache_init_validation():
     ln = np.zeros(2, np.int32)
     fr = np.zeros(2, np.uint8)
     L = K.lib()
-    assert L.kvq_cache_init(ctypes.byref(c), 3, 2, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
+    assert L.kvq_cache_init(ctypes.byref(c), 4, 2, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
     assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 8, 64, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
     assert L.kvq_cache_init(ctypes.byref(c), 1, 0, 8, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
     assert L.kvq_cache_init(ctypes.byref(c), 1, 2, 65, 128, 16, None, ln.ctypes.data, fr.ctypes.data) == K.EINVAL
@@ -336,6 +337,27 @@ def test_buffer_and_workspace_sizes():
     f = fake_cache(K.KIND_F32, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
     assert K.kvq_buffer_bytes(f, K.BUF_K) == rows * 512 and K.kvq_buffer_bytes(f, K.BUF_KQ) == 0
     assert K.kvq_workspace_bytes(c, 30) == 0 and K.kvq_workspace_bytes(c, 32) > 0
+
+
+def test_i8_kind_buffers_and_refusals():
+    """The per-row int8 kind: one scale per row for K and for V, no column
+    fields, 264 B per (row, head); calls of the other kinds refuse it."""
+    c = fake_cache(K.KIND_I8, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
+    rows = 3 * 6 * 1000
+    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == rows * 128 and K.kvq_buffer_bytes(c, K.BUF_VQ) == rows * 128
+    assert K.kvq_buffer_bytes(c, K.BUF_KS) == rows * 4 and K.kvq_buffer_bytes(c, K.BUF_VS) == rows * 4
+    assert K.kvq_buffer_bytes(c, K.BUF_KCOL) == 0 and K.kvq_buffer_bytes(c, K.BUF_K) == 0
+    c.len[:] = [2, 0, 0]
+    assert K.kvq_cache_bytes(c) == 2 * 6 * 264
+    before = snapshot(c)
+    expect(call("kv_append_q8", c.ref, 0, 1, FAKE, FAKE, None), K.ESTATE, c, before)
+    expect(call("decode_attn_q8", c.ref, 16, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE, c, before)
+    expect(call("kv_append_i8", c.ref, 0, 999, FAKE, FAKE, None), K.ECAPACITY, c, before)
+    expect(call("kv_append_i8", c.ref, 3, 1, FAKE, FAKE, None), K.EINVAL, c, before)
+    expect(call("decode_attn_i8", c.ref, 12, FAKE, FAKE, FAKE, 1 << 40, None), K.EINVAL, c, before)  # 12 % 8
+    f = fake_cache(K.KIND_F32)
+    bf = snapshot(f)
+    expect(call("decode_attn_i8", f.ref, 16, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE, f, bf)
 
 
 def test_memory_accounting_matches_pages():

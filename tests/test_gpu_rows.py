@@ -26,7 +26,8 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
-BUFS = {K.KIND_F32: ("k", "v"), K.KIND_Q8: ("kq", "ks", "vq", "vs")}
+BUFS = {K.KIND_F32: ("k", "v"), K.KIND_Q8: ("kq", "ks", "vq", "vs"), K.KIND_I8: ("kq", "ks", "vq", "vs")}
+DECODE = {K.KIND_F32: K.decode_attn_f32, K.KIND_Q8: K.decode_attn_q8, K.KIND_I8: K.decode_attn_i8}
 
 
 # (lens, w, slack, align, anchor): overlapping moves (keep > d), disjoint
@@ -39,7 +40,7 @@ TRIMS = [([3000, 2001], 1400, 150, 16, -1),
 
 
 @pytest.mark.parametrize("case", range(len(TRIMS)))
-@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
 def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
     lens, w, slack, align, anchor = TRIMS[case]
     say("case: trim kind", kind, "lens", lens, "w", w, "slack", slack, "align", align, "anchor", anchor)
@@ -71,6 +72,24 @@ def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
         for b, n in enumerate(lens):
             d = bases[b]
             assert np.array_equal(after[b, :, : n - d].view(np.uint8), before[nm][b, :, d:n].view(np.uint8)), (nm, b)
+    if kind == K.KIND_I8:
+        # per-row codes do not depend on the other rows: the trimmed cache
+        # decodes as a cache that only ever held rows [d, n)
+        out = torch.full((len(lens), hkv * hpk, 128), np.nan, device="cuda")
+        K.decode_attn_i8(c, hkv * hpk, dev(q), out)
+        torch.cuda.synchronize()
+        units = [[None] * hkv for _ in lens]
+        for b, n in enumerate(lens):
+            k, v = rows[b]
+            for g in range(hkv):
+                if alive[g]:
+                    h = oracle.I8Head(cap=n)
+                    h.append(k[bases[b]:, g], v[bases[b]:, g])
+                    units[b][g] = ("i8", h)
+        err = max_err(host(out), oracle.decode(q, units, hkv, threads=THREADS))
+        say("  i8 max err %.3g" % err)
+        assert err <= F32_TOL, err
+        return
     # the windowed decode (first = len - w) of the trimmed cache sees the rows
     # the untrimmed cache's window sees
     first = np.maximum(c.len.astype(np.int64) - w, 0).astype(np.int32)
@@ -96,7 +115,7 @@ def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
     assert err <= F32_TOL, err
 
 
-@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8])
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
 def test_truncate_then_append_equals_never_appended(kind):
     """[P2] truncate_last after a speculative append: the replacement rows
     land where the rejected ones were; storage and decode equal a cache that
@@ -125,7 +144,7 @@ def test_truncate_then_append_equals_never_appended(kind):
         assert np.array_equal(a[:, :, :n].view(np.uint8), b[:, :, :n].view(np.uint8)), nm
     q = dev(r.standard_normal((1, hkv * hpk, 128)).astype(np.float32))
     o1, o2 = (torch.full((1, hkv * hpk, 128), np.nan, device="cuda") for _ in range(2))
-    fn = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
+    fn = DECODE[kind]
     fn(test, hkv * hpk, q, o1)
     fn(ctrl, hkv * hpk, q, o2)
     torch.cuda.synchronize()
