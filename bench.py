@@ -77,6 +77,12 @@ def algorithmic_bytes_i8(lens, n_live, hq):
     return rows * 264 + len(lens) * hq * 128 * 4 * 2
 
 
+def algorithmic_bytes_rswa_i8(n_rows, heads):
+    # int8 K/V rows and their row scales read once (264 B per row and head),
+    # q read, out written, the step's f32 K/V read and its codes + scales written
+    return n_rows * heads * 264 + heads * 512 * 2 + heads * (512 * 2 + 264)
+
+
 def algorithmic_bytes_rswa(n_rows, heads):
     # K and V rows read once, q read, out written, the step's K/V read and written once
     return n_rows * heads * 1024 + heads * 512 * 2 + heads * 512 * 2 * 2
@@ -149,6 +155,19 @@ def main():
                 q, kk, vv = pool[s % 16]
                 K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
             rswa.append((c, rings, out))
+        # the same reference and steps on the int8 mirror ([P3] Int8Kv):
+        # 86.5 MB per replica, 6 replicas so the MALL cannot serve repeats
+        rswa_i8 = []
+        for rep in range(6):
+            c = K.KvCache(K.KIND_I8, 1, rs.n_heads, rs.prefill + rs.window)
+            rings = K.Rings(1)
+            K.kv_append_i8(c, 0, rs.prefill, rk_d, rv_d)
+            K.rswa_record_prefill(c, rings, 0)
+            out = torch.zeros((1, rs.n_heads, 128), device=dev)
+            for s_ in range(rs.writes - 1):
+                q, kk, vv = pool[s_ % 16]
+                K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+            rswa_i8.append((c, rings, out))
         del rk_d, rv_d
         torch.cuda.synchronize()
         log("rswa replicas ready: %d x %.1f MB, ring_len %d ring_pos %d" % (
@@ -233,6 +252,18 @@ def main():
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
             "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
             "kv_positions_per_s": round((rs.prefill + rs.window) / us * 1e6, 1)}
+
+        def rswa_i8_call(i):
+            c, rings, out = rswa_i8[i % len(rswa_i8)]
+            q, kk, vv = pool[i % 16]
+            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+        us = time_calls(rswa_i8_call, 100)
+        nb = algorithmic_bytes_rswa_i8(rs.prefill + rs.window, rs.n_heads)
+        parts["rswa_decode_i8"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "kv_positions_per_s": round((rs.prefill + rs.window) / us * 1e6, 1)}
+        del rswa_i8
 
         # [P3] verify_attention: 8 draft tokens checked against the same
         # replicas, nothing written; bytes as the decode (each row read once

@@ -324,9 +324,10 @@ int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* 
 /*
  * rswa_record_prefill -- [P3] RingCache::record_prefill for sequence `seq`
  * of an f32 cache whose reference block has just been appended with
- * kv_append_f32: prefill_len = len[seq], ring_len = ring_pos = writes = 0.
+ * kv_append_f32, or of an i8 cache (the page's int8 mirror) appended with
+ * kv_append_i8: prefill_len = len[seq], ring_len = ring_pos = writes = 0.
  * rings: host array [batch].  A prefill of 0 rows is allowed.
- * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not an f32 cache),
+ * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (a q8 cache),
  * KVQ_ECAPACITY (len[seq] + 128 > capacity: no room for the ring).
  */
 int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
@@ -359,8 +360,8 @@ size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft
 /*
  * rswa_checkpoint -- [P3] RingCache::checkpoint for sequence `seq`: copy its
  * cursors into *cp (host), taken before speculative decode steps.  O(1), no
- * device work.  Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not
- * an f32 cache).
+ * device work.  Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (a
+ * q8 cache).
  */
 int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring_checkpoint* cp);
 
@@ -374,8 +375,8 @@ int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring
  * another cache or sequence, another prefill or epoch, is from the future,
  * or when the discarded writes overwrote a slot that was live at the
  * checkpoint (cp->ring_len + discarded > 128).  No device work.
- * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (not an f32 cache,
- * or any refusal above).
+ * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (a q8 cache, or
+ * any refusal above).
  */
 int rswa_rollback_to(kvq_cache* c, kvq_ring* rings, int seq, const kvq_ring_checkpoint* cp);
 
@@ -411,8 +412,11 @@ int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int a
                    int* dropped, void* stream);
 
 /*
- * rswa_decode -- one R-SWA decode step for every sequence of an f32 cache:
- * [P3] attention() = write_decode_step() then decode_attention().
+ * rswa_decode -- one R-SWA decode step for every sequence of an f32 or i8
+ * cache: [P3] attention() = write_decode_step() then decode_attention().
+ * On an i8 cache (the page's int8 mirror) the step's K and V rows are
+ * quantised into the ring slot with quantize_row_i8 and the attention is
+ * decode_attention_int8 (query quantised per head, as decode_attn_i8).
  *
  * k_new, v_new  device float [batch][n_kv_heads][128]: this step's K/V
  * q             device float [batch][n_q_heads][128]
@@ -426,8 +430,8 @@ int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int a
  * the reference block and every live ring slot, itself included.  len[b]
  * becomes prefill_len + ring_len.  The reference rows are never written.
  * Errors: KVQ_EINVAL (null, bad group size, workspace too small),
- * KVQ_ESTATE (not an f32 cache, or a sequence whose prefill was not
- * recorded, or whose len no longer matches its ring cursors),
+ * KVQ_ESTATE (a q8 cache, or a sequence whose prefill was not recorded,
+ * or whose len no longer matches its ring cursors),
  * KVQ_ECAPACITY (prefill_len + 128 > capacity).
  */
 int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q,

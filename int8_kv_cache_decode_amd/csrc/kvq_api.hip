@@ -111,6 +111,16 @@ AppendArgs base_append(const kvq_cache* c, const float* k_new, const float* v_ne
     return a;
 }
 
+// R-SWA caches: f32, or the per-row int8 kind ([P3] keeps its int8 mirror
+// in the same reference + ring layout).
+int check_ring_cache(const kvq_cache* c, const char* fn) {
+    const int rc = check_cache(c, 0, fn);
+    if (rc) return rc;
+    if (c->kind != KVQ_KIND_F32 && c->kind != KVQ_KIND_I8)
+        return fail(KVQ_ESTATE, "%s: R-SWA needs an f32 or i8 cache (kind %d)", fn, c->kind);
+    return KVQ_OK;
+}
+
 // Launch equal-length segments (same n) in batches of kSeqPerLaunch, with
 // the append kernel of the cache's own kind (the caller has checked it, so
 // every buffer that kernel writes is present).
@@ -519,7 +529,7 @@ int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* 
 
 int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq) {
     const char* fn = "rswa_record_prefill";
-    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    int rc = check_ring_cache(c, fn);
     if (rc) return rc;
     if (!rings) return fail(KVQ_EINVAL, "%s: null rings", fn);
     if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
@@ -538,7 +548,7 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq) {
 
 int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring_checkpoint* cp) {
     const char* fn = "rswa_checkpoint";
-    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    int rc = check_ring_cache(c, fn);
     if (rc) return rc;
     if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
     if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
@@ -556,7 +566,7 @@ int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring
 
 int rswa_rollback_to(kvq_cache* c, kvq_ring* rings, int seq, const kvq_ring_checkpoint* cp) {
     const char* fn = "rswa_rollback_to";
-    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    int rc = check_ring_cache(c, fn);
     if (rc) return rc;
     if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
     if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
@@ -641,7 +651,7 @@ int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int a
 int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, const float* k_new,
                 const float* v_new, float* out, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "rswa_decode";
-    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    int rc = check_ring_cache(c, fn);
     if (rc) return rc;
     int hpk = 0;
     if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
@@ -674,9 +684,19 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
         wrows[b] = r.prefill_len + slot;
         lens[b] = r.prefill_len + r.ring_len;
     }
-    if ((rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new, nullptr,
-                         (hipStream_t)stream, fn)))
-        return rc;
+    if (c->kind == KVQ_KIND_I8) {
+        // [P3] write_decode_step quantises the step's row into the int8
+        // mirror's ring slot; the int8 decode then reads it like any row
+        std::vector<Seg> segs;
+        for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, wrows[b], 1, false});
+        if ((rc = launch_segments(c, k_new, v_new, segs, (hipStream_t)stream, fn))) return rc;
+        rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), nullptr, nullptr, nullptr, nullptr,
+                        (hipStream_t)stream, fn);
+    } else {
+        rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new, nullptr,
+                        (hipStream_t)stream, fn);
+    }
+    if (rc) return rc;
     for (int b = 0; b < c->batch; ++b) {
         rings[b] = next[b];
         c->len[b] = lens[b];

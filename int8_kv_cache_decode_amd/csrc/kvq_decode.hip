@@ -709,9 +709,15 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 // sub-group takes every ngroups-th partial, issuing the loads of up to 8 at
 // once and folding them with a running max; the sub-groups then merge in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kCombineThreads = 512;
+#ifndef KVQ_COMBINE_THREADS
+#define KVQ_COMBINE_THREADS 512
+#endif
+#ifndef KVQ_COMBINE_BATCH
+#define KVQ_COMBINE_BATCH 8
+#endif
+constexpr int kCombineThreads = KVQ_COMBINE_THREADS;
 constexpr int kCombineGroups = kCombineThreads / 32;
-constexpr int kCombineBatch = 8;
+constexpr int kCombineBatch = KVQ_COMBINE_BATCH;
 
 // Folds the nch partials at ml / acc (strides mstride / astride floats)
 // with a sink logit zs in log2 units (-inf: none) and leaves, for tid < 32,
@@ -1064,7 +1070,14 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
         }
         const int wv = resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk));
         if (wv == 0) return hipErrorInvalidDevice;
-        const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
+        int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
+#ifdef KVQ_Q8_MIN_TILES
+        if (kQ8) {
+            const int want = a.n_tiles / KVQ_Q8_MIN_TILES, lo = (wv + 3) / 4;
+            shares = want < wv ? want : wv;
+            shares = shares > lo ? shares : lo;
+        }
+#endif
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};

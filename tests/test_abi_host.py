@@ -291,8 +291,17 @@ def test_ring_rollback_refusals_leave_everything_unchanged():
     expect(call("rswa_checkpoint", q.ref, rings.ref, 0, ctypes.byref(cp)), K.ESTATE, q, bq)
 
 
-def test_rswa_refusals_leave_cache_and_rings_unchanged():
-    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=200)
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_rswa_refusals_leave_cache_and_rings_unchanged(kind):
+    """The same refusals on f32 caches and on the per-row int8 kind (the
+    page's int8 mirror shares the ring layout); q8 caches hold no ring."""
+    q = fake_cache(K.KIND_Q8, batch=2, hkv=10, cap=200)
+    qr = K.Rings(2)
+    bq = snapshot(q, qr)
+    expect(call("rswa_record_prefill", q.ref, qr.ref, 0), K.ESTATE, q, bq, qr)
+    expect(call("rswa_decode", q.ref, qr.ref, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None), K.ESTATE,
+           q, bq, qr)
+    c = fake_cache(kind, batch=2, hkv=10, cap=200)
     rings = K.Rings(2)
     ws = K.kvq_workspace_bytes(c, 10)
     before = snapshot(c, rings)

@@ -154,3 +154,62 @@ def test_i8_workload_batched():
     err = max_err(host(out), ref)
     say("  i8 batched max err %.3g" % err)
     assert err <= F32_TOL, err
+
+
+def rswa_i8_workload(name, check_steps):
+    """[P3] attention() on the int8 mirror: reference rows appended through
+    the int8 codec, then write_decode_step (the step's row quantised into
+    its ring slot) + decode_attention_int8 per step.  Outputs against the
+    oracle over the reference rows and the live ring in slot order; every
+    stored code and scale against the oracle's codec."""
+    spec = workloads.get(name)
+    W = spec.window
+    c = K.KvCache(K.KIND_I8, 1, spec.n_heads, spec.prefill + W)
+    rings = K.Rings(1)
+    rk, rv = spec.reference()
+    append_rows(c, 0, rk.transpose(1, 0, 2), rv.transpose(1, 0, 2))
+    K.rswa_record_prefill(c, rings, 0)
+    m = oracle.RingModel(W)
+    m.record_prefill(spec.prefill)
+    out = torch.full((1, spec.n_heads, 128), np.nan, device="cuda")
+    toks = {}
+
+    def heads(rows_of):
+        hs = []
+        for g in range(spec.n_heads):
+            kk, vv = rows_of(g)
+            h = oracle.I8Head(cap=kk.shape[0])
+            h.append(kk, vv)
+            hs.append(h)
+        return hs
+
+    for t in range(spec.writes):
+        q, kt, vt = spec.step(t)
+        toks[t] = (kt, vt)
+        K.rswa_decode(c, rings, spec.n_heads, dev(q[None]), dev(kt[None]), dev(vt[None]), out)
+        m.write(t)
+        if t in check_steps:
+            torch.cuda.synchronize()
+            win = m.window()
+            hs = heads(lambda g: (np.concatenate([rk[g], np.stack([toks[s][0][g] for s in win])]),
+                                  np.concatenate([rv[g], np.stack([toks[s][1][g] for s in win])])))
+            ref = oracle.decode(q[None], [[("i8", h) for h in hs]], spec.n_heads, threads=THREADS)
+            err = max_err(host(out), ref)
+            say("  %s i8 step %d max err %.3g" % (name, t, err))
+            assert err <= F32_TOL, (t, err)
+    torch.cuda.synchronize()
+    assert rings[0].ring_pos == spec.writes % W and rings[0].ring_len == min(spec.writes, W)
+    phys = m.physical()
+    hs = heads(lambda g: (np.concatenate([rk[g], np.stack([toks[t][0][g] for t in phys])]),
+                          np.concatenate([rv[g], np.stack([toks[t][1][g] for t in phys])])))
+    assert_i8_codes_equal(c, 0, hs, [1] * spec.n_heads, spec.prefill + len(phys))
+
+
+def test_rswa_i8_small():
+    say("case: rswa i8 rswa_f32")
+    rswa_i8_workload("rswa_f32", check_steps=set(range(0, 165, 3)) | {127, 128, 164})
+
+
+def test_rswa_i8_long():
+    say("case: rswa i8 rswa_long_f32")
+    rswa_i8_workload("rswa_long_f32", check_steps={0, 127, 128, 250, 499})

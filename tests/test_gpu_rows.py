@@ -151,17 +151,18 @@ def test_truncate_then_append_equals_never_appended(kind):
     assert np.array_equal(host(o1).view(np.uint32), host(o2).view(np.uint32))
 
 
-def test_rswa_rollback_restores_the_accepted_path():
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_rswa_rollback_restores_the_accepted_path(kind):
     """[P3] test checkpoint_rollback_restores_ring_rows_byte_identical at the
     decode level: 5 reference rows, 9 accepted steps, checkpoint, 6 draft
     steps, rollback, then more accepted steps: every output and every live
     row equals a control cache that never speculated, and the first dead
     slot still holds a draft row."""
-    say("case: rswa rollback")
+    say("case: rswa rollback kind", kind)
     r = rng(300)
     nh, pf = 4, 5
-    test = K.KvCache(K.KIND_F32, 1, nh, pf + 128)
-    ctrl = K.KvCache(K.KIND_F32, 1, nh, pf + 128)
+    test = K.KvCache(kind, 1, nh, pf + 128)
+    ctrl = K.KvCache(kind, 1, nh, pf + 128)
     rt, rc = K.Rings(1), K.Rings(1)
     ref = (r.standard_normal((2, pf, nh, 128))).astype(np.float32)
     for cc, rr in ((test, rt), (ctrl, rc)):
@@ -182,8 +183,12 @@ def test_rswa_rollback_restores_the_accepted_path():
     K.rswa_rollback_to(test, rt, 0, cp)
     assert (rt[0].ring_len, rt[0].ring_pos, rt[0].writes, test.len[0]) == (9, 9, 9, pf + 9)
     torch.cuda.synchronize()
-    kt = host(test.view("k"))[0]
-    assert np.array_equal(kt[:, pf + 9], host(drafts[0][1])[0])          # stale, never read
+    stale = host(drafts[0][1])[0]
+    if kind == K.KIND_F32:
+        assert np.array_equal(host(test.view("k"))[0][:, pf + 9], stale)      # stale, never read
+    else:
+        codes = np.stack([oracle.quant_row_i8(stale[g])[0] for g in range(nh)])
+        assert np.array_equal(host(test.view("kq"))[0][:, pf + 9], codes)
     for t in range(9, 14):
         q, k, v = acc[t]
         K.rswa_decode(test, rt, nh, q, k, v, ot)
@@ -191,8 +196,9 @@ def test_rswa_rollback_restores_the_accepted_path():
         torch.cuda.synchronize()
         assert np.array_equal(host(ot).view(np.uint32), host(oc).view(np.uint32)), t
     n = pf + 14
-    for nm in ("k", "v"):
-        assert np.array_equal(host(test.view(nm))[:, :, :n], host(ctrl.view(nm))[:, :, :n])
+    for nm in BUFS[kind]:
+        a, b = host(test.view(nm))[:, :, :n], host(ctrl.view(nm))[:, :, :n]
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), nm
     # the abandoned branch's checkpoint no longer matches
     with pytest.raises(K.KvqError):
         K.rswa_rollback_to(test, rt, 0, cp)
