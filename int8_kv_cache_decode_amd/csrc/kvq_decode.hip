@@ -660,22 +660,26 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 
         // Two register sets, ping-pong: the next step's loads are issued before
         // this step's arithmetic.  Rows are clamped into the piece, so a
-        // prefetch past its end re-reads its last row (and is unused).
+        // prefetch past its end re-reads its last row (and is unused).  Only
+        // steps that start inside the piece are computed, so a step's first
+        // tile needs no branch; and the loop leaves only at its head.  Both
+        // keep every path through the loop waiting for exactly the loads it
+        // consumes: a path that skipped a tile, or a break between the two
+        // halves, makes the compiler drain every load at the loop head, so
+        // the next step's loads would wait for the current step's.
         auto compute_step = [&](int r, const Tile (&t)[kTiles]) {
 #pragma unroll
             for (int k = 0; k < kTiles; ++k)
-                if (r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
+                if (k == 0 || r + 16 * k < it.row1) compute_tile(r + 16 * k, t[k]);
         };
-        while (true) {
+        while (r0 + kStep < it.row1) {          // steps r0 and r0 + kStep both hold rows
             load_step(r0 + kStep, tb);
             compute_step(r0, ta);
-            r0 += kStep;
-            if (r0 >= it.row1) break;
-            load_step(r0 + kStep, ta);
-            compute_step(r0, tb);
-            r0 += kStep;
-            if (r0 >= it.row1) break;
+            load_step(r0 + 2 * kStep, ta);
+            compute_step(r0 + kStep, tb);
+            r0 += 2 * kStep;
         }
+        if (r0 < it.row1) compute_step(r0, ta);
 
         // ---- the piece's partial: (max, sum) and the f64 accumulators per head ----
         if (since_flush) flush();
@@ -942,16 +946,16 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
         int r0 = it.row0;
         Tile ta, tb;
         load_tile(r0, ta);
-        while (true) {
+        // ping-pong with one exit at the loop head (as in k_decode_q8: a break
+        // between the halves makes the compiler drain every load there)
+        while (r0 + kTileRows < it.row1) {
             load_tile(r0 + kTileRows, tb);
             compute_tile(r0, ta);
-            r0 += kTileRows;
-            if (r0 >= it.row1) break;
-            load_tile(r0 + kTileRows, ta);
-            compute_tile(r0, tb);
-            r0 += kTileRows;
-            if (r0 >= it.row1) break;
+            load_tile(r0 + 2 * kTileRows, ta);
+            compute_tile(r0 + kTileRows, tb);
+            r0 += 2 * kTileRows;
         }
+        if (r0 < it.row1) compute_tile(r0, ta);
         // the piece's partial for each valid query
         float lt = l + __shfl_xor(l, 16, 64);
         lt += __shfl_xor(lt, 32, 64);

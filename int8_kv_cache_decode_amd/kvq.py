@@ -21,6 +21,7 @@ K_GROUP = 32
 COL_WARMUP = 64
 RING_WINDOW = 128
 MAX_KV_HEADS = 64
+MAX_CAPACITY = 1 << 24
 ALL_SEQS = -1
 
 OK, EINVAL, ECAPACITY, ESTATE, EDEVICE = 0, -1, -2, -3, -4

@@ -80,6 +80,8 @@ def _load():
         L.orc_quant_rows_i8.restype = None
         L.orc_attend_i8.argtypes = [i, i, i, P, P, P, P, P, P]
         L.orc_attend_i8.restype = None
+        L.orc_attend_i8_ex.argtypes = [i, i, i, P, P, P, P, P, i, P, P]
+        L.orc_attend_i8_ex.restype = None
         L.orc_weights_f32.argtypes = [i, i, P, P, P]
         L.orc_weights_f32.restype = None
         _lib = L
@@ -258,16 +260,19 @@ def attend_q8(q, head: Q8Head, first: int = 0, softcap: float = 0.0, sinks=None)
     return out[0] if squeeze else out
 
 
-def attend_i8(q, head: I8Head) -> np.ndarray:
+def attend_i8(q, head: I8Head, first: int = 0, sinks=None) -> np.ndarray:
     """[P3] decode_attention_int8 for one KV head: q [hpk][hd] quantised per
     head, exact integer dots scaled by qscale * kscale / sqrt(hd), softmax,
-    V dequantised per row; float64."""
+    V dequantised per row; float64.  first / sinks [hpk] as attend_f32 (the
+    page's int8 route has neither; they serve as test identities)."""
     q = _f32(q)
     squeeze = q.ndim == 1
     q2 = q.reshape(1, -1) if squeeze else q
     hpk, hd = q2.shape
     out = np.zeros((hpk, hd), np.float64)
-    _load().orc_attend_i8(head.n, hd, hpk, _p(q2), _p(head.kq), _p(head.ks), _p(head.vq), _p(head.vs), _p(out))
+    z = None if sinks is None else _f32(np.asarray(sinks).reshape(hpk))
+    _load().orc_attend_i8_ex(head.n, hd, hpk, _p(q2), _p(head.kq), _p(head.ks), _p(head.vq), _p(head.vs),
+                             int(first), _p(z), _p(out))
     return out[0] if squeeze else out
 
 
@@ -311,7 +316,7 @@ def decode(q, units, n_kv_heads: int, threads: int = 1, only=None, first=None, s
         if u[0] == "f32":
             out[b, g * hpk:(g + 1) * hpk] = attend_f32(qg, u[1], u[2], f, softcap, z)
         elif u[0] == "i8":
-            out[b, g * hpk:(g + 1) * hpk] = attend_i8(qg, u[1])
+            out[b, g * hpk:(g + 1) * hpk] = attend_i8(qg, u[1], f, z)
         else:
             out[b, g * hpk:(g + 1) * hpk] = attend_q8(qg, u[1], f, softcap, z)
 

@@ -340,35 +340,49 @@ void orc_quant_rows_i8(int n, int hd, const float* x, int8_t* q, float* s)
  * quantize_row_i8; its score against row p is the exact integer dot of the
  * codes times qscale * kscale[p] / sqrt(hd); weights by the softmax; the
  * output sums weight * vscale[p] * vcode[p][d] (all in double).
- *   kq[n][hd], ks[n], vq[n][hd], vs[n];  q[hpk][hd];  out[hpk][hd]           */
-void orc_attend_i8(int n, int hd, int hpk, const float* q,
-                   const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
-                   double* out)
+ *   kq[n][hd], ks[n], vq[n][hd], vs[n];  q[hpk][hd];  out[hpk][hd]
+ * first and sinks as attend_generic (the visible-row start and a value-less
+ * logit per head of [P2] attend_group_upto; 0 and NULL for the page's int8
+ * route, which has neither).                                               */
+void orc_attend_i8_ex(int n, int hd, int hpk, const float* q,
+                      const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
+                      int first, const float* sinks, double* out)
 {
     for (int i = 0; i < hpk * hd; ++i) out[i] = 0.0;
     if (n <= 0) return;
+    if (first > n - 1) first = n - 1;
+    if (first < 0) first = 0;
     int8_t* qc = (int8_t*)malloc((size_t)hd);
     double* s = (double*)malloc(sizeof(double) * (size_t)n);
     double scale = 1.0 / sqrt((double)hd);
     for (int h = 0; h < hpk; ++h) {
         float qs = orc_quant_row_i8(q + (size_t)h * hd, hd, qc);
         double* oh = out + (size_t)h * hd;
-        for (int p = 0; p < n; ++p) {
+        for (int p = first; p < n; ++p) {
             long dot = 0;
             for (int d = 0; d < hd; ++d) dot += (long)qc[d] * (long)kq[(size_t)p * hd + d];
             s[p] = (double)dot * (double)qs * (double)ks[p] * scale;
         }
-        double m = s[0];
-        for (int p = 1; p < n; ++p) if (s[p] > m) m = s[p];
+        double m = s[first];
+        for (int p = first + 1; p < n; ++p) if (s[p] > m) m = s[p];
+        if (sinks != NULL && (double)sinks[h] > m) m = (double)sinks[h];
         double z = 0.0;
-        for (int p = 0; p < n; ++p) { s[p] = exp(s[p] - m); z += s[p]; }
-        for (int p = 0; p < n; ++p) {
+        for (int p = first; p < n; ++p) { s[p] = exp(s[p] - m); z += s[p]; }
+        if (sinks != NULL) z += exp((double)sinks[h] - m);
+        for (int p = first; p < n; ++p) {
             double w = s[p] / z * (double)vs[p];
             for (int d = 0; d < hd; ++d) oh[d] += w * (double)vq[(size_t)p * hd + d];
         }
     }
     free(s);
     free(qc);
+}
+
+void orc_attend_i8(int n, int hd, int hpk, const float* q,
+                   const int8_t* kq, const float* ks, const int8_t* vq, const float* vs,
+                   double* out)
+{
+    orc_attend_i8_ex(n, hd, hpk, q, kq, ks, vq, vs, 0, NULL, out);
 }
 
 /* Attention weights alone (for the sum-to-one invariant): w[n] for one query

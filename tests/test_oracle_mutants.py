@@ -46,6 +46,9 @@ MUTANTS = {
     "i8_drops_vscale": ("double w = s[p] / z * (double)vs[p];", "double w = s[p] / z;"),
     "i8_drops_qscale": ("s[p] = (double)dot * (double)qs * (double)ks[p] * scale;",
                         "s[p] = (double)dot * (double)ks[p] * scale;"),
+    "i8_first_ignored": ("if (first < 0) first = 0;\n    int8_t* qc", "first = 0;\n    int8_t* qc"),
+    "i8_sink_not_in_denominator": ("if (sinks != NULL) z += exp((double)sinks[h] - m);", "", 2),
+    "i8_sink_scaled": ("z += exp((double)sinks[h] - m);", "z += exp((double)sinks[h] * scale - m);", 2),
     "softcap_missing_factor": ("s[p] = softcap * tanh(s[p] / softcap);", "s[p] = tanh(s[p] / softcap);"),
     "softcap_before_scale": ("s[p] = dot * scale;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);",
                              "s[p] = dot;\n            if (softcap > 0.0) s[p] = softcap * tanh(s[p] / softcap);\n"
@@ -66,11 +69,14 @@ sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider", sys.argv[3]]))
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
     src = open(SRC).read()
-    old, new = MUTANTS[name]
-    assert src.count(old) >= 1, "mutation site not found: " + name
+    old, new, nth = (MUTANTS[name] + (1,))[:3]         # nth: which occurrence to edit
+    assert src.count(old) >= nth, "mutation site not found: " + name
     c = tmp_path / (name + ".c")
     so = tmp_path / (name + ".so")
-    c.write_text(src.replace(old, new, 1))
+    at = -1
+    for _ in range(nth):
+        at = src.index(old, at + 1)
+    c.write_text(src[:at] + new + src[at + len(old):])
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                     "-o", str(so), str(c), "-lm"], check=True)
     runner = tmp_path / "run.py"

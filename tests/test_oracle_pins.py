@@ -920,6 +920,25 @@ def test_int8_attention_matches_sdpa_on_dequantised_rows():
     assert 127 * 127 * HD == 2_064_512 < 2 ** 31
 
 
+@pytest.mark.parametrize("first,with_sinks", [(0, True), (37, False), (37, True), (89, True), (500, False)])
+def test_int8_attention_options_match_sdpa(first, with_sinks):
+    """The visible-row start and value-less sink logits on the int8 route
+    equal the same options ([P2] attend_group_upto) on the dequantised query
+    and rows: torch SDPA in float64 with -inf before the clamped first row and
+    a zero key/value column biased by the sink."""
+    r = rng(5200 + first + 7 * with_sinks)
+    h = oracle.I8Head(cap=90)
+    h.append((r.standard_normal((90, HD)) * 3).astype(np.float32),
+             (r.standard_normal((90, HD)) * 3).astype(np.float32))
+    q = (r.standard_normal((4, HD)) * 2).astype(np.float32)
+    z = (r.standard_normal(4) * 4).astype(np.float32) if with_sinks else None
+    got = oracle.attend_i8(q, h, first=first, sinks=z)
+    qh = np.stack([oracle.quant_row_i8(q[i])[0].astype(np.float64) * float(oracle.quant_row_i8(q[i])[1])
+                   for i in range(4)])
+    ref = options_reference(qh, h.dequant_k(), h.dequant_v(), first, 0.0, z)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
 def test_workload_generators_are_deterministic():
     s = workloads.get("batched_q8")
     L = s.lengths()
