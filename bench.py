@@ -427,6 +427,19 @@ def cpu_baseline(args, rs, bq, do_rswa, do_q8):
             break
     pos_rep = positions
     positions *= reps
+    # one more repeat on a single thread
+    t1 = time.perf_counter()
+    if units_r is not None:
+        oracle.decode(q_r, units_r, rs.n_heads, threads=1)
+    if units_q is not None:
+        oracle.decode(q_q, units_q, bq.n_kv_heads, threads=1)
+    wall1 = time.perf_counter() - t1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     sample = []
     if do_rswa:
         sample.append("rswa_long_f32: one decode, 10 heads x 32768 rows")
@@ -435,7 +448,8 @@ def cpu_baseline(args, rs, bq, do_rswa, do_q8):
                       % (args.cpu_sample_seqs - 1, pos_rep - (rs.prefill + rs.window if do_rswa else 0)))
     return {"value": round(positions / wall, 1), "unit": "KV positions/s", "cores": threads,
             "kind": "oracle", "sample": "; ".join(sample) + "; float64 oracle, repeated %d times, %.2f s wall"
-            % (reps, wall)}
+            % (reps, wall),
+            "single_core_value": round(pos_rep / wall1, 1), "cpu_model": model}
 
 
 if __name__ == "__main__":

@@ -1074,14 +1074,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
         }
         const int wv = resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk));
         if (wv == 0) return hipErrorInvalidDevice;
-        int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
-#ifdef KVQ_Q8_MIN_TILES
-        if (kQ8) {
-            const int want = a.n_tiles / KVQ_Q8_MIN_TILES, lo = (wv + 3) / 4;
-            shares = want < wv ? want : wv;
-            shares = shares > lo ? shares : lo;
-        }
-#endif
+        const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};
