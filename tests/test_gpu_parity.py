@@ -320,14 +320,15 @@ def test_q8_lossless_rows_equal_f32():
 # ---------------------------------------------------------------------------
 # R-SWA
 # ---------------------------------------------------------------------------
-def rswa_run(nh, prefill, steps, seed, check_every=1, batch=1, hpk=1):
+def rswa_run(nh, prefill, steps, seed, check_every=1, batch=1, hpk=1, kind=K.KIND_F32):
     """Drive rswa_decode for `steps` steps on `batch` streams; compare outputs
-    every `check_every` steps and the ring slots at the end."""
+    every `check_every` steps and the ring slots at the end.  kind KIND_I8:
+    the int8 mirror, compared with the oracle's int8 route and codec."""
     r = rng(seed)
     W = K.RING_WINDOW
     pre = [prefill + 3 * b for b in range(batch)]
     cap = max(pre) + W
-    c = K.KvCache(K.KIND_F32, batch, nh, cap)
+    c = K.KvCache(kind, batch, nh, cap)
     rings = K.Rings(batch)
     ref_k = [r.standard_normal((p, nh, 128)).astype(np.float32) for p in pre]
     ref_v = [r.standard_normal((p, nh, 128)).astype(np.float32) for p in pre]
@@ -360,12 +361,29 @@ def rswa_run(nh, prefill, steps, seed, check_every=1, batch=1, hpk=1):
                 win = models[b].window()
                 kk = np.concatenate([ref_k[b], np.stack([tok_k[s][b] for s in win])])
                 vv = np.concatenate([ref_v[b], np.stack([tok_v[s][b] for s in win])])
-                units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
-                              for g in range(nh)])
+                if kind == K.KIND_F32:
+                    units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
+                                  for g in range(nh)])
+                else:
+                    units.append([("i8", i8_head(kk[:, g], vv[:, g])) for g in range(nh)])
             ref = oracle.decode(q, units, nh, threads=THREADS)
             err = max_err(got, ref)
             assert err <= F32_TOL, (t, err)
     torch.cuda.synchronize()
+    if kind == K.KIND_I8:
+        # every stored row (reference and ring slot) is the page's codec of its source row
+        kq, ks, vq, vs = (host(c.view(nm)) for nm in ("kq", "ks", "vq", "vs"))
+        for b in range(batch):
+            m = models[b]
+            for g in range(nh):
+                src_k = np.concatenate([ref_k[b][:, g]] + [tok_k[t][b][g][None] for t in m.physical()])
+                src_v = np.concatenate([ref_v[b][:, g]] + [tok_v[t][b][g][None] for t in m.physical()])
+                h = i8_head(src_k, src_v)
+                n = src_k.shape[0]
+                assert np.array_equal(kq[b, g, :n], h.kq[:n]) and np.array_equal(vq[b, g, :n], h.vq[:n]), (b, g)
+                assert np.array_equal(ks[b, g, :n].view(np.uint32), h.ks[:n].view(np.uint32)), (b, g)
+                assert np.array_equal(vs[b, g, :n].view(np.uint32), h.vs[:n].view(np.uint32)), (b, g)
+        return rings
     kk, vv = host(c.view("k")), host(c.view("v"))
     for b in range(batch):
         m = models[b]
@@ -377,6 +395,23 @@ def rswa_run(nh, prefill, steps, seed, check_every=1, batch=1, hpk=1):
             assert np.array_equal(kk[b, :, pre[b] + s], tok_k[t][b])
             assert np.array_equal(vv[b, :, pre[b] + s], tok_v[t][b])
     return rings
+
+
+def i8_head(k, v):
+    h = oracle.I8Head(cap=max(k.shape[0], 1))
+    if k.shape[0]:
+        h.append(k, v)
+    return h
+
+
+def test_rswa_i8_small_batched_empty():
+    """The int8 mirror through the same R-SWA drives as the f32 cases below:
+    ring wrap, three streams with GQA groups, an empty reference block."""
+    say("case: rswa i8 small / batched / empty reference")
+    rings = rswa_run(nh=4, prefill=5, steps=300, seed=31, check_every=7, kind=K.KIND_I8)
+    assert rings[0].ring_len == 128 and rings[0].ring_pos == 300 % 128
+    rswa_run(nh=2, prefill=9, steps=140, seed=32, check_every=13, batch=3, hpk=2, kind=K.KIND_I8)
+    rswa_run(nh=3, prefill=0, steps=5, seed=33, kind=K.KIND_I8)
 
 
 def test_rswa_small_wraps_ring():
