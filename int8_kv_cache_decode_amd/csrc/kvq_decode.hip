@@ -708,8 +708,11 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 // the same rescaling as the fold ([P3] fold: accumulators are rescaled by
 // exp(old max - new max)), divide, and apply the V column field (q8 only).
 // Empty partials (max -inf) weigh nothing.  Q heads of dead groups, and
-// sequences with no rows, get zeros.  Up to 512 threads = 16 sub-groups of
-// 32 lanes (a float4 of channels each), sized to the number of partials; a
+// sequences with no rows, get zeros.  When the (sequence, head) grid is
+// small (R-SWA: 10 heads), a head's 128 channels are split over up to four
+// blocks, so that more compute units share the read of its partials; a block
+// then has sub-groups of lpg = 32 / chunks lanes (a float4 of channels
+// each), as many as its partial count asks for (at most 512 threads).  A
 // sub-group takes every ngroups-th partial, issuing the loads of up to 8 at
 // once and folding them with a running max; the sub-groups then merge in LDS.
 // ---------------------------------------------------------------------------
@@ -720,20 +723,23 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #define KVQ_COMBINE_BATCH 8
 #endif
 constexpr int kCombineThreads = KVQ_COMBINE_THREADS;
-constexpr int kCombineGroups = kCombineThreads / 32;
 constexpr int kCombineBatch = KVQ_COMBINE_BATCH;
+constexpr int kCombineMinLanes = 8;                     // lanes per sub-group with 4 chunks
 
-// Folds the nch partials at ml / acc (strides mstride / astride floats)
-// with a sink logit zs in log2 units (-inf: none) and leaves, for tid < 32,
-// the normalised channels 4 tid .. 4 tid + 3 in *res.  Block-wide: every
-// thread of the block calls it.
+// Channel chunks per head for a grid of `blocks` (sequence, head) pairs.
+inline int combine_chunks(int blocks) { return blocks >= 256 ? 1 : blocks >= 128 ? 2 : 4; }
+
+// Folds the nch partials at ml / acc (strides mstride / astride floats),
+// channels ch0 .. ch0 + 4 lpg - 1, with a sink logit zs in log2 units (-inf:
+// none) and leaves, for tid < lpg, the normalised channels ch0 + 4 tid ..
+// + 3 in *res.  Block-wide: every thread of the block calls it.
 __device__ __forceinline__ bool combine_partials(const float* ml, const float* acc, size_t mstride, size_t astride,
-                                                 int nch, float zs, float4* res) {
-    __shared__ float4 sm_acc[kCombineGroups][32];
-    __shared__ float sm_m[kCombineGroups], sm_l[kCombineGroups];
+                                                 int nch, float zs, int lpg, int ch0, float4* res) {
+    __shared__ float4 sm_acc[kCombineThreads];
+    __shared__ float sm_m[kCombineThreads / kCombineMinLanes], sm_l[kCombineThreads / kCombineMinLanes];
     const int tid = threadIdx.x;
-    const int sg = tid >> 5, lane = tid & 31;
-    const int ngroups = (int)(blockDim.x >> 5);
+    const int sg = tid / lpg, lane = tid - sg * lpg;
+    const int ngroups = (int)blockDim.x / lpg;
 
     float M = -INFINITY, L = 0.0f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -746,7 +752,7 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
             const bool ok = c < nch;
             mv[k] = ok ? ml[c * mstride] : -INFINITY;
             lv[k] = ok ? ml[c * mstride + 1] : 0.0f;
-            xv[k] = ok ? *(const float4*)(acc + c * astride + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
+            xv[k] = ok ? *(const float4*)(acc + c * astride + ch0 + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float Mn = M;
 #pragma unroll
@@ -768,13 +774,13 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
         }
         M = Mn;
     }
-    sm_acc[sg][lane] = A;
+    sm_acc[tid] = A;
     if (lane == 0) {
         sm_m[sg] = M;
         sm_l[sg] = L;
     }
     __syncthreads();
-    if (tid >= 32) return false;
+    if (tid >= lpg) return false;
     // a learned sink joins the max and the denominator ([P2] attend_group_upto)
     float Mt = fmaxf(sm_m[0], zs);
     for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
@@ -782,27 +788,32 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
     float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < ngroups; ++k) {
         const float e = sm_m[k] == -INFINITY ? 0.0f : fast_exp2(sm_m[k] - Mt);   // sub-groups without rows
+        const float4 x = sm_acc[k * lpg + tid];
         Lt = fmaf(e, sm_l[k], Lt);
-        At.x = fmaf(e, sm_acc[k][tid].x, At.x);
-        At.y = fmaf(e, sm_acc[k][tid].y, At.y);
-        At.z = fmaf(e, sm_acc[k][tid].z, At.z);
-        At.w = fmaf(e, sm_acc[k][tid].w, At.w);
+        At.x = fmaf(e, x.x, At.x);
+        At.y = fmaf(e, x.y, At.y);
+        At.z = fmaf(e, x.z, At.z);
+        At.w = fmaf(e, x.w, At.w);
     }
     const float inv = 1.0f / Lt;
     *res = make_float4(At.x * inv, At.y * inv, At.z * inv, At.w * inv);
     return true;
 }
 
+// Block (Q head h x channel chunk, sequence j); chunks = gridDim.x / n_q_heads.
 template <bool kQ8>
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a) {
-    const int h = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int chunks = (int)gridDim.x / a.n_q_heads;
+    const int h = blockIdx.x / chunks, ck = blockIdx.x - h * chunks;
+    const int lpg = 32 / chunks, ch0 = 4 * lpg * ck;
+    const int j = blockIdx.y, tid = threadIdx.x;
     const int b = a.seq0 + j;
     const int g = h / a.hpk, hh = h - g * a.hpk;
     const int gl = a.live_slot[g];
-    float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD;
+    float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD + ch0;
     const int nt = a.ntile[j];
     if (gl < 0 || nt == 0) {
-        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < lpg) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
     // slots of the segment: its first..last share + segment index
@@ -813,10 +824,10 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     const float zs = a.sinks ? (float)((double)a.sinks[h] * 1.4426950408889634) : -INFINITY;
     float4 rr;
     if (!combine_partials(a.ws_ml + (it0 * a.hpk + hh) * 2, a.ws_acc + (it0 * a.hpk + hh) * kHD,
-                          (size_t)a.hpk * 2, (size_t)a.hpk * kHD, nch, zs, &rr))
+                          (size_t)a.hpk * 2, (size_t)a.hpk * kHD, nch, zs, lpg, ch0, &rr))
         return;
     if (kQ8 && a.frozen[j]) {
-        const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + 4 * tid);
+        const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + ch0 + 4 * tid);
         rr.x *= vc.x;
         rr.y *= vc.y;
         rr.z *= vc.z;
@@ -975,17 +986,20 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
     });
 }
 
-// Combine of the verify: block (draft i x Q head h, sequence).
+// Combine of the verify: block (draft i x Q head h x channel chunk, sequence).
 __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const VerifyArgs a) {
-    const int x = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int chunks = (int)gridDim.x / (a.n_draft * a.n_q_heads);
+    const int x = blockIdx.x / chunks, ck = blockIdx.x - x * chunks;
+    const int lpg = 32 / chunks, ch0 = 4 * lpg * ck;
+    const int j = blockIdx.y, tid = threadIdx.x;
     const int i = x / a.n_q_heads, h = x - i * a.n_q_heads;
     const int b = a.seq0 + j;
     const int g = h / a.hpk, hh = h - g * a.hpk;
     const int gl = a.live_slot[g];
-    float* o = a.out + (((size_t)b * a.n_draft + i) * a.n_q_heads + h) * kHD;
+    float* o = a.out + (((size_t)b * a.n_draft + i) * a.n_q_heads + h) * kHD + ch0;
     const int nt = a.ntile[j];
     if (gl < 0 || nt == 0) {
-        if (tid < 32) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < lpg) *(float4*)(o + 4 * tid) = make_float4(0.f, 0.f, 0.f, 0.f);
         return;
     }
     const int sb = a.tile_base[j] + gl * nt;
@@ -995,13 +1009,13 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const Verify
     const int vq = i * a.hpk + hh;
     float4 rr;
     if (combine_partials(a.ws_ml + (it0 * a.nq + vq) * 2, a.ws_acc + (it0 * a.nq + vq) * kHD, (size_t)a.nq * 2,
-                         (size_t)a.nq * kHD, nch, -INFINITY, &rr))
+                         (size_t)a.nq * kHD, nch, -INFINITY, lpg, ch0, &rr))
         *(float4*)(o + 4 * tid) = rr;
 }
 
-// Threads per combine block: enough 32-lane sub-groups that each folds at
-// most one batch of partials, between 1 and 16 sub-groups.
-int combine_threads(const DecodeArgs& a) {
+// Threads per combine block: enough sub-groups of lpg lanes that each folds
+// at most one batch of partials, between 1 sub-group and 512 threads.
+int combine_threads(const DecodeArgs& a, int lpg) {
     int nmax = 1;
     for (int j = 0; j < a.n_seq; ++j) {
         const int nt = a.ntile[j];
@@ -1013,8 +1027,9 @@ int combine_threads(const DecodeArgs& a) {
         }
     }
     int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
-    groups = groups < 1 ? 1 : (groups > kCombineGroups ? kCombineGroups : groups);
-    return 32 * groups;
+    const int gmax = kCombineThreads / lpg;
+    groups = groups < 1 ? 1 : (groups > gmax ? gmax : groups);
+    return lpg * groups;
 }
 
 // Waves of a decode kernel that are resident on the current device at once
@@ -1082,7 +1097,9 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     // the i8 kind has no column field to apply
-    hipLaunchKernelGGL(k_combine<kKind == kQ8k>, dim3(a.n_q_heads, a.n_seq), dim3(combine_threads(a)), 0, s, a);
+    const int chunks = combine_chunks(a.n_q_heads * a.n_seq);
+    hipLaunchKernelGGL(k_combine<kKind == kQ8k>, dim3(a.n_q_heads * chunks, a.n_seq),
+                       dim3(combine_threads(a, 32 / chunks)), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1111,9 +1128,13 @@ hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
                             tile_owner(sb, a.n_tiles, a.n_shares) + 1;
             nmax = cnt > nmax ? cnt : nmax;
         }
+    const int chunks = combine_chunks(a.n_draft * a.n_q_heads * a.n_seq);
+    const int lpg = 32 / chunks;
     int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
-    groups = groups < 1 ? 1 : (groups > kCombineGroups ? kCombineGroups : groups);
-    hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads, a.n_seq), dim3(32 * groups), 0, s, a);
+    const int gmax = kCombineThreads / lpg;
+    groups = groups < 1 ? 1 : (groups > gmax ? gmax : groups);
+    hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads * chunks, a.n_seq), dim3(lpg * groups), 0, s,
+                       a);
     return hipGetLastError();
 }
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kQ8k>(a, s); }
