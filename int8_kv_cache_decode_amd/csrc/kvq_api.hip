@@ -260,6 +260,10 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
     a.v_new = v_new;
     a.k_store = c->k;
     a.v_store = c->v;
+    a.kq_store = c->kq;
+    a.ks_store = c->ks;
+    a.vq_store = c->vq;
+    a.vs_store = c->vs;
     a.n_kv_heads = c->n_kv_heads;
     a.n_live = c->n_live;
     a.n_q_heads = n_q_heads;
@@ -684,19 +688,11 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
         wrows[b] = r.prefill_len + slot;
         lens[b] = r.prefill_len + r.ring_len;
     }
-    if (c->kind == KVQ_KIND_I8) {
-        // [P3] write_decode_step quantises the step's row into the int8
-        // mirror's ring slot; the int8 decode then reads it like any row
-        std::vector<Seg> segs;
-        for (int b = 0; b < c->batch; ++b) segs.push_back({b, b, wrows[b], 1, false});
-        if ((rc = launch_segments(c, k_new, v_new, segs, (hipStream_t)stream, fn))) return rc;
-        rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), nullptr, nullptr, nullptr, nullptr,
-                        (hipStream_t)stream, fn);
-    } else {
-        rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new, nullptr,
-                        (hipStream_t)stream, fn);
-    }
-    if (rc) return rc;
+    // the ring row is written inside the decode kernel, by the wave whose
+    // share holds it (on the i8 kind quantised there with quantize_row_i8)
+    if ((rc = run_decode(c, n_q_heads, hpk, q, out, ws, lens.data(), wrows.data(), k_new, v_new, nullptr,
+                         (hipStream_t)stream, fn)))
+        return rc;
     for (int b = 0; b < c->batch; ++b) {
         rings[b] = next[b];
         c->len[b] = lens[b];

@@ -372,6 +372,9 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
     __shared__ float sm_alpha[kWaves][2][HPK];        // per wave, two tiles: rescale factor per head
     __shared__ double sm_v64[kWaves][HPK][kHD];       // per wave: flushed V accumulators
+    // i8 kind, R-SWA: the ring row's fresh K / V codes and their scales
+    __shared__ __attribute__((aligned(16))) int8_t sm_ring[kI8 ? kWaves : 1][2][kHD];
+    __shared__ float sm_ring_s[kI8 ? kWaves : 1][2];
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -385,6 +388,44 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         const float* VS = a.vs + it.hrow;
         const bool frz = !kI8 && a.frozen[it.j] != 0;
         const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
+
+        // [P3] write_decode_step on the int8 mirror: the wave whose piece holds
+        // the R-SWA row quantises the step's K and V rows (quantize_row_i8:
+        // scale max|x| / 127, 1 for a zero row; codes rounded half to even),
+        // stores codes and scales in the cache and keeps them in its LDS slot:
+        // its own loads of that tile may predate the store, so the tile takes
+        // the row from the slot.  No other wave reads the row.
+        int wl = -1;
+        if constexpr (kI8) {
+            const int wr = a.wrow[it.j];
+            if (wr >= it.row0 && wr < it.row1) {
+                wl = wr;
+                const size_t src = ((size_t)it.b * a.n_kv_heads + it.g) * kHD + 2 * lane;
+                const float2 xk = *(const float2*)(a.k_new + src);
+                const float2 xv = *(const float2*)(a.v_new + src);
+                const float ak = wave_max(fmaxf(fabsf(xk.x), fabsf(xk.y)));
+                const float av = wave_max(fmaxf(fabsf(xv.x), fabsf(xv.y)));
+                const float sk = ak > 0.0f ? __fdiv_rn(ak, 127.0f) : 1.0f;
+                const float sv = av > 0.0f ? __fdiv_rn(av, 127.0f) : 1.0f;
+                char2 ck, cv;
+                ck.x = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(xk.x, sk)), -127.0f), 127.0f);
+                ck.y = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(xk.y, sk)), -127.0f), 127.0f);
+                cv.x = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(xv.x, sv)), -127.0f), 127.0f);
+                cv.y = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(xv.y, sv)), -127.0f), 127.0f);
+                const size_t row = it.hrow + (size_t)wl;
+                *(char2*)(&sm_ring[wave][0][2 * lane]) = ck;
+                *(char2*)(&sm_ring[wave][1][2 * lane]) = cv;
+                *(char2*)(a.kq_store + row * kHD + 2 * lane) = ck;
+                *(char2*)(a.vq_store + row * kHD + 2 * lane) = cv;
+                if (lane == 0) {
+                    sm_ring_s[wave][0] = sk;
+                    sm_ring_s[wave][1] = sv;
+                    a.ks_store[row] = sk;
+                    a.vs_store[row] = sv;
+                }
+                wave_lds_sync();
+            }
+        }
 
         // The piece's 16-row tiles, kTiles per step; the loads of the next step
         // are issued before this step's arithmetic.
@@ -573,7 +614,25 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         int since_flush = 0;
 
         int buf = 0;
-        auto compute_tile = [&](int r0, const Tile& t) {
+        auto compute_tile = [&](int r0, const Tile& tc) {
+            Tile t = tc;
+            if constexpr (kI8) {
+                if (wl >= r0 && wl < r0 + 16) {           // the ring row's tile: that row from the LDS slot
+                    const int wn = wl - r0;
+                    if (n == wn) {
+                        t.kb2[0] = *(const uint4*)(&sm_ring[wave][0][16 * (lane >> 4)]);
+                        t.kb2[1] = *(const uint4*)(&sm_ring[wave][0][64 + 16 * (lane >> 4)]);
+                        t.ks4.x = sm_ring_s[wave][0];
+                        t.vsn = sm_ring_s[wave][1];
+                    }
+                    if (ri == (wn & (kVRows - 1))) {
+                        const uint2 x = *(const uint2*)(&sm_ring[wave][1][kVDim * seg]);
+#pragma unroll
+                        for (int i = 0; i < kVLoads; ++i)
+                            if (i == wn / kVRows) t.vx[i] = x;
+                    }
+                }
+            }
             const bool valid = r0 + n < it.row1;
             // ---- scores (exact), softmax weights in the (head, row) layout ----
             bool rescale = false;

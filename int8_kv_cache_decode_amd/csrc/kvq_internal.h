@@ -112,6 +112,10 @@ struct DecodeArgs {
     const float* v_new;
     float* k_store;            // writable f32 storage for the ring write
     float* v_store;
+    int8_t* kq_store;          // writable int8 storage for the ring write (per-row int8 kind)
+    float* ks_store;
+    int8_t* vq_store;
+    float* vs_store;
     int n_kv_heads;
     int n_live;
     int n_q_heads;
