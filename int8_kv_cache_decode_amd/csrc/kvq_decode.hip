@@ -17,6 +17,8 @@
 // log2(e)/sqrt(128)) so every exponential is one v_exp_f32.
 #include <math.h>
 
+#include <atomic>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1096,18 +1098,21 @@ int combine_threads(const DecodeArgs& a, int lpg) {
 // device and kernel.  0 on a runtime error.
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
-    static int cache[kMaxDevices][25];
+    // host threads may race to fill an entry; they all store the same value
+    static std::atomic<int> cache[kMaxDevices][25];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    int& c = cache[dev][which];
-    if (c == 0) {
+    std::atomic<int>& c = cache[dev][which];
+    int v = c.load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWaves * 64, 0) != hipSuccess) return 0;
         const int64_t wv = (int64_t)cus * per_cu * kWaves;
-        c = (int)(wv < 1 ? 1 : (wv > kMaxWaves ? kMaxWaves : wv));
+        v = (int)(wv < 1 ? 1 : (wv > kMaxWaves ? kMaxWaves : wv));
+        c.store(v, std::memory_order_relaxed);
     }
-    return c;
+    return v;
 }
 
 int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
