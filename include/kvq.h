@@ -438,6 +438,46 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q,
                 const float* k_new, const float* v_new, float* out,
                 void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * rswa_shared_record_prefill -- [P3] RingCache::record_prefill for a
+ * reference block shared by n_streams decode streams (the prefix-shared
+ * reference that [P3] batched_decode_attention leaves as a seam: streams
+ * pointing at one reference block, each with its own ring).  Sequence `seq`
+ * of an f32 cache holds the reference, just appended with kv_append_f32
+ * (len[seq] rows); stream s's 128-slot ring is rows len[seq] + 128 s ..
+ * len[seq] + 128 s + 127 of the same sequence.  Sets, for s < n_streams,
+ * rings[s] = {prefill_len = len[seq], ring_len = ring_pos = writes = 0,
+ * epoch + 1} and reserves the ring rows: len[seq] += 128 n_streams.
+ * rings: host array [n_streams], the group's own (not indexed by sequence).
+ * Errors: KVQ_EINVAL (null, seq out of range, n_streams outside 1..16),
+ * KVQ_ESTATE (not an f32 cache), KVQ_ECAPACITY (len[seq] + 128 n_streams >
+ * capacity).
+ */
+int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_streams);
+
+/*
+ * rswa_shared_decode -- one R-SWA decode step for each of the n_streams
+ * streams that share sequence `seq`'s reference block.  Stream s's result is
+ * what rswa_decode would give it alone: its step's K/V go to its ring slot
+ * (the same cursor rules, row prefill + 128 s + slot), then its Q heads
+ * attend, with no mask, over the reference rows and its own live ring slots
+ * ([P3] batched_decode_attention: per stream over its own reference ++ ring).
+ * The reference rows are read once for every stream's queries: n_streams x
+ * (n_q_heads / n_kv_heads) <= 16 queries per KV head share each row read, a
+ * dense contraction on the matrix cores.
+ *
+ * q, out        device float [n_streams][n_q_heads][128]
+ * k_new, v_new  device float [n_streams][n_kv_heads][128]
+ * ws/ws_bytes   at least kvq_verify_workspace_bytes(c, n_q_heads, n_streams).
+ * Errors: KVQ_EINVAL (null, unaligned, seq out of range, n_streams x group
+ * outside 1..16, workspace too small), KVQ_ESTATE (not an f32 cache, group
+ * not recorded, len[seq] no longer prefill + 128 n_streams, a stream with
+ * another prefill or corrupt cursors).  Nothing is written on error.
+ * Checkpoint / rollback of these streams is not provided.
+ */
+int rswa_shared_decode(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, int n_q_heads, const float* q,
+                       const float* k_new, const float* v_new, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* kvq_last_error(void);
 

@@ -772,6 +772,106 @@ int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_
     return KVQ_OK;
 }
 
+int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_streams) {
+    const char* fn = "rswa_shared_record_prefill";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (!rings) return fail(KVQ_EINVAL, "%s: null rings", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if (n_streams < 1 || n_streams > kVerifyMaxQ)
+        return fail(KVQ_EINVAL, "%s: n_streams %d outside 1..%d", fn, n_streams, kVerifyMaxQ);
+    const int pre = c->len[seq];
+    if ((int64_t)pre + (int64_t)KVQ_RING_WINDOW * n_streams > c->capacity)
+        return fail(KVQ_ECAPACITY, "%s: prefill %d + %d rings of %d exceeds capacity %d", fn, pre, n_streams,
+                    KVQ_RING_WINDOW, c->capacity);
+    for (int s = 0; s < n_streams; ++s)
+        if (rings[s].epoch == INT32_MAX) return fail(KVQ_ESTATE, "%s: stream %d: lineage epoch exhausted", fn, s);
+    for (int s = 0; s < n_streams; ++s) {
+        rings[s].prefill_len = pre;
+        rings[s].ring_len = 0;
+        rings[s].ring_pos = 0;
+        rings[s].epoch += 1;
+        rings[s].writes = 0;
+    }
+    c->len[seq] = pre + KVQ_RING_WINDOW * n_streams;       // the rings' rows are reserved
+    return KVQ_OK;
+}
+
+int rswa_shared_decode(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, int n_q_heads, const float* q,
+                       const float* k_new, const float* v_new, float* out, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "rswa_shared_decode";
+    int rc = check_cache(c, KVQ_KIND_F32, fn);
+    if (rc) return rc;
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "%s: n_q_heads %d is not a multiple of n_kv_heads %d", fn, n_q_heads, c->n_kv_heads);
+    const int hpk = n_q_heads / c->n_kv_heads;
+    if (n_streams < 1 || n_streams * hpk > kVerifyMaxQ)
+        return fail(KVQ_EINVAL, "%s: n_streams %d x group %d must be within 1..%d", fn, n_streams, hpk, kVerifyMaxQ);
+    if (!rings || !q || !k_new || !v_new || !out || !ws) return fail(KVQ_EINVAL, "%s: null argument", fn);
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(ws))
+        return fail(KVQ_EINVAL, "%s: q/k_new/v_new/out/workspace not 16-byte aligned", fn);
+    const size_t need = ws_need(c, n_streams * hpk);
+    if (ws_bytes < need) return fail(KVQ_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    const int pre = rings[0].prefill_len;
+    if (pre < 0) return fail(KVQ_ESTATE, "%s: decode before rswa_shared_record_prefill", fn);
+    if ((int64_t)c->len[seq] != (int64_t)pre + (int64_t)KVQ_RING_WINDOW * n_streams)
+        return fail(KVQ_ESTATE, "%s: len %d != prefill %d + %d rings (another group size, or appended since)", fn,
+                    c->len[seq], pre, n_streams);
+    std::vector<kvq_ring> next(rings, rings + n_streams);
+    VerifyArgs a;
+    memset(&a, 0, sizeof a);
+    for (int s = 0; s < n_streams; ++s) {
+        kvq_ring& r = next[s];
+        if (r.prefill_len != pre) return fail(KVQ_ESTATE, "%s: stream %d: prefill %d != %d", fn, s, r.prefill_len, pre);
+        if (r.ring_len < 0 || r.ring_len > KVQ_RING_WINDOW || r.ring_pos < 0 || r.ring_pos >= KVQ_RING_WINDOW)
+            return fail(KVQ_ESTATE, "%s: stream %d: corrupt ring cursors", fn, s);
+        a.sring[s] = r.ring_len;                  // slots live before the step
+        int slot;                                 // [P3] write_decode_step, as rswa_decode
+        if (r.ring_len < KVQ_RING_WINDOW) {
+            slot = r.ring_len;
+            r.ring_len += 1;
+            r.ring_pos = r.ring_len % KVQ_RING_WINDOW;
+        } else {
+            slot = r.ring_pos;
+            r.ring_pos = (r.ring_pos + 1) % KVQ_RING_WINDOW;
+        }
+        r.writes += 1;
+        a.swrow[s] = pre + KVQ_RING_WINDOW * s + slot;
+    }
+    a.shared = 1;
+    a.q = q;
+    a.out = out;
+    a.k = c->k;
+    a.v = c->v;
+    a.k_store = c->k;
+    a.v_store = c->v;
+    a.kd = k_new;
+    a.vd = v_new;
+    a.ws_acc = (float*)ws;
+    a.ws_ml = (float*)ws + ws_slots(c) * (size_t)(n_streams * hpk) * kHD;
+    a.n_kv_heads = c->n_kv_heads;
+    a.n_live = c->n_live;
+    a.n_q_heads = n_q_heads;
+    a.hpk = hpk;
+    a.capacity = c->capacity;
+    a.n_draft = n_streams;
+    a.nq = n_streams * hpk;
+    fill_live(c, a.live_head);
+    memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
+    a.seq0 = seq;
+    a.n_seq = 1;
+    a.prefill[0] = pre;
+    a.len[0] = c->len[seq] + n_streams;                    // reference, rings, then the step rows
+    a.ntile[0] = (a.len[0] + kTileRows - 1) / kTileRows;
+    a.tile_base[0] = 0;
+    a.tile_base[1] = a.ntile[0] * c->n_live;
+    a.n_tiles = a.tile_base[1];
+    if ((rc = device_status(launch_verify_f32(a, (hipStream_t)stream), fn))) return rc;
+    for (int s = 0; s < n_streams; ++s) rings[s] = next[s];
+    return KVQ_OK;
+}
+
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -920,6 +920,14 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
 // reference rows always; a ring slot unless it is among the e_i = max(0,
 // ring_len + i + 1 - 128) oldest live slots; draft row d iff d <= i.
 // ---------------------------------------------------------------------------
+// kShared: the shared-reference decode -- the "drafts" are streams sharing
+// the sequence's reference rows [0, prefill); stream s owns the ring rows
+// prefill + 128 s .. + 127.  The row space is the reference, the S rings,
+// then the S step rows (read from kd / vd, like drafts): stream s sees the
+// reference, its ring slots that were live before this step except the one
+// the step overwrites, and its own step row.  The wave whose share holds
+// step row s also stores it into stream s's ring.
+template <bool kShared>
 __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
     const int w = share_index();
     if (w >= a.n_shares) return;
@@ -927,21 +935,34 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
     const int qi = lane & 15, kb = lane >> 4;
     for_each_piece(a, w, [&](const Piece& it) {
         const int j = it.j;
-        const int L = a.prefill[j] + a.ring_len[j];                  // cache rows; drafts follow
+        const int pre = a.prefill[j];
+        const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft       // reference + rings; step rows follow
+                              : pre + a.ring_len[j];                     // cache rows; drafts follow
         const float* K = a.k + it.hrow * kHD;
         const float* V = a.v + it.hrow * kHD;
         const size_t dstride = (size_t)a.n_kv_heads * kHD;
-        const float* KD = a.kd + ((size_t)it.b * a.n_draft * a.n_kv_heads + it.g) * kHD;
-        const float* VD = a.vd + ((size_t)it.b * a.n_draft * a.n_kv_heads + it.g) * kHD;
+        const size_t ob = kShared ? 0 : (size_t)it.b;                    // batch index of q / k_draft / out
+        const float* KD = a.kd + (ob * a.n_draft * a.n_kv_heads + it.g) * kHD;
+        const float* VD = a.vd + (ob * a.n_draft * a.n_kv_heads + it.g) * kHD;
         auto row_ptr = [&](const float* C, const float* D, int p) {
             return p < L ? C + (size_t)p * kHD : D + (size_t)(p - L) * dstride;
         };
-        // this lane's query (MFMA column): draft di, head hh of the group
+        if constexpr (kShared) {
+            // [P3] write_decode_step of each stream whose step row is in this piece
+            for (int s = 0; s < a.n_draft; ++s) {
+                if (L + s >= it.row0 && L + s < it.row1 && lane < 32) {
+                    const size_t wr = it.hrow + (size_t)a.swrow[s];
+                    *(float4*)(a.k_store + wr * kHD + 4 * lane) = *(const float4*)(KD + s * dstride + 4 * lane);
+                    *(float4*)(a.v_store + wr * kHD + 4 * lane) = *(const float4*)(VD + s * dstride + 4 * lane);
+                }
+            }
+        }
+        // this lane's query (MFMA column): draft (stream) di, head hh of the group
         const bool qvalid = qi < a.nq;
         const int di = qvalid ? qi / a.hpk : 0, hh = qvalid ? qi - di * a.hpk : 0;
         float qb[32];
         {
-            const float* qp = a.q + (((size_t)it.b * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 4 * kb;
+            const float* qp = a.q + ((ob * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 4 * kb;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const float4 x = qvalid ? *(const float4*)(qp + 16 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -951,12 +972,20 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
                 qb[4 * t + 3] = x.w * kQScale;
             }
         }
-        const int pre = a.prefill[j], rl = a.ring_len[j], old = a.ring_oldest[j];
+        const int rl = a.ring_len[j], old = a.ring_oldest[j];
         const int evict = max(0, rl + di + 1 - KVQ_RING_WINDOW);
+        const int live = kShared ? a.sring[di] : 0;                             // ring slots live before the step
+        const int wslot = kShared ? a.swrow[di] - pre - KVQ_RING_WINDOW * di : 0; // the slot it overwrites
         auto visible = [&](int p) {
             if (p < pre) return true;
-            if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
-            return p - L <= di;
+            if constexpr (kShared) {
+                if (p >= L) return p - L == di;
+                const int slot = (p - pre) & (KVQ_RING_WINDOW - 1);
+                return ((p - pre) >> 7) == di && slot < live && slot != wslot;
+            } else {
+                if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
+                return p - L <= di;
+            }
         };
 
         struct Tile {
@@ -1054,7 +1083,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const Verify
     const int lpg = 32 / chunks, ch0 = 4 * lpg * ck;
     const int j = blockIdx.y, tid = threadIdx.x;
     const int i = x / a.n_q_heads, h = x - i * a.n_q_heads;
-    const int b = a.seq0 + j;
+    const int b = a.shared ? 0 : a.seq0 + j;              // shared decode: out is [streams][n_q_heads][128]
     const int g = h / a.hpk, hh = h - g * a.hpk;
     const int gl = a.live_slot[g];
     float* o = a.out + (((size_t)b * a.n_draft + i) * a.n_q_heads + h) * kHD + ch0;
@@ -1099,7 +1128,7 @@ int combine_threads(const DecodeArgs& a, int lpg) {
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
     // host threads may race to fill an entry; they all store the same value
-    static std::atomic<int> cache[kMaxDevices][25];
+    static std::atomic<int> cache[kMaxDevices][26];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     std::atomic<int>& c = cache[dev][which];
@@ -1176,13 +1205,17 @@ hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
     VerifyArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {                          // zero only when every group is dead
-        const int wv = resident_waves(reinterpret_cast<const void*>(k_verify_f32), 24);
+        const void* fn = a.shared ? reinterpret_cast<const void*>(k_verify_f32<true>)
+                                  : reinterpret_cast<const void*>(k_verify_f32<false>);
+        const int wv = resident_waves(fn, a.shared ? 25 : 24);
         if (wv == 0) return hipErrorInvalidDevice;
         // one share per resident wave: up to 16 queries per row make the waves
         // compute-heavy, unlike the single-query f32 decode
         a.n_shares = wv < a.n_tiles ? wv : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
-        hipLaunchKernelGGL(k_verify_f32, grid, block, 0, s, a);
+        void* kargs[] = {&a};
+        const hipError_t e = hipLaunchKernel(fn, grid, block, kargs, 0, s);
+        if (e != hipSuccess) return e;
     }
     int nmax = 1;
     for (int j = 0; j < a.n_seq; ++j)

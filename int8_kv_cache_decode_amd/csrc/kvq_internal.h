@@ -171,11 +171,20 @@ struct VerifyArgs {
     int32_t prefill[kSeqPerLaunch];
     int32_t ring_len[kSeqPerLaunch];
     int32_t ring_oldest[kSeqPerLaunch];      // slot of the oldest live ring token
+    // Shared-reference decode (one launch per shared group: n_seq = 1; the
+    // n_draft "drafts" are the streams, kd / vd their step rows, q / out are
+    // [n_draft][n_q_heads][128]; len = prefill + 128 n_draft + n_draft).
+    // Stream s's ring is rows prefill + 128 s ..
+    int shared;
+    float* k_store;                          // writable f32 storage for the ring writes
+    float* v_store;
+    int32_t sring[16];                       // ring slots of stream s live before its step
+    int32_t swrow[16];                       // row of the sequence that stream s's step writes
 };
 constexpr int kVerifyMaxQ = 16;
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);   // a.shared: the shared-reference decode
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s);
 

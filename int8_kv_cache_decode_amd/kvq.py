@@ -85,6 +85,9 @@ _SIGNATURES = [
                                       ctypes.c_int64, _P, _P]),
     ("rswa_verify", ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("kvq_verify_workspace_bytes", ctypes.c_size_t, [_P, ctypes.c_int, ctypes.c_int]),
+    ("rswa_shared_record_prefill", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int]),
+    ("rswa_shared_decode", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     ("kvq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -351,3 +354,18 @@ def rswa_verify(cache: KvCache, rings: Rings, n_q_heads: int, n_draft: int, q, k
     nb = ws.numel() if ws_bytes is None else ws_bytes
     _check(lib().rswa_verify(cache.ref, rings.ref, n_q_heads, n_draft, _ptr(q), _ptr(k_draft), _ptr(v_draft),
                              _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def rswa_shared_record_prefill(cache: KvCache, seq: int, rings: Rings, n_streams: int) -> None:
+    _check(lib().rswa_shared_record_prefill(cache.ref, seq, rings.ref, n_streams))
+
+
+def rswa_shared_decode(cache: KvCache, seq: int, rings: Rings, n_streams: int, n_q_heads: int, q, k_new, v_new,
+                       out, ws=None, ws_bytes=None, stream=None) -> None:
+    if ws is None:
+        import torch
+        need = kvq_verify_workspace_bytes(cache, n_q_heads, n_streams)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=out.device)
+    nb = ws.numel() if ws_bytes is None else ws_bytes
+    _check(lib().rswa_shared_decode(cache.ref, seq, rings.ref, n_streams, n_q_heads, _ptr(q), _ptr(k_new),
+                                    _ptr(v_new), _ptr(out), _ptr(ws), nb, _stream(stream)))

@@ -395,3 +395,52 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         K.lib()
+
+
+def test_shared_reference_record_and_refusals():
+    """rswa_shared_record_prefill / rswa_shared_decode refuse before any
+    launch, leaving the cache and every stream's cursors unchanged; a record
+    sets each stream's cursors and reserves its ring rows."""
+    c = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=2000)
+    rings = K.Rings(16)
+    c.len[:] = [1000, 7]
+    before = snapshot(c, rings)
+    expect(call("rswa_shared_record_prefill", c.ref, 0, rings.ref, 0), K.EINVAL, c, before, rings)
+    expect(call("rswa_shared_record_prefill", c.ref, 0, rings.ref, 17), K.EINVAL, c, before, rings)
+    expect(call("rswa_shared_record_prefill", c.ref, 2, rings.ref, 4), K.EINVAL, c, before, rings)
+    expect(call("rswa_shared_record_prefill", c.ref, 0, rings.ref, 8), K.ECAPACITY, c, before, rings)   # 1000 + 1024
+    q = fake_cache(K.KIND_Q8, batch=2, hkv=10, cap=2000)
+    bq = snapshot(q, rings)
+    expect(call("rswa_shared_record_prefill", q.ref, 0, rings.ref, 4), K.ESTATE, q, bq, rings)
+    ws = K.kvq_verify_workspace_bytes(c, 10, 4)
+    assert ws > 0 and K.kvq_verify_workspace_bytes(c, 10, 17) == 0
+    # decode before the group was recorded
+    expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None),
+           K.ESTATE, c, before, rings)
+    assert call("rswa_shared_record_prefill", c.ref, 0, rings.ref, 4) == K.OK
+    assert c.len[0] == 1000 + 4 * 128
+    assert all(rings[s].prefill_len == 1000 and rings[s].ring_len == 0 and rings[s].epoch == 1 for s in range(4))
+    assert rings[4].prefill_len == -1
+    before = snapshot(c, rings)
+    bad = [((0, rings.ref, 9, 20), K.EINVAL),          # 9 x 2 > 16
+           ((0, rings.ref, 0, 10), K.EINVAL),
+           ((3, rings.ref, 4, 10), K.EINVAL),          # seq out of range
+           ((0, rings.ref, 4, 15), K.EINVAL),          # not a multiple of 10
+           ((0, rings.ref, 3, 10), K.ESTATE),          # len != prefill + 128 x 3
+           ((0, None, 4, 10), K.EINVAL)]
+    for (seq, rr, ns, hq), code in bad:
+        expect(call("rswa_shared_decode", c.ref, seq, rr, ns, hq, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None),
+               code, c, before, rings)
+    expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 256, None),
+           K.EINVAL, c, before, rings)
+    expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, None, FAKE, FAKE, FAKE, ws, None),
+           K.EINVAL, c, before, rings)
+    c.len[0] += 1                                       # appended to since the record
+    before = snapshot(c, rings)
+    expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None),
+           K.ESTATE, c, before, rings)
+    c.len[0] -= 1
+    rings[2].ring_pos = 200                             # corrupt cursor of one stream
+    before = snapshot(c, rings)
+    expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None),
+           K.ESTATE, c, before, rings)

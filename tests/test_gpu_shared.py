@@ -1,0 +1,124 @@
+"""GPU: the shared-reference R-SWA decode ([P3] batched_decode_attention
+with streams pointing at one reference block) through the C ABI.  Each
+stream's output is compared with the oracle's decode over the reference
+rows and that stream's own live ring (the oracle's ring-cursor model per
+stream); ring rows bit for bit; the reference rows and other sequences
+untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from int8_kv_cache_decode_amd import kvq as K
+from gpu_cases import F32_TOL, THREADS, append_rows, dev, host, max_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K.lib()
+
+
+def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0):
+    """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`."""
+    r = np.random.default_rng(seed)
+    W = K.RING_WINDOW
+    pre = ref_k.shape[0]
+    alive = np.ones(hkv, np.uint8) if alive is None else alive
+    c = K.KvCache(K.KIND_F32, batch, hkv, pre + W * n_streams + 8, alive=alive)
+    other = (r.standard_normal((5, hkv, 128))).astype(np.float32)
+    for b in range(batch):
+        if b != seq:
+            append_rows(c, b, other, other)
+    if pre:
+        append_rows(c, seq, ref_k, ref_v)
+    rings = K.Rings(n_streams)
+    K.rswa_shared_record_prefill(c, seq, rings, n_streams)
+    models = []
+    for s in range(n_streams):
+        m = oracle.RingModel(W)
+        m.record_prefill(pre)
+        models.append(m)
+    hq = hkv * hpk
+    toks = []
+    out = torch.full((n_streams, hq, 128), np.nan, device="cuda")
+    worst = 0.0
+    for t in range(steps):
+        q = (r.standard_normal((n_streams, hq, 128)) * step_scale).astype(np.float32)
+        kt = (r.standard_normal((n_streams, hkv, 128)) * step_scale).astype(np.float32)
+        vt = r.standard_normal((n_streams, hkv, 128)).astype(np.float32)
+        toks.append((kt, vt))
+        K.rswa_shared_decode(c, seq, rings, n_streams, hq, dev(q), dev(kt), dev(vt), out)
+        for s in range(n_streams):
+            models[s].write(t)
+            assert rings[s].ring_len == models[s].ring_len and rings[s].ring_pos == models[s].ring_pos
+        if t in check:
+            torch.cuda.synchronize()
+            got = host(out)
+            units = []
+            for s in range(n_streams):
+                win = models[s].window()
+                kk = np.concatenate([ref_k, np.stack([toks[u][0][s] for u in win])])
+                vv = np.concatenate([ref_v, np.stack([toks[u][1][s] for u in win])])
+                units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
+                              if alive[g] else None for g in range(hkv)])
+            ref = oracle.decode(q, units, hkv, threads=THREADS)
+            err = max_err(got, ref)
+            worst = max(worst, err)
+            assert err <= F32_TOL, (t, err)
+            for g in np.flatnonzero(alive == 0):
+                assert not got[:, g * hpk:(g + 1) * hpk].any()
+    torch.cuda.synchronize()
+    kk, vv = host(c.view("k")), host(c.view("v"))
+    live = np.flatnonzero(alive)
+    assert np.array_equal(kk[seq, :, :pre], ref_k[:, live].transpose(1, 0, 2))
+    for b in range(batch):
+        if b != seq:
+            assert np.array_equal(kk[b, :, :5], other[:, live].transpose(1, 0, 2))
+    for s in range(n_streams):
+        for slot, t in enumerate(models[s].physical()):
+            assert np.array_equal(kk[seq, :, pre + W * s + slot], toks[t][0][s][live])
+            assert np.array_equal(vv[seq, :, pre + W * s + slot], toks[t][1][s][live])
+    say("  max err %.3g" % worst)
+    return rings
+
+
+def test_shared_small_gqa_dead_group_ring_wrap():
+    """Five streams x GQA group 2 (10 queries per KV head), a dead group,
+    a 700-row reference in sequence 1 of 2; 150 steps (warm-up, the ring
+    filling at 128, steady overwrite)."""
+    say("case: shared small")
+    r = np.random.default_rng(800)
+    hkv = 3
+    ref_k, ref_v = r.standard_normal((2, 700, hkv, 128)).astype(np.float32)
+    rings = shared_run(ref_k, ref_v, n_streams=5, hkv=hkv, hpk=2, steps=150, check=set(range(0, 150, 7)) | {127, 128},
+                       seed=801, alive=np.array([1, 0, 1], np.uint8))
+    assert all(rings[s].ring_len == 128 and rings[s].ring_pos == 150 % 128 for s in range(5))
+
+
+@pytest.mark.parametrize("n_streams,hpk", [(1, 1), (16, 1), (2, 8)])
+def test_shared_group_sizes_and_empty_reference(n_streams, hpk):
+    """One stream (the single-stream case), 16 streams (16 queries per KV
+    head), GQA group 8 with two streams; an empty reference block."""
+    say("case: shared streams", n_streams, "hpk", hpk)
+    r = np.random.default_rng(810 + n_streams + hpk)
+    hkv = 2
+    for pre in (0, 33):
+        ref_k, ref_v = r.standard_normal((2, pre, hkv, 128)).astype(np.float32)
+        shared_run(ref_k, ref_v, n_streams=n_streams, hkv=hkv, hpk=hpk, steps=12, check={0, 5, 11},
+                   seed=820 + pre + n_streams, seq=0, batch=1)
+
+
+@pytest.mark.timeout(600)
+def test_shared_workload_rswa_long_16_streams():
+    """The 32640-row R-SWA reference (10 MHA heads) shared by 16 streams,
+    200 steps, checked at the ring's turning points."""
+    say("case: shared rswa_long x 16 streams")
+    spec = workloads.get("rswa_long_f32")
+    rk, rv = spec.reference()
+    shared_run(rk.transpose(1, 0, 2).copy(), rv.transpose(1, 0, 2).copy(), n_streams=16, hkv=spec.n_heads, hpk=1,
+               steps=200, check={0, 127, 128, 199}, seed=830, seq=0, batch=1)
