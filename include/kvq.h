@@ -1,6 +1,7 @@
 /*
  * kvq.h -- C ABI of the MI355X (gfx950) decode-attention library over a
- * head-major f32 or int8 ("q8_2f") KV cache.
+ * head-major KV cache: f32, int8 with column fields ("q8_2f", [P1]/[P2]),
+ * or per-row int8 ([P3]'s int8 mirror).
  *
  * Sources (web pages the operations come from):
  *   [P1] cortiq-engine 0.3.4, src/cortiq_engine/kv_cache.rs
@@ -354,7 +355,10 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
 int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_draft, const float* q,
                 const float* k_draft, const float* v_draft, float* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes rswa_verify needs (0 on invalid arguments). */
+/* Workspace bytes rswa_verify needs with n_draft drafts, and rswa_shared_decode
+ * with n_draft streams: partial states for n_draft x (n_q_heads / n_kv_heads)
+ * queries per slot (at most 16), slots as kvq_workspace_bytes; 0 on invalid
+ * arguments or more than 16 queries. */
 size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft);
 
 /*
