@@ -263,44 +263,68 @@ def main():
             "us_per_call": round(us, 2), "algorithmic_bytes": nb,
             "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
             "kv_positions_per_s": round((rs.prefill + rs.window) / us * 1e6, 1)}
-        del rswa_i8
+
+        # [P3] verify_attention on the int8 mirror: 8 drafts, quantised into
+        # the workspace, checked against the i8 replicas
+        n_draft = 8
+        vq_ = t(workloads.normal_f32(workloads.key(rs.seed, 91), (1, n_draft, rs.n_heads, 128)))
+        vk_ = t(workloads.normal_f32(workloads.key(rs.seed, 92), (1, n_draft, rs.n_heads, 128)))
+        vv_ = t(workloads.normal_f32(workloads.key(rs.seed, 93), (1, n_draft, rs.n_heads, 128)))
+        vout = torch.zeros((1, n_draft, rs.n_heads, 128), device=dev)
+        vws8 = torch.empty(K.kvq_verify_workspace_bytes(rswa_i8[0][0], rs.n_heads, n_draft), dtype=torch.uint8,
+                           device=dev)
+
+        def verify_i8_call(i):
+            c, rings, _ = rswa_i8[i % len(rswa_i8)]
+            K.rswa_verify(c, rings, rs.n_heads, n_draft, vq_, vk_, vv_, vout, vws8)
+        us = time_calls(verify_i8_call, 100)
+        rows = rs.prefill + rs.window
+        nb = rows * rs.n_heads * 264 + n_draft * rs.n_heads * (512 * 4 + 264 * 2)
+        parts["rswa_verify_i8_k8"] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+            "draft_positions_per_s": round(n_draft * rows / us * 1e6, 1)}
+        del rswa_i8, vws8
 
         # prefix-shared reference ([P3] batched_decode_attention's seam): the
         # same 32640-row reference shared by 16 streams, each with its own
-        # ring, steady state; 3 replicas of 355 MB
+        # ring, steady state; 3 replicas (355 MB f32, 92 MB i8 each; the i8
+        # replicas do not all exceed the MALL together: 6 of them)
         n_str = 16
-        shared = []
         sq = t(workloads.normal_f32(workloads.key(rs.seed, 81), (n_str, rs.n_heads, 128)))
         sk = t(workloads.normal_f32(workloads.key(rs.seed, 82), (n_str, rs.n_heads, 128)))
         sv = t(workloads.normal_f32(workloads.key(rs.seed, 83), (n_str, rs.n_heads, 128)))
         sout = torch.zeros((n_str, rs.n_heads, 128), device=dev)
         rk_d = t(rk.transpose(1, 0, 2))
         rv_d = t(rv.transpose(1, 0, 2))
-        for rep in range(3):
-            c = K.KvCache(K.KIND_F32, 1, rs.n_heads, rs.prefill + rs.window * n_str)
-            rings = K.Rings(n_str)
-            K.kv_append_f32(c, 0, rs.prefill, rk_d, rv_d)
-            K.rswa_shared_record_prefill(c, 0, rings, n_str)
-            sws = torch.empty(K.kvq_verify_workspace_bytes(c, rs.n_heads, n_str), dtype=torch.uint8, device=dev)
-            for s_ in range(rs.window + 2):
-                K.rswa_shared_decode(c, 0, rings, n_str, rs.n_heads, sq, sk, sv, sout, sws)
-            shared.append((c, rings, sws))
-        del rk_d, rv_d
+        for kind, tag, nrep, row_b, app in ((K.KIND_F32, "f32", 3, 1024, K.kv_append_f32),
+                                            (K.KIND_I8, "i8", 6, 264, K.kv_append_i8)):
+            shared = []
+            for rep in range(nrep):
+                c = K.KvCache(kind, 1, rs.n_heads, rs.prefill + rs.window * n_str)
+                rings = K.Rings(n_str)
+                app(c, 0, rs.prefill, rk_d, rv_d)
+                K.rswa_shared_record_prefill(c, 0, rings, n_str)
+                sws = torch.empty(K.kvq_verify_workspace_bytes(c, rs.n_heads, n_str), dtype=torch.uint8, device=dev)
+                for s_ in range(rs.window + 2):
+                    K.rswa_shared_decode(c, 0, rings, n_str, rs.n_heads, sq, sk, sv, sout, sws)
+                shared.append((c, rings, sws))
 
-        def shared_call(i):
-            c, rings, sws = shared[i % len(shared)]
-            K.rswa_shared_decode(c, 0, rings, n_str, rs.n_heads, sq, sk, sv, sout, sws)
-        us = time_calls(shared_call, 100)
-        rows = rs.prefill + rs.window          # visible rows per stream
-        nb = (rs.prefill + n_str * rs.window) * rs.n_heads * 1024 + n_str * rs.n_heads * 512 * 2 \
-            + n_str * rs.n_heads * 512 * 2 * 2
-        flops = 4 * 128 * n_str * rs.n_heads * (rs.prefill + n_str * rs.window)
-        parts["rswa_shared_decode_f32_16_streams"] = {
-            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
-            "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
-            "mfma_TFLOPs": round(flops / us / 1e6, 2),
-            "kv_positions_per_s": round(n_str * rows / us * 1e6, 1)}
-        del shared
+            def shared_call(i, shared=shared):
+                c, rings, sws = shared[i % len(shared)]
+                K.rswa_shared_decode(c, 0, rings, n_str, rs.n_heads, sq, sk, sv, sout, sws)
+            us = time_calls(shared_call, 100)
+            rows = rs.prefill + rs.window          # visible rows per stream
+            # every stored row read once; q read and out written; the step rows
+            # read (f32) and written (f32 or codes)
+            nb = (rs.prefill + n_str * rs.window) * rs.n_heads * row_b + n_str * rs.n_heads * 512 * 2 \
+                + n_str * rs.n_heads * (1024 + 2 * row_b // 2)
+            parts["rswa_shared_decode_%s_16_streams" % tag] = {
+                "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+                "GBps": round(nb / us / 1e3, 1), "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                "kv_positions_per_s": round(n_str * rows / us * 1e6, 1)}
+            del shared
+        del rk_d, rv_d
 
         # [P3] verify_attention: 8 draft tokens checked against the same
         # replicas, nothing written; bytes as the decode (each row read once

@@ -342,6 +342,9 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
  * written (the oldest live slots evicted once it is full), and those draft
  * tokens.  Nothing is written: the cache and the ring cursors are unchanged
  * (accepting drafts is then rswa_decode, or a checkpoint / rollback).
+ * On an i8 cache (the page's int8 mirror, its decode_attention being
+ * decode_attention_int8) the drafts are quantised with quantize_row_i8 into
+ * the workspace first, and every query per head.
  *
  * q        device float [batch][n_draft][n_q_heads][128]
  * k_draft, v_draft  device float [batch][n_draft][n_kv_heads][128]
@@ -349,16 +352,17 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
  * ws/ws_bytes  device workspace of at least kvq_verify_workspace_bytes().
  * n_draft x (n_q_heads / n_kv_heads) must be within 1..16.
  * Errors: KVQ_EINVAL (null, unaligned, bad counts, workspace too small),
- * KVQ_ESTATE (not an f32 cache, a prefill not recorded, or a len that no
- * longer matches the cursors).
+ * KVQ_ESTATE (a q8 cache, a prefill not recorded, or a len that no longer
+ * matches the cursors).
  */
 int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_draft, const float* q,
                 const float* k_draft, const float* v_draft, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes rswa_verify needs with n_draft drafts, and rswa_shared_decode
  * with n_draft streams: partial states for n_draft x (n_q_heads / n_kv_heads)
- * queries per slot (at most 16), slots as kvq_workspace_bytes; 0 on invalid
- * arguments or more than 16 queries. */
+ * queries per slot (at most 16), slots as kvq_workspace_bytes, and on an i8
+ * cache the drafts' int8 mirror (batch x n_draft x n_kv_heads rows of codes
+ * and scales); 0 on invalid arguments or more than 16 queries. */
 size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft);
 
 /*
@@ -447,14 +451,14 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q,
  * reference block shared by n_streams decode streams (the prefix-shared
  * reference that [P3] batched_decode_attention leaves as a seam: streams
  * pointing at one reference block, each with its own ring).  Sequence `seq`
- * of an f32 cache holds the reference, just appended with kv_append_f32
- * (len[seq] rows); stream s's 128-slot ring is rows len[seq] + 128 s ..
+ * of an f32 or i8 cache holds the reference, just appended with
+ * kv_append_f32 / kv_append_i8 (len[seq] rows); stream s's 128-slot ring is rows len[seq] + 128 s ..
  * len[seq] + 128 s + 127 of the same sequence.  Sets, for s < n_streams,
  * rings[s] = {prefill_len = len[seq], ring_len = ring_pos = writes = 0,
  * epoch + 1} and reserves the ring rows: len[seq] += 128 n_streams.
  * rings: host array [n_streams], the group's own (not indexed by sequence).
  * Errors: KVQ_EINVAL (null, seq out of range, n_streams outside 1..16),
- * KVQ_ESTATE (not an f32 cache), KVQ_ECAPACITY (len[seq] + 128 n_streams >
+ * KVQ_ESTATE (a q8 cache), KVQ_ECAPACITY (len[seq] + 128 n_streams >
  * capacity).
  */
 int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_streams);
@@ -468,13 +472,14 @@ int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_str
  * ([P3] batched_decode_attention: per stream over its own reference ++ ring).
  * The reference rows are read once for every stream's queries: n_streams x
  * (n_q_heads / n_kv_heads) <= 16 queries per KV head share each row read, a
- * dense contraction on the matrix cores.
+ * dense contraction on the matrix cores.  On an i8 cache the step rows are
+ * quantised into the ring slots first and the decode is the int8 route.
  *
  * q, out        device float [n_streams][n_q_heads][128]
  * k_new, v_new  device float [n_streams][n_kv_heads][128]
  * ws/ws_bytes   at least kvq_verify_workspace_bytes(c, n_q_heads, n_streams).
  * Errors: KVQ_EINVAL (null, unaligned, seq out of range, n_streams x group
- * outside 1..16, workspace too small), KVQ_ESTATE (not an f32 cache, group
+ * outside 1..16, workspace too small), KVQ_ESTATE (a q8 cache, group
  * not recorded, len[seq] no longer prefill + 128 n_streams, a stream with
  * another prefill or corrupt cursors).  Nothing is written on error.
  * Checkpoint / rollback of these streams is not provided.

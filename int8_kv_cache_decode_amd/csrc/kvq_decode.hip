@@ -1076,6 +1076,196 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
     });
 }
 
+// ---------------------------------------------------------------------------
+// The query-batched kernel on the per-row int8 kind: [P3] verify_attention and
+// batched_decode_attention go through decode_attention, which with the int8
+// mirror is decode_attention_int8 -- every query quantised per head
+// (quantize_row_i8), exact i32 dots with the K codes scaled by qscale and the
+// row's K scale, V codes dequantised by the row's V scale.  Up to 16 queries
+// per KV head share each row read:
+//   scores  v_mfma_i32_16x16x64_i8, A = K codes (lane l: row l % 16 of the
+//           tile, 16 channels at 16 (l / 16) + 64 sp), B = the 16 queries'
+//           codes (lane l: query l % 16, the same channels), one MFMA per
+//           64-channel span; lane l receives rows 4 (l / 16) + r of query
+//           l % 16, scaled in f64;
+//   values  (P V)^T on v_mfma_f32_16x16x4f32 as in k_verify_f32, with the V
+//           codes converted exactly to f32 (lane l: channels 8 (l % 16) ..
+//           + 7 of rows 4 (l / 16) + s, one 8-byte load per row) and each
+//           row's V scale folded into its weight; block cb of the output
+//           holds channels 8 m + cb.
+// Verify: the draft rows come from a quantised mirror of the drafts (the
+// page writes them to a clone of the mirror before each decode).  Shared
+// decode: the step rows are already in the rings, so stream s sees the
+// reference and its live ring slots.
+// ---------------------------------------------------------------------------
+template <bool kShared>
+__global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
+    const int w = share_index();
+    if (w >= a.n_shares) return;
+    const int lane = threadIdx.x & 63;
+    const int qi = lane & 15, kb = lane >> 4;
+    for_each_piece(a, w, [&](const Piece& it) {
+        const int j = it.j;
+        const int pre = a.prefill[j];
+        const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft : pre + a.ring_len[j];
+        const size_t ob = kShared ? 0 : (size_t)it.b;
+        const int8_t* KQ = a.kq + it.hrow * kHD;
+        const float* KS = a.ks + it.hrow;
+        const int8_t* VQ = a.vq + it.hrow * kHD;
+        const float* VS = a.vs + it.hrow;
+        const size_t d0 = ob * a.n_draft * a.n_kv_heads + it.g;       // mirror row of draft 0
+        const size_t dstep = (size_t)a.n_kv_heads;
+        auto mrow = [&](int p) { return d0 + (size_t)(p - L) * dstep; };
+
+        // this lane's query (B column): draft / stream di, head hh of the group,
+        // quantised with quantize_row_i8 in f32 (amax over the 4 lanes of qi)
+        const bool qvalid = qi < a.nq;
+        const int di = qvalid ? qi / a.hpk : 0, hh = qvalid ? qi - di * a.hpk : 0;
+        v4i qa[2];
+        double qsc;
+        {
+            const float* qp = a.q + ((ob * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 16 * kb;
+            float x[2][16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4) {
+                    const float4 v = qvalid ? *(const float4*)(qp + 64 * sp + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    x[sp][4 * t4 + 0] = v.x;
+                    x[sp][4 * t4 + 1] = v.y;
+                    x[sp][4 * t4 + 2] = v.z;
+                    x[sp][4 * t4 + 3] = v.w;
+                    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                }
+            amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                v4i pk = {0, 0, 0, 0};
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const int c = (int)fminf(fmaxf(rintf(__fdiv_rn(x[sp][t], qs)), -127.0f), 127.0f);
+                    pk[t >> 2] |= (c & 0xff) << (8 * (t & 3));
+                }
+                qa[sp] = pk;
+            }
+            qsc = (double)qs * kQScale64;
+        }
+        const int rl = a.ring_len[j], old = a.ring_oldest[j];
+        const int evict = max(0, rl + di + 1 - KVQ_RING_WINDOW);
+        const int live = kShared ? a.sring[di] : 0;
+        auto visible = [&](int p) {
+            if (p < pre) return true;
+            if constexpr (kShared) {
+                return ((p - pre) >> 7) == di && ((p - pre) & (KVQ_RING_WINDOW - 1)) < live;
+            } else {
+                if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
+                return p - L <= di;
+            }
+        };
+
+        struct Tile {
+            uint4 kc[2];       // K codes of row r0 + qi, spans 0 and 1
+            float ks[4];       // K scales of rows r0 + 4 kb + r
+            uint2 vc[4];       // V codes of rows r0 + 4 kb + s, channels 8 qi ..
+            float vs[4];
+        };
+        auto load_tile = [&](int r0, Tile& t) {
+            const int pk = min(r0 + qi, it.row1 - 1);
+            const int8_t* kr = (pk < L ? KQ + (size_t)pk * kHD : a.kdq + mrow(pk) * kHD) + 16 * kb;
+            t.kc[0] = ld_stream(kr);
+            t.kc[1] = ld_stream(kr + 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = min(r0 + 4 * kb + r, it.row1 - 1);
+                if (p < L) {
+                    t.ks[r] = ld_stream1(KS + p);
+                    ld_v(VQ + (size_t)p * kHD + 8 * qi, t.vc[r]);
+                    t.vs[r] = ld_stream1(VS + p);
+                } else {
+                    const size_t m = mrow(p);
+                    t.ks[r] = a.kds[m];
+                    t.vc[r] = *(const uint2*)(a.vdq + m * kHD + 8 * qi);
+                    t.vs[r] = a.vds[m];
+                }
+            }
+        };
+        float m = -INFINITY, l = 0.0f;
+        v4f acc[8];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+        auto compute_tile = [&](int r0, const Tile& t) {
+            v4i d = {0, 0, 0, 0};
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const v4i kc = {(int)t.kc[sp].x, (int)t.kc[sp].y, (int)t.kc[sp].z, (int)t.kc[sp].w};
+                d = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qa[sp], d, 0, 0, 0);
+            }
+            double s64[4];
+            float tmax = -INFINITY;
+            bool vis[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = r0 + 4 * kb + r;
+                vis[r] = qvalid && p < it.row1 && visible(p);
+                s64[r] = (double)d[r] * (qsc * (double)t.ks[r]);
+                if (vis[r]) tmax = fmaxf(tmax, (float)s64[r]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mnew = fmaxf(m, tmax);
+            const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(m - mnew);
+            float pw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pw[r] = vis[r] ? fast_exp2((float)(s64[r] - (double)mnew)) : 0.0f;
+            l = l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+            m = mnew;
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const float pv = pw[s2] * t.vs[s2];
+                float vv[8];
+                unpack(t.vc[s2], vv);
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[cb], pv, acc[cb], 0, 0, 0);
+            }
+        };
+        int r0 = it.row0;
+        Tile ta, tb;
+        load_tile(r0, ta);
+        // ping-pong with one exit at the loop head (as in k_decode_q8)
+        while (r0 + kTileRows < it.row1) {
+            load_tile(r0 + kTileRows, tb);
+            compute_tile(r0, ta);
+            load_tile(r0 + 2 * kTileRows, ta);
+            compute_tile(r0 + kTileRows, tb);
+            r0 += 2 * kTileRows;
+        }
+        if (r0 < it.row1) compute_tile(r0, ta);
+        // the piece's partial for each valid query: lane (qi, kb) holds
+        // channels 8 (4 kb + r) + cb
+        float lt = l + __shfl_xor(l, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (qvalid) {
+            const size_t ix = (size_t)it.slot * a.nq + qi;
+            if (kb == 0) {
+                a.ws_ml[ix * 2] = m;
+                a.ws_ml[ix * 2 + 1] = lt;
+            }
+            float* dst = a.ws_acc + ix * kHD + 32 * kb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *(float4*)(dst + 8 * r) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+                *(float4*)(dst + 8 * r + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+            }
+        }
+    });
+}
+
 // Combine of the verify: block (draft i x Q head h x channel chunk, sequence).
 __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const VerifyArgs a) {
     const int chunks = (int)gridDim.x / (a.n_draft * a.n_q_heads);
@@ -1128,7 +1318,7 @@ int combine_threads(const DecodeArgs& a, int lpg) {
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
     // host threads may race to fill an entry; they all store the same value
-    static std::atomic<int> cache[kMaxDevices][26];
+    static std::atomic<int> cache[kMaxDevices][28];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     std::atomic<int>& c = cache[dev][which];
@@ -1201,13 +1391,15 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<kF32>(a, s); }
 hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kI8k>(a, s); }
 
-hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
+namespace {
+
+// The query-batched launch: the kernel, then its combine.  which: the
+// resident-wave cache entry of the kernel.
+hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int which, hipStream_t s) {
     VerifyArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {                          // zero only when every group is dead
-        const void* fn = a.shared ? reinterpret_cast<const void*>(k_verify_f32<true>)
-                                  : reinterpret_cast<const void*>(k_verify_f32<false>);
-        const int wv = resident_waves(fn, a.shared ? 25 : 24);
+        const int wv = resident_waves(fn, which);
         if (wv == 0) return hipErrorInvalidDevice;
         // one share per resident wave: up to 16 queries per row make the waves
         // compute-heavy, unlike the single-query f32 decode
@@ -1234,6 +1426,19 @@ hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
                        a);
     return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, s);
+}
+
+hipError_t launch_verify_i8(const VerifyArgs& a, hipStream_t s) {
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, s);
+}
+
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kQ8k>(a, s); }
 
 }  // namespace kvq

@@ -411,7 +411,7 @@ class RingModel:
 # --------------------------------------------------------------------------
 # Query-batched verify ([P3] verify_attention)
 # --------------------------------------------------------------------------
-def rswa_verify(q, ref_k, ref_v, history_k, history_v, draft_k, draft_v, window: int = RING_W):
+def rswa_verify(q, ref_k, ref_v, history_k, history_v, draft_k, draft_v, window: int = RING_W, kind: str = "f32"):
     """K-token verify by definition: draft query i attends, with no mask, to
     the reference rows plus the ring as it would stand after the draft
     tokens 0..i were written in order -- the last min(window, n + i + 1)
@@ -423,6 +423,9 @@ def rswa_verify(q, ref_k, ref_v, history_k, history_v, draft_k, draft_v, window:
     history  [Hkv][n][hd] f32: every ring token written since the prefill,
              oldest first (only the last `window` are live)
     draft    [K][Hkv][hd] f32
+    kind     "f32", or "i8": the int8 mirror -- every row through
+             quantize_row_i8 and the decode is decode_attention_int8 (the
+             page's decode_attention with its int8 switch on)
     Returns out [K][Hq][hd] float64."""
     q = _f32(q)
     K_, Hq, hd = q.shape
@@ -435,7 +438,13 @@ def rswa_verify(q, ref_k, ref_v, history_k, history_v, draft_k, draft_v, window:
             toks_v = np.concatenate([history_v[g], draft_v[: i + 1, g]])
             rows_k = np.concatenate([ref_k[g], toks_k[-window:]])
             rows_v = np.concatenate([ref_v[g], toks_v[-window:]])
-            out[i, g * hpk:(g + 1) * hpk] = attend_f32(q[i, g * hpk:(g + 1) * hpk], rows_k, rows_v)
+            qg = q[i, g * hpk:(g + 1) * hpk]
+            if kind == "i8":
+                h = I8Head(cap=max(rows_k.shape[0], 1))
+                h.append(rows_k, rows_v)
+                out[i, g * hpk:(g + 1) * hpk] = attend_i8(qg, h)
+            else:
+                out[i, g * hpk:(g + 1) * hpk] = attend_f32(qg, rows_k, rows_v)
     return out
 
 

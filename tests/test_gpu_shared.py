@@ -23,13 +23,22 @@ def _gpu():
     K.lib()
 
 
-def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0):
-    """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`."""
+def i8_head(k, v):
+    h = oracle.I8Head(cap=max(k.shape[0], 1))
+    if k.shape[0]:
+        h.append(k, v)
+    return h
+
+
+def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0,
+               kind=K.KIND_F32):
+    """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`;
+    kind KIND_I8: the int8 mirror (oracle: its codec and int8 decode)."""
     r = np.random.default_rng(seed)
     W = K.RING_WINDOW
     pre = ref_k.shape[0]
     alive = np.ones(hkv, np.uint8) if alive is None else alive
-    c = K.KvCache(K.KIND_F32, batch, hkv, pre + W * n_streams + 8, alive=alive)
+    c = K.KvCache(kind, batch, hkv, pre + W * n_streams + 8, alive=alive)
     other = (r.standard_normal((5, hkv, 128))).astype(np.float32)
     for b in range(batch):
         if b != seq:
@@ -64,8 +73,11 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
                 win = models[s].window()
                 kk = np.concatenate([ref_k, np.stack([toks[u][0][s] for u in win])])
                 vv = np.concatenate([ref_v, np.stack([toks[u][1][s] for u in win])])
-                units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
-                              if alive[g] else None for g in range(hkv)])
+                if kind == K.KIND_I8:
+                    units.append([("i8", i8_head(kk[:, g], vv[:, g])) if alive[g] else None for g in range(hkv)])
+                else:
+                    units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
+                                  if alive[g] else None for g in range(hkv)])
             ref = oracle.decode(q, units, hkv, threads=THREADS)
             err = max_err(got, ref)
             worst = max(worst, err)
@@ -73,8 +85,25 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
             for g in np.flatnonzero(alive == 0):
                 assert not got[:, g * hpk:(g + 1) * hpk].any()
     torch.cuda.synchronize()
-    kk, vv = host(c.view("k")), host(c.view("v"))
     live = np.flatnonzero(alive)
+    if kind == K.KIND_I8:
+        kq, ks, vq, vs = (host(c.view(nm)) for nm in ("kq", "ks", "vq", "vs"))
+        for sl, g in enumerate(live):
+            rows_k = np.concatenate([ref_k[:, g]] + [toks[t][0][s][g][None] for s in range(n_streams)
+                                                     for t in models[s].physical()])
+            rows_v = np.concatenate([ref_v[:, g]] + [toks[t][1][s][g][None] for s in range(n_streams)
+                                                     for t in models[s].physical()])
+            h = i8_head(rows_k, rows_v)
+            # storage order: reference, then each stream's ring slots in order
+            idx = list(range(pre)) + [pre + W * s + slot for s in range(n_streams)
+                                      for slot in range(len(models[s].physical()))]
+            n = len(idx)
+            assert np.array_equal(kq[seq, sl, idx], h.kq[:n]) and np.array_equal(vq[seq, sl, idx], h.vq[:n])
+            assert np.array_equal(ks[seq, sl, idx].view(np.uint32), h.ks[:n].view(np.uint32))
+            assert np.array_equal(vs[seq, sl, idx].view(np.uint32), h.vs[:n].view(np.uint32))
+        say("  max err %.3g" % worst)
+        return rings
+    kk, vv = host(c.view("k")), host(c.view("v"))
     assert np.array_equal(kk[seq, :, :pre], ref_k[:, live].transpose(1, 0, 2))
     for b in range(batch):
         if b != seq:
@@ -87,21 +116,23 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
     return rings
 
 
-def test_shared_small_gqa_dead_group_ring_wrap():
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_shared_small_gqa_dead_group_ring_wrap(kind):
     """Five streams x GQA group 2 (10 queries per KV head), a dead group,
     a 700-row reference in sequence 1 of 2; 150 steps (warm-up, the ring
     filling at 128, steady overwrite)."""
-    say("case: shared small")
+    say("case: shared small kind", kind)
     r = np.random.default_rng(800)
     hkv = 3
     ref_k, ref_v = r.standard_normal((2, 700, hkv, 128)).astype(np.float32)
     rings = shared_run(ref_k, ref_v, n_streams=5, hkv=hkv, hpk=2, steps=150, check=set(range(0, 150, 7)) | {127, 128},
-                       seed=801, alive=np.array([1, 0, 1], np.uint8))
+                       seed=801, alive=np.array([1, 0, 1], np.uint8), kind=kind)
     assert all(rings[s].ring_len == 128 and rings[s].ring_pos == 150 % 128 for s in range(5))
 
 
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
 @pytest.mark.parametrize("n_streams,hpk", [(1, 1), (16, 1), (2, 8)])
-def test_shared_group_sizes_and_empty_reference(n_streams, hpk):
+def test_shared_group_sizes_and_empty_reference(n_streams, hpk, kind):
     """One stream (the single-stream case), 16 streams (16 queries per KV
     head), GQA group 8 with two streams; an empty reference block."""
     say("case: shared streams", n_streams, "hpk", hpk)
@@ -110,15 +141,16 @@ def test_shared_group_sizes_and_empty_reference(n_streams, hpk):
     for pre in (0, 33):
         ref_k, ref_v = r.standard_normal((2, pre, hkv, 128)).astype(np.float32)
         shared_run(ref_k, ref_v, n_streams=n_streams, hkv=hkv, hpk=hpk, steps=12, check={0, 5, 11},
-                   seed=820 + pre + n_streams, seq=0, batch=1)
+                   seed=820 + pre + n_streams, seq=0, batch=1, kind=kind)
 
 
 @pytest.mark.timeout(600)
-def test_shared_workload_rswa_long_16_streams():
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_shared_workload_rswa_long_16_streams(kind):
     """The 32640-row R-SWA reference (10 MHA heads) shared by 16 streams,
     200 steps, checked at the ring's turning points."""
-    say("case: shared rswa_long x 16 streams")
+    say("case: shared rswa_long x 16 streams kind", kind)
     spec = workloads.get("rswa_long_f32")
     rk, rv = spec.reference()
     shared_run(rk.transpose(1, 0, 2).copy(), rv.transpose(1, 0, 2).copy(), n_streams=16, hkv=spec.n_heads, hpk=1,
-               steps=200, check={0, 127, 128, 199}, seed=830, seq=0, batch=1)
+               steps=200, check={0, 127, 128, 199}, seed=830, seq=0, batch=1, kind=kind)

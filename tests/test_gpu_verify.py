@@ -25,10 +25,13 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
-def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed):
+BUFS = {K.KIND_F32: ("k", "v"), K.KIND_I8: ("kq", "ks", "vq", "vs")}
+
+
+def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32):
     r = rng(seed)
     W = K.RING_WINDOW
-    c = K.KvCache(K.KIND_F32, batch, hkv, prefill + W)
+    c = K.KvCache(kind, batch, hkv, prefill + W)
     rings = K.Rings(batch)
     hq = hkv * hpk
     ref = [(r.standard_normal((prefill, hkv, 128)).astype(np.float32),
@@ -44,7 +47,7 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed):
     for t in range(n_hist):
         K.rswa_decode(c, rings, hq, q1, dev(hist_k[t]), dev(hist_v[t]), out1)
     torch.cuda.synchronize()
-    before = (host(c.view("k")).copy(), host(c.view("v")).copy(), bytes(rings.arr), c.len.copy())
+    before = ([host(c.view(nm)).copy() for nm in BUFS[kind]], bytes(rings.arr), c.len.copy())
     q = r.standard_normal((batch, n_draft, hq, 128)).astype(np.float32)
     dk = r.standard_normal((batch, n_draft, hkv, 128)).astype(np.float32)
     dv = r.standard_normal((batch, n_draft, hkv, 128)).astype(np.float32)
@@ -55,20 +58,23 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed):
     torch.cuda.synchronize()
     got = host(out)
     assert np.array_equal(got.view(np.uint32), host(out2).view(np.uint32)), "verify is not deterministic"
-    assert np.array_equal(host(c.view("k")), before[0]) and np.array_equal(host(c.view("v")), before[1])
-    assert bytes(rings.arr) == before[2] and np.array_equal(c.len, before[3])
+    for nm, b0 in zip(BUFS[kind], before[0]):
+        assert np.array_equal(host(c.view(nm)).view(np.uint8), b0.view(np.uint8)), nm
+    assert bytes(rings.arr) == before[1] and np.array_equal(c.len, before[2])
     err = 0.0
     for b in range(batch):
         ref_k = np.ascontiguousarray(ref[b][0].transpose(1, 0, 2))
         ref_v = np.ascontiguousarray(ref[b][1].transpose(1, 0, 2))
         hk = np.ascontiguousarray(hist_k[:, b].transpose(1, 0, 2))
         hv = np.ascontiguousarray(hist_v[:, b].transpose(1, 0, 2))
-        want = oracle.rswa_verify(q[b], ref_k, ref_v, hk, hv, dk[b], dv[b], W)
+        want = oracle.rswa_verify(q[b], ref_k, ref_v, hk, hv, dk[b], dv[b], W,
+                                  kind="i8" if kind == K.KIND_I8 else "f32")
         err = max(err, max_err(got[b], want))
     say("  max err %.3g" % err)
     assert err <= F32_TOL, err
 
 
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
 @pytest.mark.parametrize("hkv,hpk,prefill,n_hist,n_draft", [
     (2, 1, 7, 5, 4),        # warm-up
     (2, 1, 300, 126, 5),    # the drafts fill the ring and evict
@@ -77,19 +83,20 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed):
     (2, 1, 65, 128, 16),    # ring exactly full, 16 drafts
     (2, 4, 33, 70, 2),      # GQA groups of 4
 ])
-def test_verify_matches_sequential_definition(hkv, hpk, prefill, n_hist, n_draft):
-    say("case: verify hkv", hkv, "hpk", hpk, "prefill", prefill, "hist", n_hist, "drafts", n_draft)
-    run_verify(2, hkv, hpk, prefill, n_hist, n_draft, seed=500 + prefill + n_hist + n_draft)
+def test_verify_matches_sequential_definition(hkv, hpk, prefill, n_hist, n_draft, kind):
+    say("case: verify kind", kind, "hkv", hkv, "hpk", hpk, "prefill", prefill, "hist", n_hist, "drafts", n_draft)
+    run_verify(2, hkv, hpk, prefill, n_hist, n_draft, seed=500 + prefill + n_hist + n_draft, kind=kind)
 
 
-def test_verify_long_reference():
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_verify_long_reference(kind):
     """rswa_long_f32's shape: 10 heads, 32640 reference rows, ring full
     after 500 writes, 8 drafts."""
-    say("case: verify long reference")
+    say("case: verify long reference kind", kind)
     spec = workloads.get("rswa_long_f32")
     r = rng(600)
     W = spec.window
-    c = K.KvCache(K.KIND_F32, 1, spec.n_heads, spec.prefill + W)
+    c = K.KvCache(kind, 1, spec.n_heads, spec.prefill + W)
     rings = K.Rings(1)
     rk, rv = spec.reference()
     append_rows(c, 0, rk.transpose(1, 0, 2), rv.transpose(1, 0, 2))
@@ -107,7 +114,7 @@ def test_verify_long_reference():
     torch.cuda.synchronize()
     hk = np.stack([s[1] for s in steps], axis=1)
     hv = np.stack([s[2] for s in steps], axis=1)
-    want = oracle.rswa_verify(q[0], rk, rv, hk, hv, dk[0], dv[0], W)
+    want = oracle.rswa_verify(q[0], rk, rv, hk, hv, dk[0], dv[0], W, kind="i8" if kind == K.KIND_I8 else "f32")
     err = max_err(host(out)[0], want)
     say("  max err %.3g" % err)
     assert err <= F32_TOL, err

@@ -857,6 +857,46 @@ def test_verify_equals_sequential_ring_steps(prefill, n_hist, K):
     assert np.array_equal(got2[:-1], got[:-1]) and not np.array_equal(got2[-1], got[-1])
 
 
+@pytest.mark.parametrize("prefill,n_hist,K", [(7, 5, 4), (7, 126, 5), (3, 300, 6), (0, 0, 3)])
+def test_verify_i8_equals_sequential_int8_decodes(prefill, n_hist, K):
+    """The verify on the int8 mirror: draft i's context is the i-th of K
+    sequential steps on the mirror -- each row quantised once as it is
+    written (quantize_row_i8, a row's codes do not depend on the others) and
+    decode_attention_int8 over the physical ring of a RingModel."""
+    r = rng(4100 + prefill + n_hist + K)
+    hkv, hpk, W = 2, 2, oracle.RING_W
+    ref_k = (r.standard_normal((hkv, prefill, HD)) * 2).astype(np.float32)
+    ref_v = r.standard_normal((hkv, prefill, HD)).astype(np.float32)
+    hist_k = (r.standard_normal((hkv, n_hist, HD)) * 2).astype(np.float32)
+    hist_v = r.standard_normal((hkv, n_hist, HD)).astype(np.float32)
+    dk = (r.standard_normal((K, hkv, HD)) * 2).astype(np.float32)
+    dv = r.standard_normal((K, hkv, HD)).astype(np.float32)
+    q = r.standard_normal((K, hkv * hpk, HD)).astype(np.float32)
+    got = oracle.rswa_verify(q, ref_k, ref_v, hist_k, hist_v, dk, dv, kind="i8")
+    m = oracle.RingModel(W)
+    m.record_prefill(prefill)
+    codes = {g: {} for g in range(hkv)}               # slot -> (kq, ks, vq, vs)
+    for t in range(n_hist + K):
+        s_ = m.write(t)
+        for g in range(hkv):
+            kx = hist_k[g, t] if t < n_hist else dk[t - n_hist, g]
+            vx = hist_v[g, t] if t < n_hist else dv[t - n_hist, g]
+            codes[g][s_] = oracle.quant_row_i8(kx) + oracle.quant_row_i8(vx)
+        if t < n_hist:
+            continue
+        i = t - n_hist
+        for g in range(hkv):
+            h = oracle.I8Head(cap=prefill + m.ring_len + 1)
+            if prefill:
+                h.append(ref_k[g], ref_v[g])
+            for slot in range(m.ring_len):
+                kq, ks, vq, vs = codes[g][slot]
+                h.kq[h.n], h.ks[h.n], h.vq[h.n], h.vs[h.n] = kq, ks, vq, vs
+                h.n += 1
+            want = oracle.attend_i8(q[i, g * hpk:(g + 1) * hpk], h)
+            np.testing.assert_allclose(got[i, g * hpk:(g + 1) * hpk], want, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # Per-row int8 route ([P3] quantize_row_i8, decode_attention_int8)
 # ---------------------------------------------------------------------------
