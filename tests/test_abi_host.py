@@ -444,3 +444,25 @@ def test_shared_reference_record_and_refusals():
     before = snapshot(c, rings)
     expect(call("rswa_shared_decode", c.ref, 0, rings.ref, 4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None),
            K.ESTATE, c, before, rings)
+
+
+def test_int8_verify_workspace_holds_the_draft_mirror():
+    """On the per-row int8 kind the verify workspace also holds the drafts'
+    int8 mirror (batch x drafts x KV heads rows of 2 x (128 codes + a
+    scale)); a workspace sized for the f32 kind is refused untouched."""
+    f = fake_cache(K.KIND_F32, batch=3, hkv=4, cap=300)
+    i = fake_cache(K.KIND_I8, batch=3, hkv=4, cap=300)
+    wf, wi = K.kvq_verify_workspace_bytes(f, 8, 5), K.kvq_verify_workspace_bytes(i, 8, 5)
+    mirror = 3 * 5 * 4 * 2 * (128 + 4)
+    assert wi - wf == (mirror + 255) // 256 * 256
+    rings = K.Rings(3)
+    for b in range(3):
+        i.len[b] = 10
+        assert call("rswa_record_prefill", i.ref, rings.ref, b) == K.OK
+    before = snapshot(i, rings)
+    expect(call("rswa_verify", i.ref, rings.ref, 8, 5, FAKE, FAKE, FAKE, FAKE, FAKE, wf, None), K.EINVAL,
+           i, before, rings)
+    q = fake_cache(K.KIND_Q8, batch=3, hkv=4, cap=300)
+    bq = snapshot(q, rings)
+    expect(call("rswa_verify", q.ref, rings.ref, 8, 5, FAKE, FAKE, FAKE, FAKE, FAKE, wi, None), K.ESTATE,
+           q, bq, rings)
