@@ -64,10 +64,12 @@ extern "C" {
 /* Device buffers of a cache, for kvq_buffer_bytes(). */
 #define KVQ_BUF_K     0   /* f32:  float [batch][n_live][capacity][128]            */
 #define KVQ_BUF_V     1   /* f32:  float [batch][n_live][capacity][128]            */
-#define KVQ_BUF_KQ    2   /* q8:   int8  [batch][n_live][capacity][128] (16 B rows) */
+#define KVQ_BUF_KQ    2   /* q8, i8: int8 [batch][n_live][capacity16 / 16][2][4][16][16],
+                             tile-major (below); capacity16 = capacity rounded up
+                             to a multiple of 16                             */
 #define KVQ_BUF_KS    3   /* q8:   float [batch][n_live][capacity][4]  (one 16 B record per row);
                              i8:   float [batch][n_live][capacity]                 */
-#define KVQ_BUF_VQ    4   /* q8:   int8  [batch][n_live][capacity][128]            */
+#define KVQ_BUF_VQ    4   /* q8, i8: int8 [batch][n_live][capacity][128]           */
 #define KVQ_BUF_VS    5   /* q8, i8: float [batch][n_live][capacity]              */
 #define KVQ_BUF_KCOL  6   /* q8:   float [batch][n_live][128]                      */
 #define KVQ_BUF_VCOL  7   /* q8:   float [batch][n_live][128]                      */
@@ -93,6 +95,11 @@ extern "C" {
  * i8 kind ([P3] Int8Kv, the per-row int8 route): K and V rows as int8 codes
  * with one f32 scale per row each (kq, ks, vq, vs; KVQ_BUF_KQ/VQ as for q8),
  *   K^[p][d] = kq[p][d] * ks[p],  V^[p][d] = vq[p][d] * vs[p].
+ * K codes (both int8 kinds) are stored tile-major, in the order the matrix
+ * cores read them: kq[p][d] of a (sequence, live head) is the byte at
+ *   (p / 16) * 2048 + (d / 64) * 1024 + ((d / 16) % 4) * 256 + (p % 16) * 16
+ *   + d % 16
+ * of its capacity16 * 128-byte block; every other buffer is row-major.
  *
  * Fill it with kvq_cache_init(), then set the device pointers of the kind's
  * buffers (sizes from kvq_buffer_bytes(); every base must be 16-byte

@@ -283,8 +283,11 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
             // [P2] attend_group_upto: first clamped so that one row stays visible
             const int f = (opts && opts->first && L > 0) ? std::min(opts->first[s0 + j], L - 1) : 0;
             a.len[j] = L;
+            // int8 kinds: the tile stream starts on a K tile boundary
+            const int st = c->kind == KVQ_KIND_F32 ? f : f & ~(kTileRows - 1);
             a.first[j] = f;
-            a.ntile[j] = (L - f + kTileRows - 1) / kTileRows;
+            a.start[j] = st;
+            a.ntile[j] = (L - st + kTileRows - 1) / kTileRows;
             a.wrow[j] = wrows ? wrows[s0 + j] : -1;
             a.frozen[j] = c->frozen[s0 + j] ? 1 : 0;
             a.tile_base[j] = (int32_t)tiles;
@@ -348,7 +351,7 @@ size_t kvq_buffer_bytes(const kvq_cache* c, int which) {
     switch (which) {
         case KVQ_BUF_K:
         case KVQ_BUF_V: return f32 ? rows * kHD * sizeof(float) : 0;
-        case KVQ_BUF_KQ:
+        case KVQ_BUF_KQ: return (q8 || i8) ? heads * (size_t)kq_rows(c->capacity) * kHD : 0;   // tile-major
         case KVQ_BUF_VQ: return (q8 || i8) ? rows * kHD : 0;
         case KVQ_BUF_KS: return q8 ? rows * kKScales * sizeof(float) : i8 ? rows * sizeof(float) : 0;
         case KVQ_BUF_VS: return (q8 || i8) ? rows * sizeof(float) : 0;

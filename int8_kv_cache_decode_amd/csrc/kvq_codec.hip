@@ -70,7 +70,11 @@ __global__ __launch_bounds__(128) void k_append_q8(const AppendArgs a) {
     char2 c;
     c.x = quant_code(r0, s);
     c.y = quant_code(r1, s);
-    *(char2*)((is_k ? a.kq : a.vq) + hrow * kHD + 2 * lane) = c;
+    if (is_k)
+        *(char2*)(a.kq + ((size_t)a.seq[j] * a.n_live + gl) * kq_rows(a.capacity) * kHD +
+                  kq_offset(a.dst_row0[j] + r, 2 * lane)) = c;
+    else
+        *(char2*)(a.vq + hrow * kHD + 2 * lane) = c;
     if (is_k) {
         if ((lane & 15) == 0) a.ks[hrow * kKScales + (lane >> 4)] = s;
     } else {
@@ -96,7 +100,11 @@ __global__ __launch_bounds__(128) void k_append_i8(const AppendArgs a) {
     char2 c;
     c.x = (int8_t)(int)c0;
     c.y = (int8_t)(int)c1;
-    *(char2*)((is_k ? a.kq : a.vq) + hrow * kHD + 2 * lane) = c;
+    if (is_k)
+        *(char2*)(a.kq + ((size_t)a.seq[j] * a.n_live + gl) * kq_rows(a.capacity) * kHD +
+                  kq_offset(a.dst_row0[j] + r, 2 * lane)) = c;
+    else
+        *(char2*)(a.vq + hrow * kHD + 2 * lane) = c;
     if (lane == 0) (is_k ? a.ks : a.vs)[hrow] = s;
 }
 
@@ -130,21 +138,21 @@ __global__ __launch_bounds__(128) void k_freeze(const FreezeArgs a) {
 
     // ---- K: group of 32 channels, scale per (row, group) ----
     {
-        int8_t* q = a.kq + row0 * kHD;
+        int8_t* q = a.kq + head * kq_rows(a.capacity) * kHD;    // tile-major K codes
         float* s = a.ks + row0 * kKScales;
         float acc = 0.0f;
         for (int p = 0; p < n; ++p) {
-            const float x = (float)q[(size_t)p * kHD + d] * s[(size_t)p * kKScales + d / kKGroup];
+            const float x = (float)q[kq_offset(p, d)] * s[(size_t)p * kKScales + d / kKGroup];
             const float sq = x * x;
             acc = acc + sq;
         }
         const float col = fmaxf(sqrtf(__fdiv_rn(acc, (float)n)), 1e-6f);
         a.kcol[head * kHD + d] = col;
         for (int p = 0; p < n; ++p) {
-            const float x = (float)q[(size_t)p * kHD + d] * s[(size_t)p * kKScales + d / kKGroup];
+            const float x = (float)q[kq_offset(p, d)] * s[(size_t)p * kKScales + d / kKGroup];
             const float r = __fdiv_rn(x, col);
             const float sc = group_scale(group_max<32>(fabsf(r)));
-            q[(size_t)p * kHD + d] = quant_code(r, sc);
+            q[kq_offset(p, d)] = quant_code(r, sc);
             if ((d & (kKGroup - 1)) == 0) s[(size_t)p * kKScales + d / kKGroup] = sc;
         }
     }
@@ -189,12 +197,29 @@ __device__ __forceinline__ void copy_rows(T* base, int units_per_row, int src, i
         d[i] = s[i];
 }
 
+// K codes, tile-major: threads walk the destination's 16-byte pieces (row,
+// 16 channels) in storage order over the 16-row tiles that hold rows
+// [dst, dst + m), so a wave writes 1 KB runs; pieces of rows outside the
+// range are skipped.  Each piece comes from the source row at the same
+// offset in [src, src + m).
+__device__ __forceinline__ void copy_kq_rows(int8_t* base, int src, int dst, int m) {
+    const int db = dst & ~(kTileRows - 1);
+    const size_t n = (size_t)((dst + m - db + kTileRows - 1) / kTileRows) * (kTileRows * kHD / 16);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const int r = db + kTileRows * (int)(i >> 7) + (int)(i & 15);
+        const int c = 16 * (int)((i >> 4) & 7);
+        if (r < dst || r >= dst + m) continue;
+        *(uint4*)(base + kq_offset(r, c)) = *(const uint4*)(base + kq_offset(r - dst + src, c));
+    }
+}
+
 __global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, int dst, int m) {
-    const size_t row0 = ((size_t)a.seq * a.n_live + blockIdx.y) * a.capacity;
+    const size_t head = (size_t)a.seq * a.n_live + blockIdx.y;
+    const size_t row0 = head * a.capacity;
     const int z = blockIdx.z;
     const int which = a.kind == KVQ_KIND_F32 ? 4 + z : (a.kind == KVQ_KIND_I8 && z == 1) ? 6 : z;
     switch (which) {
-        case 0: copy_rows(reinterpret_cast<uint4*>(a.kq + row0 * kHD), kHD / 16, src, dst, m); break;
+        case 0: copy_kq_rows(a.kq + head * kq_rows(a.capacity) * kHD, src, dst, m); break;
         case 1: copy_rows(reinterpret_cast<uint4*>(a.ks + row0 * kKScales), 1, src, dst, m); break;
         case 2: copy_rows(reinterpret_cast<uint4*>(a.vq + row0 * kHD), kHD / 16, src, dst, m); break;
         case 3: copy_rows(reinterpret_cast<uint32_t*>(a.vs + row0), 1, src, dst, m); break;

@@ -64,18 +64,24 @@ __host__ __device__ inline int tile_owner(int t, int T, int W) {
 }
 
 // The part of one share that lies in one (sequence, live head) segment.
-// A segment's tiles start at the sequence's first visible row.
+// A segment's tiles start at its stream start (the first visible row, or for
+// the int8 kinds the 16-row boundary at or below it); rows below the first
+// visible one are masked.
 struct Piece {
     int j, gl, b, g;
     int row0, row1;  // rows of the segment, [row0, row1)
+    int lo;          // first visible row of the segment
     int slot;        // partial slot: share + segment index
     size_t hrow;     // first storage row of the (sequence, live head)
+    size_t hidx;     // index of the (sequence, live head): b * n_live + gl
 };
 
-// First row of a segment's tile stream: the visible-row start of a decode,
-// row 0 of a verify.
-__device__ __forceinline__ int seg_first(const DecodeArgs& a, int j) { return a.first[j]; }
+// First row of a segment's tile stream and its first visible row: a
+// decode's stream start and visible-row start, row 0 for a verify.
+__device__ __forceinline__ int seg_first(const DecodeArgs& a, int j) { return a.start[j]; }
 __device__ __forceinline__ int seg_first(const VerifyArgs&, int) { return 0; }
+__device__ __forceinline__ int seg_lo(const DecodeArgs& a, int j) { return a.first[j]; }
+__device__ __forceinline__ int seg_lo(const VerifyArgs&, int) { return 0; }
 
 // Calls f(piece) for each piece of share w, in stream order.
 template <class Args, class F>
@@ -102,8 +108,10 @@ __device__ __forceinline__ void for_each_piece(const Args& a, int w, F&& f) {
         p.g = a.live_head[gl];
         p.row0 = seg_first(a, j) + kTileRows * (t - sb);
         p.row1 = min(seg_first(a, j) + kTileRows * (pe - sb), a.len[j]);
+        p.lo = seg_lo(a, j);
         p.slot = w + j * a.n_live + gl;
-        p.hrow = ((size_t)p.b * a.n_live + gl) * a.capacity;
+        p.hidx = (size_t)p.b * a.n_live + gl;
+        p.hrow = p.hidx * a.capacity;
         f(p);
         t = pe;
         if (t < t1 && ++gl == a.n_live) {   // next segment with tiles
@@ -384,7 +392,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     const int hq = lane >> 4, n = lane & 15;          // score layout
     const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
     for_each_piece(a, w, [&](const Piece& it) {
-        const int8_t* KQ = a.kq + it.hrow * kHD;
+        const int8_t* KQ = a.kq + it.hidx * kq_rows(a.capacity) * kHD;   // tile-major K codes
         const float* KS = a.ks + it.hrow * (kI8 ? 1 : kKScales);
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
                 const size_t row = it.hrow + (size_t)wl;
                 *(char2*)(&sm_ring[wave][0][2 * lane]) = ck;
                 *(char2*)(&sm_ring[wave][1][2 * lane]) = cv;
-                *(char2*)(a.kq_store + row * kHD + 2 * lane) = ck;
+                *(char2*)(a.kq_store + it.hidx * kq_rows(a.capacity) * kHD + kq_offset(wl, 2 * lane)) = ck;
                 *(char2*)(a.vq_store + row * kHD + 2 * lane) = cv;
                 if (lane == 0) {
                     sm_ring_s[wave][0] = sk;
@@ -444,7 +452,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         auto load_tile = [&](int r0, Tile& t) {
             const uint32_t rk = (uint32_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
-            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + (rk * kHD + 64 * sp + 16 * (lane >> 4)));
+            for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + kq_offset((int)rk, 64 * sp + 16 * (lane >> 4)));
             if constexpr (kI8)
                 t.ks4.x = ld_stream1(KS + rk);
             else
@@ -635,7 +643,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
                     }
                 }
             }
-            const bool valid = r0 + n < it.row1;
+            const bool valid = r0 + n >= it.lo && r0 + n < it.row1;
             // ---- scores (exact), softmax weights in the (head, row) layout ----
             bool rescale = false;
 #pragma unroll
@@ -1109,7 +1117,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         const int pre = a.prefill[j];
         const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft : pre + a.ring_len[j];
         const size_t ob = kShared ? 0 : (size_t)it.b;
-        const int8_t* KQ = a.kq + it.hrow * kHD;
+        const int8_t* KQ = a.kq + it.hidx * kq_rows(a.capacity) * kHD;   // tile-major K codes
         const float* KS = a.ks + it.hrow;
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
@@ -1174,9 +1182,14 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         };
         auto load_tile = [&](int r0, Tile& t) {
             const int pk = min(r0 + qi, it.row1 - 1);
-            const int8_t* kr = (pk < L ? KQ + (size_t)pk * kHD : a.kdq + mrow(pk) * kHD) + 16 * kb;
-            t.kc[0] = ld_stream(kr);
-            t.kc[1] = ld_stream(kr + 64);
+            if (pk < L) {
+                t.kc[0] = ld_stream(KQ + kq_offset(pk, 16 * kb));
+                t.kc[1] = ld_stream(KQ + kq_offset(pk, 64 + 16 * kb));
+            } else {                                     // the drafts' mirror is row-major
+                const int8_t* kr = a.kdq + mrow(pk) * kHD + 16 * kb;
+                t.kc[0] = *(const uint4*)kr;
+                t.kc[1] = *(const uint4*)(kr + 64);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int p = min(r0 + 4 * kb + r, it.row1 - 1);

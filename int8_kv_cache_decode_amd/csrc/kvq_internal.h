@@ -31,6 +31,19 @@ constexpr int kSeqPerLaunch = 128;
 constexpr int kTileRows = 16;
 constexpr int kMaxWaves = 8192;
 
+// K codes of the int8 kinds are stored tile-major, in the order the matrix
+// cores read them: the rows of a (sequence, live head) form 16-row tiles of
+// 2 KB, and within a tile the 16-byte piece (row n, channels 16 c .. 16 c +
+// 15) sits at (c / 4) * 1024 + (c % 4) * 256 + n * 16.  One MFMA operand
+// load of a tile (64 lanes x 16 bytes: lane 16 (c % 4) + n) is then 1 KB of
+// whole lines.  A (sequence, live head) holds kq_rows(capacity) rows: the
+// capacity rounded up to whole tiles.  The other buffers stay row-major.
+__host__ __device__ inline int kq_rows(int capacity) { return (capacity + kTileRows - 1) & ~(kTileRows - 1); }
+__host__ __device__ inline uint32_t kq_offset(int row, int ch) {
+    return (uint32_t)(row >> 4) * 2048u + (uint32_t)(ch >> 6) * 1024u + (uint32_t)((ch >> 4) & 3) * 256u +
+           (uint32_t)(row & 15) * 16u + (uint32_t)(ch & 15);
+}
+
 // ---- codec ---------------------------------------------------------------
 struct AppendArgs {
     const float* k_new;        // source rows [src_row][n_kv_heads][128]
@@ -130,8 +143,10 @@ struct DecodeArgs {
     int8_t live_head[KVQ_MAX_KV_HEADS];      // KV head of live slot
     int8_t live_slot[KVQ_MAX_KV_HEADS];      // live slot of KV head, -1 dead
     int32_t tile_base[kSeqPerLaunch + 1];    // first tile of each sequence (its live heads in order)
-    int32_t ntile[kSeqPerLaunch];            // tiles per (sequence, live head) = ceil((len - first) / 16)
+    int32_t ntile[kSeqPerLaunch];            // tiles per (sequence, live head) = ceil((len - start) / 16)
     int32_t first[kSeqPerLaunch];            // first visible row (rows [first, len) are attended)
+    int32_t start[kSeqPerLaunch];            // first row of the tile stream: first, rounded down to
+                                             // a multiple of 16 for the int8 kinds (whole K tiles)
     int32_t len[kSeqPerLaunch];              // rows stored
     int32_t wrow[kSeqPerLaunch];             // R-SWA row taken from k_new/v_new, -1 none
     uint8_t frozen[kSeqPerLaunch];           // q8: column fields hold the frozen RMS

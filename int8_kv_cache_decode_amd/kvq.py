@@ -184,7 +184,13 @@ class KvCache:
         t = self.buffers[name]
         if name in ("k", "v"):
             return t[: B * H * C * HEAD_DIM * 4].view(torch.float32).view(B, H, C, HEAD_DIM)
-        if name in ("kq", "vq"):
+        if name == "kq":
+            # K codes are stored tile-major (16-row tiles in MFMA operand
+            # order); this returns them row-major, as a copy
+            C16 = (C + 15) // 16 * 16
+            raw = t[: B * H * C16 * HEAD_DIM].view(torch.int8).view(B, H, C16 // 16, 2, 4, 16, 16)
+            return raw.permute(0, 1, 2, 5, 3, 4, 6).reshape(B, H, C16, HEAD_DIM)[:, :, :C]
+        if name == "vq":
             return t[: B * H * C * HEAD_DIM].view(torch.int8).view(B, H, C, HEAD_DIM)
         if name == "ks" and self.kind == KIND_I8:
             return t[: B * H * C * 4].view(torch.float32).view(B, H, C)

@@ -337,7 +337,8 @@ def test_rswa_refusals_leave_cache_and_rings_unchanged(kind):
 def test_buffer_and_workspace_sizes():
     c = fake_cache(K.KIND_Q8, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
     rows = 3 * 6 * 1000
-    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == rows * 128
+    # K codes are tile-major: each (sequence, live head) holds whole 16-row tiles
+    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == 3 * 6 * 1008 * 128
     assert K.kvq_buffer_bytes(c, K.BUF_KS) == rows * 16
     assert K.kvq_buffer_bytes(c, K.BUF_VQ) == rows * 128
     assert K.kvq_buffer_bytes(c, K.BUF_VS) == rows * 4
@@ -353,8 +354,10 @@ def test_i8_kind_buffers_and_refusals():
     fields, 264 B per (row, head); calls of the other kinds refuse it."""
     c = fake_cache(K.KIND_I8, batch=3, hkv=8, cap=1000, alive=[1, 1, 0, 1, 1, 0, 1, 1])
     rows = 3 * 6 * 1000
-    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == rows * 128 and K.kvq_buffer_bytes(c, K.BUF_VQ) == rows * 128
+    assert K.kvq_buffer_bytes(c, K.BUF_KQ) == 3 * 6 * 1008 * 128 and K.kvq_buffer_bytes(c, K.BUF_VQ) == rows * 128
     assert K.kvq_buffer_bytes(c, K.BUF_KS) == rows * 4 and K.kvq_buffer_bytes(c, K.BUF_VS) == rows * 4
+    c16 = fake_cache(K.KIND_I8, batch=1, hkv=2, cap=1024)
+    assert K.kvq_buffer_bytes(c16, K.BUF_KQ) == K.kvq_buffer_bytes(c16, K.BUF_VQ) == 2 * 1024 * 128
     assert K.kvq_buffer_bytes(c, K.BUF_KCOL) == 0 and K.kvq_buffer_bytes(c, K.BUF_K) == 0
     c.len[:] = [2, 0, 0]
     assert K.kvq_cache_bytes(c) == 2 * 6 * 264
