@@ -40,8 +40,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--replicas", type=int, default=4, help="f32 R-SWA cache replicas (>= 1 GB total)")
     p.add_argument("--part", choices=["both", "rswa", "q8"], default="both")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -783,7 +783,10 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 // then has sub-groups of lpg = 32 / chunks lanes (a float4 of channels
 // each), as many as its partial count asks for (at most 512 threads).  A
 // sub-group takes every ngroups-th partial, issuing the loads of up to 8 at
-// once and folding them with a running max; the sub-groups then merge in LDS.
+// once and folding them with a running max.  The sub-groups of a wave then
+// merge by a butterfly over lanes lpg, 2 lpg, .. apart, and the block's
+// waves (at most 8) merge in LDS.  Blocks are whole waves: sub-groups past
+// the partial count hold empty states (max -inf, sum 0).
 // ---------------------------------------------------------------------------
 #ifndef KVQ_COMBINE_THREADS
 #define KVQ_COMBINE_THREADS 512
@@ -793,7 +796,6 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #endif
 constexpr int kCombineThreads = KVQ_COMBINE_THREADS;
 constexpr int kCombineBatch = KVQ_COMBINE_BATCH;
-constexpr int kCombineMinLanes = 8;                     // lanes per sub-group with 4 chunks
 
 // Channel chunks per head for a grid of `blocks` (sequence, head) pairs.
 inline int combine_chunks(int blocks) { return blocks >= 256 ? 1 : blocks >= 128 ? 2 : 4; }
@@ -804,11 +806,12 @@ inline int combine_chunks(int blocks) { return blocks >= 256 ? 1 : blocks >= 128
 // + 3 in *res.  Block-wide: every thread of the block calls it.
 __device__ __forceinline__ bool combine_partials(const float* ml, const float* acc, size_t mstride, size_t astride,
                                                  int nch, float zs, int lpg, int ch0, float4* res) {
-    __shared__ float4 sm_acc[kCombineThreads];
-    __shared__ float sm_m[kCombineThreads / kCombineMinLanes], sm_l[kCombineThreads / kCombineMinLanes];
+    __shared__ float4 sm_acc[kCombineThreads / 64][32];
+    __shared__ float sm_m[kCombineThreads / 64], sm_l[kCombineThreads / 64];
     const int tid = threadIdx.x;
     const int sg = tid / lpg, lane = tid - sg * lpg;
     const int ngroups = (int)blockDim.x / lpg;
+    const int wave = tid >> 6, nwaves = (int)blockDim.x >> 6;
 
     float M = -INFINITY, L = 0.0f;
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -819,8 +822,9 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
         for (int k = 0; k < kCombineBatch; ++k) {
             const int c = c0 + k * ngroups;
             const bool ok = c < nch;
-            mv[k] = ok ? ml[c * mstride] : -INFINITY;
-            lv[k] = ok ? ml[c * mstride + 1] : 0.0f;
+            const float2 x = ok ? *(const float2*)(ml + c * mstride) : make_float2(-INFINITY, 0.0f);
+            mv[k] = x.x;
+            lv[k] = x.y;
             xv[k] = ok ? *(const float4*)(acc + c * astride + ch0 + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float Mn = M;
@@ -843,21 +847,38 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
         }
         M = Mn;
     }
-    sm_acc[tid] = A;
-    if (lane == 0) {
-        sm_m[sg] = M;
-        sm_l[sg] = L;
+    // the wave's sub-groups: butterfly over lanes lpg, 2 lpg, .. apart
+    for (int msk = lpg; msk < 64; msk <<= 1) {
+        const float Mo = __shfl_xor(M, msk, 64), Lo = __shfl_xor(L, msk, 64);
+        const float4 Ao = make_float4(__shfl_xor(A.x, msk, 64), __shfl_xor(A.y, msk, 64),
+                                      __shfl_xor(A.z, msk, 64), __shfl_xor(A.w, msk, 64));
+        const float Mn = fmaxf(M, Mo);
+        const float e0 = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+        const float e1 = Mo == -INFINITY ? 0.0f : fast_exp2(Mo - Mn);
+        L = L * e0 + Lo * e1;
+        A.x = A.x * e0 + Ao.x * e1;
+        A.y = A.y * e0 + Ao.y * e1;
+        A.z = A.z * e0 + Ao.z * e1;
+        A.w = A.w * e0 + Ao.w * e1;
+        M = Mn;
+    }
+    if ((tid & 63) < lpg) {
+        sm_acc[wave][tid & 63] = A;
+        if ((tid & 63) == 0) {
+            sm_m[wave] = M;
+            sm_l[wave] = L;
+        }
     }
     __syncthreads();
     if (tid >= lpg) return false;
     // a learned sink joins the max and the denominator ([P2] attend_group_upto)
-    float Mt = fmaxf(sm_m[0], zs);
-    for (int k = 1; k < ngroups; ++k) Mt = fmaxf(Mt, sm_m[k]);
+    float Mt = zs;
+    for (int k = 0; k < nwaves; ++k) Mt = fmaxf(Mt, sm_m[k]);
     float Lt = zs == -INFINITY ? 0.0f : fast_exp2(zs - Mt);
     float4 At = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < ngroups; ++k) {
-        const float e = sm_m[k] == -INFINITY ? 0.0f : fast_exp2(sm_m[k] - Mt);   // sub-groups without rows
-        const float4 x = sm_acc[k * lpg + tid];
+    for (int k = 0; k < nwaves; ++k) {
+        const float e = sm_m[k] == -INFINITY ? 0.0f : fast_exp2(sm_m[k] - Mt);   // waves without rows
+        const float4 x = sm_acc[k][tid];
         Lt = fmaf(e, sm_l[k], Lt);
         At.x = fmaf(e, x.x, At.x);
         At.y = fmaf(e, x.y, At.y);
@@ -1307,7 +1328,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const Verify
 }
 
 // Threads per combine block: enough sub-groups of lpg lanes that each folds
-// at most one batch of partials, between 1 sub-group and 512 threads.
+// at most one batch of partials, at most 512 threads, in whole waves.
 int combine_threads(const DecodeArgs& a, int lpg) {
     int nmax = 1;
     for (int j = 0; j < a.n_seq; ++j) {
@@ -1322,7 +1343,7 @@ int combine_threads(const DecodeArgs& a, int lpg) {
     int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
     const int gmax = kCombineThreads / lpg;
     groups = groups < 1 ? 1 : (groups > gmax ? gmax : groups);
-    return lpg * groups;
+    return (lpg * groups + 63) / 64 * 64;          // whole waves
 }
 
 // Waves of a decode kernel that are resident on the current device at once
@@ -1434,7 +1455,7 @@ hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int whic
     int groups = (nmax + kCombineBatch - 1) / kCombineBatch;
     const int gmax = kCombineThreads / lpg;
     groups = groups < 1 ? 1 : (groups > gmax ? gmax : groups);
-    hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads * chunks, a.n_seq), dim3(lpg * groups), 0, s,
+    hipLaunchKernelGGL(k_combine_verify, dim3(a.n_draft * a.n_q_heads * chunks, a.n_seq), dim3((lpg * groups + 63) / 64 * 64), 0, s,
                        a);
     return hipGetLastError();
 }
