@@ -46,6 +46,57 @@ __device__ __forceinline__ uint4 ld_stream(const int8_t* p) {
 }
 __device__ __forceinline__ float ld_stream1(const float* p) { return __builtin_nontemporal_load(p); }
 
+// Cross-lane exchanges on the VALU only (no LDS permute): DPP row
+// permutations within 16-lane rows, and gfx950's permlane swaps across rows.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
+// Rows 2k + 1 of a exchanged with rows 2k of b (16-lane rows): afterwards
+// a + b (or max) at every lane combines lanes l and l ^ 16 of the inputs.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// Upper 32 lanes of a exchanged with the lower 32 of b.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// Max over the 16 lanes of a row (lanes sharing lane >> 4): quad swaps, then
+// the half-row and row mirrors pair whole quads and half-rows.  In the q8
+// decode's tile loop this replaced four LDS permutes on the path from the
+// scores to the weights (batched q8 decode 388.9 -> 381.5 us, int8 route
+// 360.5 -> 354.1 us on one MI355X).
+__device__ __forceinline__ float max16(float x) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+
+// Max (sum) of x over lanes l and l ^ 16, then over l and l ^ 32.
+__device__ __forceinline__ float max_rows(float x) {
+    float a = x, b = x;
+    swap16(a, b);
+    a = b = fmaxf(a, b);
+    swap32(a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_rows(float x) {
+    float a = x, b = x;
+    swap16(a, b);
+    a = b = a + b;
+    swap32(a, b);
+    return a + b;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
@@ -133,7 +184,10 @@ __device__ __forceinline__ int share_index() {
 // ---------------------------------------------------------------------------
 // Sum 8 per-lane partials over the 32 lanes of a half so that lanes with
 // (seg >> 2) == i end with the total of partial i (transpose-reduce: 9
-// exchanges instead of 40).
+// exchanges instead of 40).  In this kernel the LDS permutes measured
+// faster than the VALU row permutations of the q8 kernel (57.6 vs 58.8 us
+// for the 32k R-SWA step): with them the compiler kept only a few of the
+// tile's loads in flight.
 __device__ __forceinline__ float reduce8_over32(const float (&v)[8], int seg) {
     const bool b4 = seg & 16, b3 = seg & 8, b2 = seg & 4;
     float x[4], y[2];
@@ -355,19 +409,6 @@ __device__ __forceinline__ int take_digit(int& x) {
     const int d = ((x + 64) & 127) - 64;
     x = (x - d) >> 7;
     return d;
-}
-
-// Max over the 16 lanes sharing lane >> 4.
-__device__ __forceinline__ float max16(float x) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-    return x;
-}
-
-__device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
-    return x;
 }
 
 // Orders this wave's LDS writes before its following LDS reads.
@@ -604,16 +645,21 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         // ri with entries [kOwn ri, kOwn ri + kOwn)), add into f64, clear acc.
         auto flush = [&]() {
             constexpr int N = HPK * kVDim;
-            const bool b5 = ri & 2, b4 = ri & 1;
             float y[N / 2], z[kOwn];
 #pragma unroll
             for (int i = 0; i < N / 2; ++i) {
-                const float lo = acc[i / kVDim][i % kVDim], hi = acc[(i + N / 2) / kVDim][(i + N / 2) % kVDim];
-                y[i] = (b5 ? hi : lo) + __shfl_xor(b5 ? lo : hi, 32, 64);
+                // lanes 0..31 keep entry i, lanes 32..63 entry i + N / 2
+                float lo = acc[i / kVDim][i % kVDim], hi = acc[(i + N / 2) / kVDim][(i + N / 2) % kVDim];
+                swap32(lo, hi);
+                y[i] = lo + hi;
             }
 #pragma unroll
-            for (int i = 0; i < kOwn; ++i)
-                z[i] = (b4 ? y[i + kOwn] : y[i]) + __shfl_xor(b4 ? y[i] : y[i + kOwn], 16, 64);
+            for (int i = 0; i < kOwn; ++i) {
+                // rows with lane bit 4 clear keep y[i], the others y[i + kOwn]
+                float lo = y[i], hi = y[i + kOwn];
+                swap16(lo, hi);
+                z[i] = lo + hi;
+            }
 #pragma unroll
             for (int i = 0; i < kOwn; ++i) cell(i) += (double)z[i];
 #pragma unroll
@@ -1053,8 +1099,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
                 sc[r] = (qvalid && p < it.row1 && visible(p)) ? c[r] : -INFINITY;
                 tmax = fmaxf(tmax, sc[r]);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = max_rows(tmax);
             const float mnew = fmaxf(m, tmax);
             const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(m - mnew);
             float pw[4];
@@ -1087,8 +1132,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
         }
         if (r0 < it.row1) compute_tile(r0, ta);
         // the piece's partial for each valid query
-        float lt = l + __shfl_xor(l, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = sum_rows(l);
         if (qvalid) {
             const size_t ix = (size_t)it.slot * a.nq + qi;
             if (kb == 0) {
@@ -1247,8 +1291,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
                 s64[r] = (double)d[r] * (qsc * (double)t.ks[r]);
                 if (vis[r]) tmax = fmaxf(tmax, (float)s64[r]);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            tmax = max_rows(tmax);
             const float mnew = fmaxf(m, tmax);
             const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(m - mnew);
             float pw[4];
@@ -1282,8 +1325,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         if (r0 < it.row1) compute_tile(r0, ta);
         // the piece's partial for each valid query: lane (qi, kb) holds
         // channels 8 (4 kb + r) + cb
-        float lt = l + __shfl_xor(l, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = sum_rows(l);
         if (qvalid) {
             const size_t ix = (size_t)it.slot * a.nq + qi;
             if (kb == 0) {
