@@ -48,10 +48,10 @@ __device__ __forceinline__ float ld_stream1(const float* p) { return __builtin_n
 
 // Cross-lane exchanges on the VALU only (no LDS permute): DPP row
 // permutations within 16-lane rows, and gfx950's permlane swaps across rows.
+// Lane l takes x of another lane of its row (every source lane is inside the
+// row, so bound_ctrl never applies while the whole wave is active).
 template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
-}
+__device__ __forceinline__ int dpp_row(int x) { return __builtin_amdgcn_mov_dpp(x, kCtrl, 0xf, 0xf, true); }
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]: lane i <- i ^ 1
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]: lane i <- i ^ 2
 constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
@@ -70,15 +70,21 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
     b = __uint_as_float(r[1]);
 }
 // Max over the 16 lanes of a row (lanes sharing lane >> 4): quad swaps, then
-// the half-row and row mirrors pair whole quads and half-rows.  In the q8
-// decode's tile loop this replaced four LDS permutes on the path from the
-// scores to the weights (batched q8 decode 388.9 -> 381.5 us, int8 route
-// 360.5 -> 354.1 us on one MI355X).
+// the half-row and row mirrors pair whole quads and half-rows.  The max runs
+// on integer keys that order like the floats (a negative float's magnitude
+// bits flipped), so each step is one v_max_i32 with its DPP operand and needs
+// no NaN canonicalisation; the result is exact.  Every lane must be active.
+// In the q8 decode's tile loop this replaced four LDS permutes on the path
+// from the scores to the weights (batched q8 decode 388.9 -> 381.5 us, int8
+// route 360.5 -> 354.1 us on one MI355X).
 __device__ __forceinline__ float max16(float x) {
-    x = fmaxf(x, dpp_f<kDppXor1>(x));
-    x = fmaxf(x, dpp_f<kDppXor2>(x));
-    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-    return fmaxf(x, dpp_f<kDppMirror>(x));
+    const int b = __float_as_int(x);
+    int k = b ^ ((b >> 31) & 0x7fffffff);
+    k = max(k, dpp_row<kDppXor1>(k));
+    k = max(k, dpp_row<kDppXor2>(k));
+    k = max(k, dpp_row<kDppHalfMirror>(k));
+    k = max(k, dpp_row<kDppMirror>(k));
+    return __int_as_float(k ^ ((k >> 31) & 0x7fffffff));
 }
 
 // Max (sum) of x over lanes l and l ^ 16, then over l and l ^ 32.
