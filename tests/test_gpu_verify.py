@@ -28,7 +28,13 @@ def rng(seed):
 BUFS = {K.KIND_F32: ("k", "v"), K.KIND_I8: ("kq", "ks", "vq", "vs")}
 
 
-def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32):
+def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32, spread=False):
+    """spread: every key row is 0 on channel 0 except one reference spike row
+    per (sequence, KV head) at 64, and each query is +-32 on channel 0 (sign
+    alternating over the queries of a KV head) and 0 elsewhere: the spike
+    scores +-181 (natural units), every other row exactly 0, so a running max
+    taken over another query's lanes, or missing the spike's lane, gives 0/0
+    or inf (see tests/test_gpu_spread.py)."""
     r = rng(seed)
     W = K.RING_WINDOW
     c = K.KvCache(kind, batch, hkv, prefill + W)
@@ -36,12 +42,19 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32)
     hq = hkv * hpk
     ref = [(r.standard_normal((prefill, hkv, 128)).astype(np.float32),
             r.standard_normal((prefill, hkv, 128)).astype(np.float32)) for _ in range(batch)]
+    if spread:
+        for b in range(batch):
+            ref[b][0][:, :, 0] = 0.0
+            for g in range(hkv):
+                ref[b][0][(7 + 13 * b + 5 * g) % prefill, g, 0] = 64.0
     for b in range(batch):
         if prefill:
             append_rows(c, b, *ref[b])
         K.rswa_record_prefill(c, rings, b)
     hist_k = r.standard_normal((n_hist, batch, hkv, 128)).astype(np.float32)
     hist_v = r.standard_normal((n_hist, batch, hkv, 128)).astype(np.float32)
+    if spread:
+        hist_k[..., 0] = 0.0
     out1 = torch.zeros((batch, hq, 128), device="cuda")
     q1 = dev(r.standard_normal((batch, hq, 128)).astype(np.float32))
     for t in range(n_hist):
@@ -51,12 +64,17 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32)
     q = r.standard_normal((batch, n_draft, hq, 128)).astype(np.float32)
     dk = r.standard_normal((batch, n_draft, hkv, 128)).astype(np.float32)
     dv = r.standard_normal((batch, n_draft, hkv, 128)).astype(np.float32)
+    if spread:
+        dk[..., 0] = 0.0
+        q[:] = 0.0
+        q[..., 0] = np.where((np.arange(n_draft)[:, None] * hq + np.arange(hq)[None, :]) % 2 == 0, 32.0, -32.0)
     out = torch.full((batch, n_draft, hq, 128), np.nan, device="cuda")
     K.rswa_verify(c, rings, hq, n_draft, dev(q), dev(dk), dev(dv), out)
     out2 = torch.full_like(out, np.nan)
     K.rswa_verify(c, rings, hq, n_draft, dev(q), dev(dk), dev(dv), out2)
     torch.cuda.synchronize()
     got = host(out)
+    assert np.isfinite(got).all()
     assert np.array_equal(got.view(np.uint32), host(out2).view(np.uint32)), "verify is not deterministic"
     for nm, b0 in zip(BUFS[kind], before[0]):
         assert np.array_equal(host(c.view(nm)).view(np.uint8), b0.view(np.uint8)), nm
@@ -86,6 +104,13 @@ def run_verify(batch, hkv, hpk, prefill, n_hist, n_draft, seed, kind=K.KIND_F32)
 def test_verify_matches_sequential_definition(hkv, hpk, prefill, n_hist, n_draft, kind):
     say("case: verify kind", kind, "hkv", hkv, "hpk", hpk, "prefill", prefill, "hist", n_hist, "drafts", n_draft)
     run_verify(2, hkv, hpk, prefill, n_hist, n_draft, seed=500 + prefill + n_hist + n_draft, kind=kind)
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+@pytest.mark.parametrize("hkv,hpk,n_hist,n_draft", [(2, 1, 20, 8), (2, 4, 130, 4), (1, 2, 127, 7)])
+def test_verify_extreme_score_spread(hkv, hpk, n_hist, n_draft, kind):
+    say("case: verify spread kind", kind, "hkv", hkv, "hpk", hpk, "hist", n_hist, "drafts", n_draft)
+    run_verify(2, hkv, hpk, 300, n_hist, n_draft, seed=800 + n_hist + n_draft, kind=kind, spread=True)
 
 
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
