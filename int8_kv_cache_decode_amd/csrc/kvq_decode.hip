@@ -432,6 +432,8 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     // i8 kind, R-SWA: the ring row's fresh K / V codes and their scales
     __shared__ __attribute__((aligned(16))) int8_t sm_ring[kI8 ? kWaves : 1][2][kHD];
     __shared__ float sm_ring_s[kI8 ? kWaves : 1][2];
+    // i8 kind: the query codes of each head of the group
+    __shared__ __attribute__((aligned(16))) int8_t sm_qc[kI8 ? kWaves : 1][kI8 ? HPK : 1][kHD];
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -582,46 +584,40 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             }
         } else {
             // ---- query codes ([P3] quantize_row_i8 on each Q head, in f32) ----
-            // A rows m = 4 * head carry the head's codes over all 64 channels
-            // of a span (one K scale per row, so no group is zeroed); the rows
-            // of digits 1..3 are zero.  gsc[hb][0] = qscale * log2(e)/sqrt(128)
-            // of this lane's score head 4 hb + hq.
+            // Lane l quantises channels 2 l and 2 l + 1 of every head of the
+            // group (the head's max over the wave) into a per-wave LDS row;
+            // then A rows m = 4 * head take the head's codes over all 64
+            // channels of a span (one K scale per row, so no group is zeroed),
+            // and the rows of digits 1..3 are zero.  gsc[hb][0] = qscale *
+            // log2(e)/sqrt(128) of this lane's score head 4 hb + hq.
+            float qsh[HPK];
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                const float2 x = *(const float2*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 2 * lane);
+                const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+                const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
+                char2 cq;
+                cq.x = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(x.x, qs)), -127.0f), 127.0f);
+                cq.y = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(x.y, qs)), -127.0f), 127.0f);
+                *(char2*)(&sm_qc[wave][h][2 * lane]) = cq;
+                qsh[h] = qs;
+            }
+            wave_lds_sync();
 #pragma unroll
             for (int hb = 0; hb < NB; ++hb) {
                 const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
-                float xs[2][16];
-                float amax = 0.0f;
-#pragma unroll
-                for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4) {
-                        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-                        if (hm < HPK)
-                            qv = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD +
-                                                  64 * sp + 16 * kb + 4 * t4);
-                        xs[sp][4 * t4 + 0] = qv.x;
-                        xs[sp][4 * t4 + 1] = qv.y;
-                        xs[sp][4 * t4 + 2] = qv.z;
-                        xs[sp][4 * t4 + 3] = qv.w;
-                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(qv.x), fabsf(qv.y)), fmaxf(fabsf(qv.z), fabsf(qv.w))));
-                    }
-                amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-                amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-                const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
                     v4i pk = {0, 0, 0, 0};
-                    if (jm == 0 && hm < HPK) {
-#pragma unroll
-                        for (int t = 0; t < 16; ++t) {
-                            const int c = (int)fminf(fmaxf(rintf(__fdiv_rn(xs[sp][t], qs)), -127.0f), 127.0f);
-                            pk[t >> 2] |= (c & 0xff) << (8 * (t & 3));
-                        }
-                    }
+                    if (jm == 0 && hm < HPK) pk = *(const v4i*)(&sm_qc[wave][hm][64 * sp + 16 * kb]);
                     qa_lo[hb][sp] = pk;
                     qa_hi[hb][sp] = pk;
                 }
-                gsc[hb][0] = (double)__shfl(qs, 4 * hq, 64) * kQScale64;
+                float qs = qsh[0];
+#pragma unroll
+                for (int h = 1; h < HPK; ++h)
+                    if (h == 4 * hb + hq) qs = qsh[h];
+                gsc[hb][0] = (double)qs * kQScale64;
             }
         }
 
