@@ -240,8 +240,13 @@ __device__ __forceinline__ double soft_cap(double s, double c2, double inv_c2) {
     return copysign(c2 * ((1.0 - e) / (1.0 + e)), s);
 }
 
+// One wave per SIMD streams the f32 rows (the launch gives one share per
+// SIMD); the occupancy hint lets the scheduler keep more of a step's loads
+// in flight.  Measured on the 32k R-SWA step: two tiles per step with the
+// hint 57.3 us, one tile without it 57.8 us; two tiles without the hint
+// 58.8 us, one tile with it 59.1 us.
 template <int HPK, bool kCap>
-__global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_decode_f32(const DecodeArgs a) {
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int lane = threadIdx.x & 63;
@@ -276,45 +281,56 @@ __global__ __launch_bounds__(256) void k_decode_f32(const DecodeArgs a) {
             acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
 
-        for (int r = it.row0; r < it.row1; r += kTileRows) {
-            float4 kx[8], vx[8];
+        // kF32Tiles 16-row tiles per step: all their loads leave before the
+        // step's arithmetic (rows clamped into the piece; a tile that starts
+        // past the piece's end is loaded but not computed)
+        constexpr int kF32Tiles = 2;
+        for (int r = it.row0; r < it.row1; r += kF32Tiles * kTileRows) {
+            float4 kx[8 * kF32Tiles], vx[8 * kF32Tiles];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 8 * kF32Tiles; ++i) {
                 const int row = min(r + 2 * i + half, it.row1 - 1);
                 const bool wr = has_w && row == wrow;
                 kx[i] = ld_stream((wr ? kn : K + (size_t)row * kHD) + 4 * seg);
                 vx[i] = ld_stream((wr ? vn : V + (size_t)row * kHD) + 4 * seg);
             }
-            const int myrow = r + 2 * (seg >> 2) + half;
 #pragma unroll
-            for (int h = 0; h < HPK; ++h) {
-                float part[8];
+            for (int tt = 0; tt < kF32Tiles; ++tt) {
+                const int rt = r + tt * kTileRows;
+                if (tt > 0 && rt >= it.row1) break;
+                const int myrow = rt + 2 * (seg >> 2) + half;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float d = qv[h].x * kx[i].x;
-                    d = fmaf(qv[h].y, kx[i].y, d);
-                    d = fmaf(qv[h].z, kx[i].z, d);
-                    d = fmaf(qv[h].w, kx[i].w, d);
-                    part[i] = d;
+                for (int h = 0; h < HPK; ++h) {
+                    float part[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float4 kt = kx[8 * tt + i];
+                        float d = qv[h].x * kt.x;
+                        d = fmaf(qv[h].y, kt.y, d);
+                        d = fmaf(qv[h].z, kt.z, d);
+                        d = fmaf(qv[h].w, kt.w, d);
+                        part[i] = d;
+                    }
+                    float sc = reduce8_over32(part, seg);
+                    if (kCap) sc = (float)soft_cap((double)sc, a.softcap2, inv_c2);
+                    if (myrow >= it.row1) sc = -INFINITY;
+                    const float mnew = fmaxf(m[h], wave_max(sc));
+                    const float alpha = fast_exp2(m[h] - mnew);
+                    const float p = fast_exp2(sc - mnew);
+                    l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
+                    float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float pi = __shfl(p, half * 32 + 4 * i, 64);
+                        const float4 vt = vx[8 * tt + i];
+                        ac.x = fmaf(pi, vt.x, ac.x);
+                        ac.y = fmaf(pi, vt.y, ac.y);
+                        ac.z = fmaf(pi, vt.z, ac.z);
+                        ac.w = fmaf(pi, vt.w, ac.w);
+                    }
+                    acc[h] = ac;
+                    m[h] = mnew;
                 }
-                float sc = reduce8_over32(part, seg);
-                if (kCap) sc = (float)soft_cap((double)sc, a.softcap2, inv_c2);
-                if (myrow >= it.row1) sc = -INFINITY;
-                const float mnew = fmaxf(m[h], wave_max(sc));
-                const float alpha = fast_exp2(m[h] - mnew);
-                const float p = fast_exp2(sc - mnew);
-                l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
-                float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pi = __shfl(p, half * 32 + 4 * i, 64);
-                    ac.x = fmaf(pi, vx[i].x, ac.x);
-                    ac.y = fmaf(pi, vx[i].y, ac.y);
-                    ac.z = fmaf(pi, vx[i].z, ac.z);
-                    ac.w = fmaf(pi, vx[i].w, ac.w);
-                }
-                acc[h] = ac;
-                m[h] = mnew;
             }
         }
 
@@ -1429,6 +1445,22 @@ int resident_waves(const void* kernel, int which) {
     return v;
 }
 
+// SIMDs of the current device (compute units x 4), cached per device; 0 on
+// a runtime error.
+int simd_count() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        v = cus * 4;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
 
 // Cache kinds of the decode launcher.
@@ -1443,12 +1475,12 @@ const void* decode_kernel(bool cap) {
 }
 
 // Shares per launch: one per resident wave for the q8 kernel (a wave keeps
-// one 4.4-KB tile in flight beside the one it computes), one per four
-// resident waves for the f32 kernel: a wave's 16-KB tile keeps HBM busy with
-// one wave per SIMD, and fewer shares make the combine cheaper (measured on
-// MI355X, 4 x 10 heads x 32k rows: decode 52.0 vs 52.6 us, combine 9.1 vs
-// 5.0 us).
-constexpr int kF32WavesPerShare = 4;
+// one 4.4-KB tile in flight beside the one it computes), one per SIMD for the
+// f32 kernel: a wave's 16-KB tiles keep HBM busy with one wave per SIMD, and
+// fewer shares make the combine cheaper (measured on MI355X, 4 x 10 heads x
+// 32k rows, the R-SWA step: one share per 2 SIMDs 89.0 us, per SIMD 57.9 us,
+// 2 per SIMD 59.0 us; the combine alone 5.0 us at one per SIMD and 9.1 us at
+// 4 per SIMD).
 
 template <int kKind>
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
@@ -1465,9 +1497,8 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
             case 8: fn = decode_kernel<8, kKind>(cap); break;
             default: return hipErrorInvalidValue;
         }
-        const int wv = resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk));
-        if (wv == 0) return hipErrorInvalidDevice;
-        const int shares = kQ8 ? wv : (wv + kF32WavesPerShare - 1) / kF32WavesPerShare;
+        const int shares = kQ8 ? resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk)) : simd_count();
+        if (shares == 0) return hipErrorInvalidDevice;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};
