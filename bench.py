@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--replicas", type=int, default=4, help="f32 R-SWA cache replicas (>= 1 GB total)")
     p.add_argument("--part", choices=["both", "rswa", "q8"], default="both")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-small", action="store_true", help="skip the three small workloads")
     p.add_argument("--cpu-sample-seqs", type=int, default=8)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="host time the oracle sample is repeated for")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -414,6 +415,10 @@ def main():
             "rows_moved_per_head": moved, "bytes_moved": nb, "GBps": round(nb / us / 1e3, 1),
             "frac_of_peak": round(nb / us / 1e3 / HBM_PEAK_GBS, 4)}
 
+    # ---------------- the three small configurations ----------------
+    if not args.no_small:
+        small_parts(parts, K, t, dev, time_calls, log, do_rswa, do_q8)
+
     dominant = "decode_attn_q8" if do_q8 else "rswa_decode_f32"
     kernel_tag = "k_decode_q8_batched_q8" if do_q8 else "k_decode_f32_rswa_long_f32"
     d = parts[dominant]
@@ -439,6 +444,110 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
     }
     print(json.dumps(rec), flush=True)
+
+
+def small_parts(parts, K, t, dev, time_calls, log, do_rswa, do_q8):
+    """Per-call time of the three small workloads: rswa_f32 (10 heads, 256
+    reference rows + full ring), gqa_f32 (32 / 8 heads, 4096 rows, two dead
+    groups) and gqa_q8 (32 / 8 heads, 8192 rows).  Each is rotated over
+    enough replicas (> 256 MB in all) that the Infinity Cache cannot serve
+    repeated reads.  Each is timed as back-to-back calls (us_per_call, which
+    includes the host's launch cost at these sizes) and as 200 calls captured
+    in one HIP graph and replayed (us_per_call_graph; GB/s and the fraction
+    of peak use it).  An R-SWA replay repeats the captured ring write, the
+    same work as a step.  These calls are bound by launch and latency more
+    than by bandwidth."""
+    import torch
+    import workloads
+    mall = 280e6
+
+    def time_graph(call, n, repeats=5):
+        """us per call of n calls captured in one HIP graph and replayed (no
+        host launch cost between the calls)."""
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        per_call = []
+        for _ in range(repeats):
+            s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_ev.record()
+            g.replay()
+            e_ev.record()
+            e_ev.synchronize()
+            per_call.append(s_ev.elapsed_time(e_ev) / n * 1e3)
+        del g
+        return float(np.median(per_call))
+
+    def record(name, call, nb, positions, reps):
+        us = time_calls(call, 200)
+        ug = time_graph(call, 200)
+        parts[name] = {"us_per_call": round(us, 2), "us_per_call_graph": round(ug, 2), "algorithmic_bytes": nb,
+                       "GBps": round(nb / ug / 1e3, 1), "frac_of_peak": round(nb / ug / 1e3 / HBM_PEAK_GBS, 4),
+                       "kv_positions_per_s": round(positions / ug * 1e6, 1), "replicas": reps}
+
+    if do_rswa:
+        rs = workloads.get("rswa_f32")
+        rows = rs.prefill + rs.window
+        nb = algorithmic_bytes_rswa(rows, rs.n_heads)
+        reps = int(mall // (rows * rs.n_heads * 1024)) + 1
+        rk, rv = rs.reference()
+        rk_d, rv_d = t(rk.transpose(1, 0, 2)), t(rv.transpose(1, 0, 2))
+        pool = [tuple(t(x[None]) for x in rs.step(s)) for s in range(16)]
+        caches = []
+        for _ in range(reps):
+            c = K.KvCache(K.KIND_F32, 1, rs.n_heads, rows)
+            rings = K.Rings(1)
+            K.kv_append_f32(c, 0, rs.prefill, rk_d, rv_d)
+            K.rswa_record_prefill(c, rings, 0)
+            out = torch.zeros((1, rs.n_heads, 128), device=dev)
+            for s_ in range(rs.writes - 1):
+                q, kk, vv = pool[s_ % 16]
+                K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+            caches.append((c, rings, out))
+        torch.cuda.synchronize()
+        log("rswa_f32 replicas ready: %d" % reps)
+
+        def call(i):
+            c, rings, out = caches[i % reps]
+            q, kk, vv = pool[i % 16]
+            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+        record("rswa_decode_f32_small", call, nb, rows, reps)
+        del caches
+    if do_q8:
+        for name, kind in (("gqa_f32", K.KIND_F32), ("gqa_q8", K.KIND_Q8)):
+            spec = workloads.get(name)
+            n = int(spec.lengths()[0])
+            alive = spec.alive()
+            n_live = int(alive.sum())
+            per_row = 1024 if kind == K.KIND_F32 else 276
+            nb = (n * n_live * per_row + spec.n_q_heads * 128 * 4 * 2
+                  + (n_live * 2 * 128 * 4 if kind == K.KIND_Q8 else 0))
+            reps = int(mall // (n * n_live * per_row)) + 1
+            k, v = spec.kv_rows(0)
+            kd, vd = t(k), t(v)
+            app = K.kv_append_f32 if kind == K.KIND_F32 else K.kv_append_q8
+            dec = K.decode_attn_f32 if kind == K.KIND_F32 else K.decode_attn_q8
+            caches = []
+            for _ in range(reps):
+                c = K.KvCache(kind, 1, spec.n_kv_heads, n, alive=alive)
+                app(c, 0, n, kd, vd)
+                caches.append((c, c.workspace(spec.n_q_heads)))
+            q = t(spec.query())
+            out = torch.zeros((1, spec.n_q_heads, 128), device=dev)
+            torch.cuda.synchronize()
+            log("%s replicas ready: %d" % (name, reps))
+
+            def call(i, caches=caches, dec=dec, spec=spec, q=q, out=out):
+                c, ws = caches[i % len(caches)]
+                dec(c, spec.n_q_heads, q, out, ws)
+            record("decode_attn_%s_%s" % ("f32" if kind == K.KIND_F32 else "q8", name), call, nb, n, reps)
+            del caches
 
 
 def cpu_baseline(args, rs, bq, do_rswa, do_q8):

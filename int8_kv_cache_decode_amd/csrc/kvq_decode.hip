@@ -1476,12 +1476,20 @@ const void* decode_kernel(bool cap) {
 }
 
 // Shares per launch: one per resident wave for the q8 kernel (a wave keeps
-// one 4.4-KB tile in flight beside the one it computes), one per SIMD for the
+// one 4.4-KB tile in flight beside the one it computes) -- but one per SIMD
+// when that would leave fewer than kQ8MinTilesPerWave tiles per resident
+// wave: a short launch is then dominated by each share's query set-up and
+// partial (measured on MI355X, one 8192-row sequence, 32 Q / 8 KV heads,
+// 4096 tiles: one share per resident wave, 3072 shares, 21.2 us; 2048 shares
+// 18.2 us; 1024, one per SIMD, 16.4 us; 1365 or 682 shares, not a whole
+// number of workgroups per compute unit, 21.2 and 21.6 us) -- and one per SIMD for the
 // f32 kernel: a wave's 16-KB tiles keep HBM busy with one wave per SIMD, and
 // fewer shares make the combine cheaper (measured on MI355X, 4 x 10 heads x
 // 32k rows, the R-SWA step: one share per 2 SIMDs 89.0 us, per SIMD 57.9 us,
 // 2 per SIMD 59.0 us; the combine alone 5.0 us at one per SIMD and 9.1 us at
 // 4 per SIMD).
+
+constexpr int kQ8MinTilesPerWave = 4;
 
 template <int kKind>
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
@@ -1498,7 +1506,8 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
             case 8: fn = decode_kernel<8, kKind>(cap); break;
             default: return hipErrorInvalidValue;
         }
-        const int shares = kQ8 ? resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk)) : simd_count();
+        int shares = kQ8 ? resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk)) : simd_count();
+        if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = simd_count();
         if (shares == 0) return hipErrorInvalidDevice;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
