@@ -448,6 +448,10 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     // i8 kind, R-SWA: the ring row's fresh K / V codes and their scales
     __shared__ __attribute__((aligned(16))) int8_t sm_ring[kI8 ? kWaves : 1][2][kHD];
     __shared__ float sm_ring_s[kI8 ? kWaves : 1][2];
+    // q8 kind: the query digits as A operands [head block][span][row][channel],
+    // and the exponent of each (head, K group)
+    __shared__ __attribute__((aligned(16))) int8_t sm_dig[kI8 ? 1 : kWaves][kI8 ? 1 : NB][2][16][64];
+    __shared__ int sm_ge[kI8 ? 1 : kWaves][kI8 ? 1 : HPK][4];
     // i8 kind: the query codes of each head of the group
     __shared__ __attribute__((aligned(16))) int8_t sm_qc[kI8 ? kWaves : 1][kI8 ? HPK : 1][kHD];
     const int w = share_index();
@@ -549,51 +553,49 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         v4i qa_lo[NB][2], qa_hi[NB][2];                   // [head block][span]
         double gsc[NB][4];                                // for this lane's score head 4 hb + hq
         if constexpr (!kI8) {
-    #pragma unroll
+            // Lane l takes channels 2 l and 2 l + 1 of every head of the group:
+            // qc = q (.) kcol exactly in f64, the group's largest |qc| over the
+            // 16 lanes that hold its 32 channels, and the four digits, written
+            // into a per-wave LDS copy of the A operands; each lane then reads
+            // its 16 digit bytes.  The group exponents go through LDS too.
+            const float2 cv = frz ? *(const float2*)(kcol + 2 * lane) : make_float2(1.f, 1.f);
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                const float2 qv = *(const float2*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 2 * lane);
+                const double q0 = (double)qv.x * (double)cv.x, q1 = (double)qv.y * (double)cv.y;   // exact
+                double gmax = fmax(fabs(q0), fabs(q1));
+#pragma unroll
+                for (int msk = 1; msk < 16; msk <<= 1) gmax = fmax(gmax, shfl_xor_f64(gmax, msk));
+                int e = 0;
+                (void)frexp(gmax, &e);                             // gmax < 2^e
+                const double up = ldexp(1.0, 27 - e);
+                int x0 = (int)rint(q0 * up), x1 = (int)rint(q1 * up);   // |x| <= 2^27
+                char2 dg[4];
+                dg[3] = make_char2((int8_t)take_digit(x0), (int8_t)take_digit(x1));
+                dg[2] = make_char2((int8_t)take_digit(x0), (int8_t)take_digit(x1));
+                dg[1] = make_char2((int8_t)take_digit(x0), (int8_t)take_digit(x1));
+                dg[0] = make_char2((int8_t)x0, (int8_t)x1);
+                const int c = 2 * lane;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *(char2*)(&sm_dig[wave][h >> 2][c >> 6][4 * (h & 3) + j][c & 63]) = dg[j];
+                if ((lane & 15) == 0) sm_ge[wave][h][lane >> 4] = e;
+            }
+            wave_lds_sync();
+#pragma unroll
             for (int hb = 0; hb < NB; ++hb) {
-                const int hm = 4 * hb + ((lane & 15) >> 2), jm = lane & 3, kb = lane >> 4;
+                const int hm = 4 * hb + ((lane & 15) >> 2), kb = lane >> 4;
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
-                    const int d0 = 64 * sp + 16 * kb;
-                    double qc[16];
-                    double gmax = 0.0;
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) qc[t] = 0.0;
-                    if (hm < HPK) {
-                        const float* qp = a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + hm) * kHD + d0;
-#pragma unroll
-                        for (int t4 = 0; t4 < 4; ++t4) {
-                            const float4 qv = *(const float4*)(qp + 4 * t4);
-                            float4 cv = make_float4(1.f, 1.f, 1.f, 1.f);
-                            if (frz) cv = *(const float4*)(kcol + d0 + 4 * t4);
-                            qc[4 * t4 + 0] = (double)qv.x * (double)cv.x;   // exact products
-                            qc[4 * t4 + 1] = (double)qv.y * (double)cv.y;
-                            qc[4 * t4 + 2] = (double)qv.z * (double)cv.z;
-                            qc[4 * t4 + 3] = (double)qv.w * (double)cv.w;
-                        }
-#pragma unroll
-                        for (int t = 0; t < 16; ++t) gmax = fmax(gmax, fabs(qc[t]));
-                    }
-                    gmax = fmax(gmax, shfl_xor_f64(gmax, 16));     // the group's other 16 channels
-                    int e = 0;
-                    (void)frexp(gmax, &e);                         // gmax < 2^e
-                    const double up = ldexp(1.0, 27 - e);
                     v4i pk = {0, 0, 0, 0};
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) {
-                        int x = (int)rint(qc[t] * up);             // |x| <= 2^27
-                        const int d3 = take_digit(x);
-                        const int d2 = take_digit(x);
-                        const int d1 = take_digit(x);
-                        const int d = jm == 0 ? x : jm == 1 ? d1 : jm == 2 ? d2 : d3;
-                        pk[t >> 2] |= (d & 0xff) << (8 * (t & 3));
-                    }
+                    if (hm < HPK) pk = *(const v4i*)(&sm_dig[wave][hb][sp][lane & 15][16 * kb]);
                     const v4i zero = {0, 0, 0, 0};
                     qa_lo[hb][sp] = first_half ? pk : zero;
                     qa_hi[hb][sp] = first_half ? zero : pk;
 #pragma unroll
-                    for (int gs = 0; gs < 2; ++gs) {               // lane 4 hq + 32 gs holds head 4 hb + hq
-                        const int es = __shfl(e, 4 * hq + 32 * gs, 64);
+                    for (int gs = 0; gs < 2; ++gs) {               // score head 4 hb + hq, group 2 sp + gs
+                        const int hs = 4 * hb + hq;
+                        const int es = hs < HPK ? sm_ge[wave][hs][2 * sp + gs] : 0;
                         gsc[hb][2 * sp + gs] = ldexp(kQScale64, es - 27);
                     }
                 }
