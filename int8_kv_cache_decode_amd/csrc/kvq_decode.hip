@@ -522,11 +522,14 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             const uint32_t rk = (uint32_t)min(r0 + n, it.row1 - 1);
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) t.kb2[sp] = ld_stream(KQ + kq_offset((int)rk, 64 * sp + 16 * (lane >> 4)));
+            // The 4-byte row scales of a 16-row tile fill half a 128-byte
+            // line, and the next tile reads the other half: plain loads keep
+            // the line in L2 for it.
             if constexpr (kI8)
-                t.ks4.x = ld_stream1(KS + rk);
+                t.ks4.x = KS[rk];
             else
                 t.ks4 = ld_stream(KS + rk * kKScales);
-            t.vsn = ld_stream1(VS + rk);
+            t.vsn = VS[rk];
 #pragma unroll
             for (int i = 0; i < kVLoads; ++i) {
                 const uint32_t rv = (uint32_t)min(r0 + ri + kVRows * i, it.row1 - 1);
