@@ -1281,9 +1281,9 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t p = (uint32_t)min(r0 + 4 * kb + r, it.row1 - 1);
-                    t.ks[r] = ld_stream1(KS + p);
+                    t.ks[r] = KS[p];                   // row scales: plain loads, as in k_decode_q8
                     ld_v(VQ + (p * kHD + 8 * qi), t.vc[r]);
-                    t.vs[r] = ld_stream1(VS + p);
+                    t.vs[r] = VS[p];
                 }
                 return;
             }
@@ -1300,9 +1300,9 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int p = min(r0 + 4 * kb + r, it.row1 - 1);
                 if (p < L) {
-                    t.ks[r] = ld_stream1(KS + p);
+                    t.ks[r] = KS[p];
                     ld_v(VQ + (size_t)p * kHD + 8 * qi, t.vc[r]);
-                    t.vs[r] = ld_stream1(VS + p);
+                    t.vs[r] = VS[p];
                 } else {
                     const size_t m = mrow(p);
                     t.ks[r] = a.kds[m];
