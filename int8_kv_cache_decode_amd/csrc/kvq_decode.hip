@@ -1535,14 +1535,15 @@ hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s) { return launch_
 namespace {
 
 // The query-batched launch: the kernel, then its combine.  which: the
-// resident-wave cache entry of the kernel; one share per wps resident waves.
+// resident-wave cache entry of the kernel; one share per wps resident waves,
+// or one per SIMD when wps is 0.
 hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int which, int wps, hipStream_t s) {
     VerifyArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {                          // zero only when every group is dead
-        const int wv = resident_waves(fn, which);
+        const int wv = wps ? resident_waves(fn, which) : simd_count();
         if (wv == 0) return hipErrorInvalidDevice;
-        const int shares = (wv + wps - 1) / wps;
+        const int shares = wps ? (wv + wps - 1) / wps : wv;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};
@@ -1573,14 +1574,16 @@ hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int whic
 // single-query decode.  Measured on MI355X (32k R-SWA reference): the f32
 // kernel (2 waves/SIMD) is fastest with one share per 2 resident waves
 // (verify 70.0 -> 68.0 us), the i8 kernel (3 waves/SIMD) with one per wave
-// (verify 43.1 us; 47.2 us with one per 2).
+// (verify 43.1 us; 47.2 us with one per 2, 44.9 against 39.7 us with one per
+// SIMD), except the shared decode, whose 16 queries per head double the
+// partials: one share per SIMD took it from 49.0 to 45.0 us.
 hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
     return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, s)
                     : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, s);
 }
 
 hipError_t launch_verify_i8(const VerifyArgs& a, hipStream_t s) {
-    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, 1, s)
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, 0, s)
                     : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, 1, s);
 }
 
