@@ -1451,8 +1451,9 @@ int resident_waves(const void* kernel, int which) {
     return v;
 }
 
-// SIMDs of the current device (compute units x 4), cached per device; 0 on
-// a runtime error.
+// SIMDs of the current device (compute units x 4), at most kMaxWaves (the
+// share bound the workspace is sized for); cached per device; 0 on a runtime
+// error.
 int simd_count() {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
@@ -1461,7 +1462,7 @@ int simd_count() {
     if (v == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        v = cus * 4;
+        v = cus < 1 ? 1 : (cus * 4 > kMaxWaves ? kMaxWaves : cus * 4);
         cache[dev].store(v, std::memory_order_relaxed);
     }
     return v;
