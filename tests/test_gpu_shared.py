@@ -31,9 +31,13 @@ def i8_head(k, v):
 
 
 def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0,
-               kind=K.KIND_F32):
+               kind=K.KIND_F32, spread=False):
     """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`;
-    kind KIND_I8: the int8 mirror (oracle: its codec and int8 decode)."""
+    kind KIND_I8: the int8 mirror (oracle: its codec and int8 decode).
+    spread: the step rows are 0 on channel 0 and every query is +-32 there
+    (sign alternating over the queries of a KV head) and 0 elsewhere, so a
+    reference row with 64 on channel 0 scores +-181 and every other row 0
+    (see tests/test_gpu_spread.py)."""
     r = np.random.default_rng(seed)
     W = K.RING_WINDOW
     pre = ref_k.shape[0]
@@ -60,6 +64,10 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
         q = (r.standard_normal((n_streams, hq, 128)) * step_scale).astype(np.float32)
         kt = (r.standard_normal((n_streams, hkv, 128)) * step_scale).astype(np.float32)
         vt = r.standard_normal((n_streams, hkv, 128)).astype(np.float32)
+        if spread:
+            kt[..., 0] = 0.0
+            q[:] = 0.0
+            q[..., 0] = np.where((np.arange(n_streams)[:, None] * hq + np.arange(hq)[None, :]) % 2 == 0, 32.0, -32.0)
         toks.append((kt, vt))
         K.rswa_shared_decode(c, seq, rings, n_streams, hq, dev(q), dev(kt), dev(vt), out)
         for s in range(n_streams):
@@ -68,6 +76,7 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
         if t in check:
             torch.cuda.synchronize()
             got = host(out)
+            assert np.isfinite(got).all()
             units = []
             for s in range(n_streams):
                 win = models[s].window()
@@ -154,3 +163,19 @@ def test_shared_workload_rswa_long_16_streams(kind):
     rk, rv = spec.reference()
     shared_run(rk.transpose(1, 0, 2).copy(), rv.transpose(1, 0, 2).copy(), n_streams=16, hkv=spec.n_heads, hpk=1,
                steps=200, check={0, 127, 128, 199}, seed=830, seq=0, batch=1, kind=kind)
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_shared_extreme_score_spread(kind):
+    """Four streams x GQA group 4 (16 queries per KV head) over a 300-row
+    reference holding one spike row per KV head (64 on channel 0, every
+    other row 0 there); 140 steps, so the rings wrap."""
+    say("case: shared spread kind", kind)
+    r = np.random.default_rng(930)
+    hkv, pre = 2, 300
+    ref_k, ref_v = r.standard_normal((2, pre, hkv, 128)).astype(np.float32)
+    ref_k[:, :, 0] = 0.0
+    ref_k[17, 0, 0] = 64.0
+    ref_k[45, 1, 0] = 64.0
+    shared_run(ref_k, ref_v, n_streams=4, hkv=hkv, hpk=4, steps=140, check={0, 70, 139}, seed=931, kind=kind,
+               spread=True)
