@@ -469,3 +469,16 @@ def test_int8_verify_workspace_holds_the_draft_mirror():
     bq = snapshot(q, rings)
     expect(call("rswa_verify", q.ref, rings.ref, 8, 5, FAKE, FAKE, FAKE, FAKE, FAKE, wi, None), K.ESTATE,
            q, bq, rings)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark has no multi-GPU path: --gpus 2 exits non-zero with a
+    message, before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
