@@ -197,31 +197,6 @@ def main():
         log("q8 cache ready: %d rows, %.2f GB stored (i8: %.2f GB)" % (
             int(lens.sum()), cq.cache_bytes() / 1e9, ci8.cache_bytes() / 1e9))
 
-    def step(i):
-        if do_rswa:
-            c, rings, out = rswa[i % len(rswa)]
-            q, kk, vv = pool[i % 16]
-            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
-        if do_q8:
-            K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
-            K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # positions attended per step (context rows per sequence)
-    pos_rswa = (rs.prefill + rs.window) if do_rswa else 0
-    pos_q8 = int(cq.len.sum()) if do_q8 else 0
-    positions = pos_rswa + pos_q8
-    value = positions / (ms_per_step / 1e3)
-
     # ---------------- per-part kernel timing with HIP events ----------------
     # 5 untimed calls, then 5 repeats of n back-to-back calls, each bracketed
     # by two events on the launch stream; the median repeat's average call.
@@ -397,6 +372,40 @@ def main():
         if int(cq.len.max()) + 40 <= cq.capacity:
             parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 5, repeats=1), 2)}
 
+    # ---------------- the timed decode steps ----------------
+    # They run after the per-part timing above, so the GPU's clocks have
+    # settled when the warm-up steps start (measured: the same step took
+    # 485 us after 5 warm-up steps on a cold GPU and 450 us after 100).
+    def step(i):
+        if do_rswa:
+            c, rings, out = rswa[i % len(rswa)]
+            q, kk, vv = pool[i % 16]
+            K.rswa_decode(c, rings, rs.n_heads, q, kk, vv, out)
+        if do_q8:
+            K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
+            K.decode_attn_q8(cq, bq.n_q_heads, qq, qout, ws_q8)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # positions attended per step (context rows per sequence)
+    pos_rswa = (rs.prefill + rs.window) if do_rswa else 0
+    pos_q8 = int(cq.len.sum()) if do_q8 else 0
+    positions = pos_rswa + pos_q8
+    value = positions / (ms_per_step / 1e3)
+    # the step's calls timed on their own (back-to-back calls of each entry
+    # point): their sum beside ms_per_step shows what the step adds
+    parts_sum_us = round(sum(parts[k]["us_per_call"] for k in ("rswa_decode_f32", "decode_attn_q8",
+                                                                 "kv_append_q8_one_row") if k in parts), 2)
+
+    if do_q8:
         # [P2] trim_window over every sequence (window 8192, slack 64, align 64):
         # runs once, last, since it shortens the cache.  Bytes: each kept row
         # of each live head read and written once.
@@ -434,6 +443,7 @@ def main():
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "parts_sum_us": parts_sum_us,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32+i8",
         "data": "synthetic (seeded SplitMix64 / Box-Muller; no datasets or weights)",
         "config": {"workload": "decode step: " + " + ".join(
@@ -563,7 +573,15 @@ def cpu_baseline(args, rs, bq, do_rswa, do_q8):
     timed).  Reported in the same unit, KV positions/s."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
-    threads = min(16, os.cpu_count() or 1)
+    # The host's core count is reported; the oracle runs one worker per core
+    # of this process's CPU share (at most 16: a one-GPU job's share of the
+    # host, which a larger pool would oversubscribe).
+    host_cores = os.cpu_count() or 1
+    try:
+        share = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        share = host_cores
+    threads = max(1, min(16, share))
     units_r, q_r, units_q, q_q = None, None, None, None
     positions = 0
     if do_rswa:
@@ -623,6 +641,7 @@ def cpu_baseline(args, rs, bq, do_rswa, do_q8):
         sample.append("batched_q8: sequences 0..%d of 64 (%d rows x 8 KV heads x 4 Q heads)"
                       % (args.cpu_sample_seqs - 1, pos_rep - (rs.prefill + rs.window if do_rswa else 0)))
     return {"value": round(positions / wall, 1), "unit": "KV positions/s", "cores": threads,
+            "host_cores": host_cores, "cpu_affinity": share,
             "kind": "oracle", "sample": "; ".join(sample) + "; float64 oracle, repeated %d times, %.2f s wall"
             % (reps, wall),
             "single_core_value": round(pos_rep / wall1, 1), "cpu_model": model}

@@ -141,8 +141,10 @@ typedef struct kvq_ring {
 } kvq_ring;
 
 /*
- * A checkpoint of one sequence's ring cursors ([P3] RingCheckpoint): the
- * cache and sequence it belongs to, and the cursors.  No K/V is copied.
+ * A checkpoint of one ring's cursors ([P3] RingCheckpoint): the cache,
+ * sequence and stream it belongs to, and the cursors.  No K/V is copied.
+ * `stream` is -1 for the ring of a sequence (rswa_checkpoint) and the
+ * stream index for a stream of a shared reference (rswa_shared_checkpoint).
  */
 typedef struct kvq_ring_checkpoint {
     const kvq_cache* cache;
@@ -151,7 +153,7 @@ typedef struct kvq_ring_checkpoint {
     int32_t ring_len;
     int32_t ring_pos;
     int32_t epoch;
-    int32_t reserved;
+    int32_t stream;
     int64_t writes;
 } kvq_ring_checkpoint;
 
@@ -305,9 +307,10 @@ int decode_attn_i8(const kvq_cache* c, int n_q_heads, const float* q, float* out
  * softcap  > 0: every scaled score s becomes softcap * tanh(s / softcap)
  *          (Gemma-2 soft-capping) before the softmax; 0 = off.
  * sinks    device float [n_q_heads], or NULL for none: one learned logit per
- *          Q head (same for every sequence).  It joins the softmax max and
- *          adds exp(sink - max) to the denominator; it has no value row and
- *          is not soft-capped.  A sequence with no rows still gives zeros.
+ *          Q head (same for every sequence).  The softmax treats it as one
+ *          more logit that carries no value: it takes part in the maximum
+ *          and contributes exp(sink - max) to the normaliser; it is not
+ *          soft-capped.  A sequence with no rows still gives zeros.
  * The struct is read during the call only; `first` is copied into the
  * launch, so the caller may reuse it once the call returns.
  */
@@ -389,7 +392,8 @@ int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring
  * matching.  Refused, with nothing changed, when the checkpoint belongs to
  * another cache or sequence, another prefill or epoch, is from the future,
  * or when the discarded writes overwrote a slot that was live at the
- * checkpoint (cp->ring_len + discarded > 128).  No device work.
+ * checkpoint (cp->ring_len + discarded > 128), or when *cp is a shared
+ * stream's checkpoint (cp->stream != -1).  No device work.
  * Errors: KVQ_EINVAL (null, seq out of range), KVQ_ESTATE (a q8 cache, or
  * any refusal above).
  */
@@ -489,10 +493,40 @@ int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_str
  * outside 1..16, workspace too small), KVQ_ESTATE (a q8 cache, group
  * not recorded, len[seq] no longer prefill + 128 n_streams, a stream with
  * another prefill or corrupt cursors).  Nothing is written on error.
- * Checkpoint / rollback of these streams is not provided.
  */
 int rswa_shared_decode(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, int n_q_heads, const float* q,
                        const float* k_new, const float* v_new, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * rswa_shared_checkpoint -- [P3] BatchedRingCache::checkpoint: the cursors
+ * of stream `s` (0 <= s < n_streams) of the shared group recorded on
+ * sequence `seq` (rswa_shared_record_prefill), copied into *cp (host), with
+ * cp->stream = s.  Each stream is checkpointed on its own.  O(1), no device
+ * work.
+ * Errors: KVQ_EINVAL (null, seq or s out of range, n_streams outside
+ * 1..16), KVQ_ESTATE (a q8 cache, a group not recorded, or len[seq] not
+ * prefill + 128 n_streams).
+ */
+int rswa_shared_checkpoint(const kvq_cache* c, int seq, const kvq_ring* rings, int n_streams, int s,
+                           kvq_ring_checkpoint* cp);
+
+/*
+ * rswa_shared_rollback_to -- [P3] BatchedRingCache::rollback_to: stream s
+ * of the shared group on sequence `seq` goes back to *cp under the
+ * lossless contract of rswa_rollback_to (ring_len, ring_pos and writes
+ * restored; a rollback that discards writes advances the stream's epoch).
+ * No other stream and no row of the cache changes (len[seq] stays prefill
+ * + 128 n_streams: the rings' rows stay reserved), and nothing runs on the
+ * device.  Refused, with nothing changed, when the checkpoint belongs to
+ * another cache, sequence or stream, another prefill or epoch, is from the
+ * future, or would need a ring row the discarded writes overwrote
+ * (cp->ring_len + discarded > 128).
+ * Errors: KVQ_EINVAL (null, seq or s out of range, n_streams outside
+ * 1..16), KVQ_ESTATE (a q8 cache, a group not recorded, len[seq] not
+ * prefill + 128 n_streams, or any refusal above).
+ */
+int rswa_shared_rollback_to(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, int s,
+                            const kvq_ring_checkpoint* cp);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* kvq_last_error(void);

@@ -307,6 +307,61 @@ int run_decode(const kvq_cache* c, int n_q_heads, int hpk, const float* q, float
     return KVQ_OK;
 }
 
+// [P3] RingCache::checkpoint: the cursors of one ring.
+void take_checkpoint(const kvq_cache* c, const kvq_ring& r, int seq, int stream, kvq_ring_checkpoint* cp) {
+    cp->cache = c;
+    cp->seq = seq;
+    cp->prefill_len = r.prefill_len;
+    cp->ring_len = r.ring_len;
+    cp->ring_pos = r.ring_pos;
+    cp->epoch = r.epoch;
+    cp->stream = stream;
+    cp->writes = r.writes;
+}
+
+// [P3] RingCache::rollback_to on one ring whose checkpoint identity the
+// caller has checked: the page's refusals, in its order, before any change;
+// then the cursors are restored, and a rollback that discards writes starts
+// a new lineage.
+int rollback_ring(kvq_ring& r, const kvq_ring_checkpoint* cp, const char* fn) {
+    if (cp->prefill_len != r.prefill_len)
+        return fail(KVQ_ESTATE, "%s: checkpoint prefill_len %d != %d", fn, cp->prefill_len, r.prefill_len);
+    if (cp->epoch != r.epoch)
+        return fail(KVQ_ESTATE, "%s: stale checkpoint lineage (epoch %d != %d)", fn, cp->epoch, r.epoch);
+    if (cp->writes > r.writes)
+        return fail(KVQ_ESTATE, "%s: checkpoint is from the future (writes %lld > %lld)", fn, (long long)cp->writes,
+                    (long long)r.writes);
+    const int64_t discarded = r.writes - cp->writes;
+    if (cp->ring_len < 0 || cp->ring_len > KVQ_RING_WINDOW || discarded > KVQ_RING_WINDOW - cp->ring_len)
+        return fail(KVQ_ESTATE, "%s: not lossless: %lld discarded writes wrapped the ring past ring_len %d", fn,
+                    (long long)discarded, cp->ring_len);
+    if (cp->ring_pos < 0 || cp->ring_pos >= KVQ_RING_WINDOW)
+        return fail(KVQ_ESTATE, "%s: checkpoint ring_pos %d outside 0..%d", fn, cp->ring_pos, KVQ_RING_WINDOW - 1);
+    if (discarded > 0 && r.epoch == INT32_MAX) return fail(KVQ_ESTATE, "%s: lineage epoch exhausted", fn);
+    r.ring_len = cp->ring_len;
+    r.ring_pos = cp->ring_pos;
+    r.writes = cp->writes;
+    if (discarded > 0) r.epoch += 1;
+    return KVQ_OK;
+}
+
+// A shared group's stream s: the cache kind, the indices, and a group that
+// is recorded on sequence seq with n_streams rings.
+int check_shared_stream(const kvq_cache* c, int seq, const kvq_ring* rings, int n_streams, int s, const char* fn) {
+    const int rc = check_ring_cache(c, fn);
+    if (rc) return rc;
+    if (!rings) return fail(KVQ_EINVAL, "%s: null rings", fn);
+    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if (n_streams < 1 || n_streams > kVerifyMaxQ)
+        return fail(KVQ_EINVAL, "%s: n_streams %d outside 1..%d", fn, n_streams, kVerifyMaxQ);
+    if (s < 0 || s >= n_streams) return fail(KVQ_EINVAL, "%s: stream %d outside 0..%d", fn, s, n_streams - 1);
+    const int pre = rings[s].prefill_len;
+    if (pre < 0) return fail(KVQ_ESTATE, "%s: stream %d: group not recorded", fn, s);
+    if ((int64_t)c->len[seq] != (int64_t)pre + (int64_t)KVQ_RING_WINDOW * n_streams)
+        return fail(KVQ_ESTATE, "%s: len %d != prefill %d + %d rings", fn, c->len[seq], pre, n_streams);
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -553,21 +608,14 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq) {
     return KVQ_OK;
 }
 
+
 int rswa_checkpoint(const kvq_cache* c, const kvq_ring* rings, int seq, kvq_ring_checkpoint* cp) {
     const char* fn = "rswa_checkpoint";
     int rc = check_ring_cache(c, fn);
     if (rc) return rc;
     if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
     if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
-    const kvq_ring& r = rings[seq];
-    cp->cache = c;
-    cp->seq = seq;
-    cp->prefill_len = r.prefill_len;
-    cp->ring_len = r.ring_len;
-    cp->ring_pos = r.ring_pos;
-    cp->epoch = r.epoch;
-    cp->reserved = 0;
-    cp->writes = r.writes;
+    take_checkpoint(c, rings[seq], seq, -1, cp);
     return KVQ_OK;
 }
 
@@ -577,28 +625,34 @@ int rswa_rollback_to(kvq_cache* c, kvq_ring* rings, int seq, const kvq_ring_chec
     if (rc) return rc;
     if (!rings || !cp) return fail(KVQ_EINVAL, "%s: null rings/checkpoint", fn);
     if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    if (cp->cache != c || cp->seq != seq || cp->stream != -1)
+        return fail(KVQ_ESTATE, "%s: checkpoint belongs to another cache, sequence or a shared stream", fn);
     kvq_ring& r = rings[seq];
-    // [P3] rollback_to: the refusals, in the page's order, before any change
-    if (cp->cache != c || cp->seq != seq)
-        return fail(KVQ_ESTATE, "%s: checkpoint belongs to another cache or sequence", fn);
-    if (cp->prefill_len != r.prefill_len)
-        return fail(KVQ_ESTATE, "%s: checkpoint prefill_len %d != %d", fn, cp->prefill_len, r.prefill_len);
-    if (cp->epoch != r.epoch)
-        return fail(KVQ_ESTATE, "%s: stale checkpoint lineage (epoch %d != %d)", fn, cp->epoch, r.epoch);
-    if (cp->writes > r.writes)
-        return fail(KVQ_ESTATE, "%s: checkpoint is from the future (writes %lld > %lld)", fn, (long long)cp->writes,
-                    (long long)r.writes);
-    const int64_t discarded = r.writes - cp->writes;
-    if (cp->ring_len < 0 || cp->ring_len > KVQ_RING_WINDOW || discarded > KVQ_RING_WINDOW - cp->ring_len)
-        return fail(KVQ_ESTATE, "%s: not lossless: %lld discarded writes wrapped the ring past ring_len %d", fn,
-                    (long long)discarded, cp->ring_len);
-    if (discarded > 0 && r.epoch == INT32_MAX) return fail(KVQ_ESTATE, "%s: lineage epoch exhausted", fn);
-    r.ring_len = cp->ring_len;
-    r.ring_pos = cp->ring_pos;
-    r.writes = cp->writes;
-    if (discarded > 0) r.epoch += 1;
+    if ((rc = rollback_ring(r, cp, fn))) return rc;
     c->len[seq] = r.prefill_len + r.ring_len;
     return KVQ_OK;
+}
+
+int rswa_shared_checkpoint(const kvq_cache* c, int seq, const kvq_ring* rings, int n_streams, int s,
+                           kvq_ring_checkpoint* cp) {
+    const char* fn = "rswa_shared_checkpoint";
+    if (!cp) return fail(KVQ_EINVAL, "%s: null checkpoint", fn);
+    const int rc = check_shared_stream(c, seq, rings, n_streams, s, fn);
+    if (rc) return rc;
+    take_checkpoint(c, rings[s], seq, s, cp);
+    return KVQ_OK;
+}
+
+int rswa_shared_rollback_to(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, int s,
+                            const kvq_ring_checkpoint* cp) {
+    const char* fn = "rswa_shared_rollback_to";
+    if (!cp) return fail(KVQ_EINVAL, "%s: null checkpoint", fn);
+    const int rc = check_shared_stream(c, seq, rings, n_streams, s, fn);
+    if (rc) return rc;
+    if (cp->cache != c || cp->seq != seq || cp->stream != s)
+        return fail(KVQ_ESTATE, "%s: checkpoint belongs to another cache, sequence or stream", fn);
+    // the rings' rows stay reserved: len[seq] does not move
+    return rollback_ring(rings[s], cp, fn);
 }
 
 int kv_truncate_last(kvq_cache* c, int seq, int n_drop) {

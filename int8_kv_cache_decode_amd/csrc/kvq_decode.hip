@@ -941,7 +941,8 @@ __device__ __forceinline__ bool combine_partials(const float* ml, const float* a
     }
     __syncthreads();
     if (tid >= lpg) return false;
-    // a learned sink joins the max and the denominator ([P2] attend_group_upto)
+    // the sink logit enters the running max and the normaliser, with no V
+    // row ([P2] attend_group_upto)
     float Mt = zs;
     for (int k = 0; k < nwaves; ++k) Mt = fmaxf(Mt, sm_m[k]);
     float Lt = zs == -INFINITY ? 0.0f : fast_exp2(zs - Mt);
@@ -1133,10 +1134,34 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
             m = mnew;
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
+            // Shared decode: a ring row that no stream may read -- a slot never
+            // written since the prefill (its memory may hold anything, NaN
+            // included), or the slot this step overwrites -- enters the value
+            // product as zeros, so that a zero weight times it stays zero.  A
+            // tile that reaches into the rings (wave-uniform) spans at most two
+            // streams' rings; their cursors come through scalar loads (per-lane
+            // loads of them would wait behind the prefetched tile's loads).
+            bool ok[4] = {true, true, true, true};
+            if (kShared && r0 + kTileRows > pre && r0 < L) {
+                const int s_lo = __builtin_amdgcn_readfirstlane(max(0, (r0 - pre) >> 7));
+                const int s_hi = __builtin_amdgcn_readfirstlane(min(a.n_draft - 1, (r0 + kTileRows - 1 - pre) >> 7));
+                const int live_lo = a.sring[s_lo], live_hi = a.sring[s_hi];
+                const int over_lo = a.swrow[s_lo] - pre - KVQ_RING_WINDOW * s_lo;
+                const int over_hi = a.swrow[s_hi] - pre - KVQ_RING_WINDOW * s_hi;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int p = r0 + 4 * kb + s2;
+                    const int rs = (p - pre) >> 7, slot = (p - pre) & (KVQ_RING_WINDOW - 1);
+                    const int lv = rs == s_lo ? live_lo : live_hi, ov = rs == s_lo ? over_lo : over_hi;
+                    ok[s2] = p < pre || p >= L || (slot < lv && slot != ov);
+                }
+            }
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
-                const float vv[8] = {t.vt[s2][0].x, t.vt[s2][0].y, t.vt[s2][0].z, t.vt[s2][0].w,
-                                     t.vt[s2][1].x, t.vt[s2][1].y, t.vt[s2][1].z, t.vt[s2][1].w};
+                float vv[8] = {t.vt[s2][0].x, t.vt[s2][0].y, t.vt[s2][0].z, t.vt[s2][0].w,
+                               t.vt[s2][1].x, t.vt[s2][1].y, t.vt[s2][1].z, t.vt[s2][1].w};
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) vv[cb] = ok[s2] ? vv[cb] : 0.0f;
 #pragma unroll
                 for (int cb = 0; cb < 8; ++cb)
                     acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[cb], pw[s2], acc[cb], 0, 0, 0);
@@ -1344,7 +1369,9 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
-                const float pv = pw[s2] * t.vs[s2];
+                // a row this query does not see weighs exactly 0: its V scale
+                // (of a never-written ring slot, say) never enters the product
+                const float pv = vis[s2] ? pw[s2] * t.vs[s2] : 0.0f;
                 float vv[8];
                 unpack(t.vc[s2], vv);
 #pragma unroll

@@ -51,7 +51,7 @@ class kvq_ring(ctypes.Structure):
 class kvq_ring_checkpoint(ctypes.Structure):
     _fields_ = [("cache", _P), ("seq", ctypes.c_int32), ("prefill_len", ctypes.c_int32),
                 ("ring_len", ctypes.c_int32), ("ring_pos", ctypes.c_int32), ("epoch", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("writes", ctypes.c_int64)]
+                ("stream", ctypes.c_int32), ("writes", ctypes.c_int64)]
 
 
 class kvq_decode_opts(ctypes.Structure):
@@ -88,6 +88,8 @@ _SIGNATURES = [
     ("rswa_shared_record_prefill", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int]),
     ("rswa_shared_decode", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    ("rswa_shared_checkpoint", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P]),
+    ("rswa_shared_rollback_to", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P]),
     ("kvq_last_error", ctypes.c_char_p, []),
 ]
 
@@ -375,3 +377,15 @@ def rswa_shared_decode(cache: KvCache, seq: int, rings: Rings, n_streams: int, n
     nb = ws.numel() if ws_bytes is None else ws_bytes
     _check(lib().rswa_shared_decode(cache.ref, seq, rings.ref, n_streams, n_q_heads, _ptr(q), _ptr(k_new),
                                     _ptr(v_new), _ptr(out), _ptr(ws), nb, _stream(stream)))
+
+
+def rswa_shared_checkpoint(cache: KvCache, seq: int, rings: Rings, n_streams: int, s: int) -> kvq_ring_checkpoint:
+    cp = kvq_ring_checkpoint()
+    _check(lib().rswa_shared_checkpoint(cache.ref, seq, rings.ref, n_streams, s, ctypes.byref(cp)))
+    return cp
+
+
+def rswa_shared_rollback_to(cache: KvCache, seq: int, rings: Rings, n_streams: int, s: int,
+                            cp: kvq_ring_checkpoint) -> None:
+    _check(lib().rswa_shared_rollback_to(cache.ref, seq, rings.ref, n_streams, s, ctypes.byref(cp)))
+

@@ -160,6 +160,12 @@ class Q8Head:
         if rc != 0:
             raise ValueError("oracle q8 append: capacity exceeded")
 
+    def truncate_last(self, n_drop: int) -> None:
+        """[P2] LayerKvCache::truncate_last on this head: the last
+        min(n_drop, n) rows are dropped; the column fields stay as they are
+        (a frozen field stays frozen, so later rows quantise against it)."""
+        self._n.value = truncate_last(self.n, n_drop)
+
     def freeze(self) -> bool:
         return bool(_load().orc_q8_freeze_head(
             self.hd, _p(self.kq), _p(self.ks), _p(self.vq), _p(self.vs),
@@ -209,6 +215,11 @@ class I8Head:
             _load().orc_quant_rows_i8(n_new, self.hd, _p(np.ascontiguousarray(src)), _p(qq), _p(ss))
             q[n0:n0 + n_new], sc[n0:n0 + n_new] = qq, ss
         self.n += n_new
+
+    def truncate_last(self, n_drop: int) -> None:
+        """[P2] LayerKvCache::truncate_last: the last min(n_drop, n) rows are
+        dropped (per-row codes do not depend on other rows)."""
+        self.n = truncate_last(self.n, n_drop)
 
     def dequant_k(self) -> np.ndarray:
         return self.kq[: self.n].astype(np.float64) * self.ks[: self.n, None].astype(np.float64)

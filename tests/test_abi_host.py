@@ -449,6 +449,100 @@ def test_shared_reference_record_and_refusals():
            K.ESTATE, c, before, rings)
 
 
+def shared_group(kind=K.KIND_F32, n_streams=4, pre=100):
+    c = fake_cache(kind, batch=2, hkv=10, cap=pre + 128 * 16)
+    rings = K.Rings(16)
+    c.len[:] = [pre, 7]
+    assert call("rswa_shared_record_prefill", c.ref, 0, rings.ref, n_streams) == K.OK
+    return c, rings
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_shared_checkpoint_and_rollback_cursors(kind):
+    """[P3] BatchedRingCache::checkpoint / rollback_to: per stream, on the
+    single-stream rules; the page's 9-accept / 6-draft example on stream 2
+    of 4 leaves every other stream and the reserved rows as they were."""
+    c, rings = shared_group(kind)
+    e0 = [rings[s].epoch for s in range(4)]
+    for s in range(4):
+        rings[s].ring_len, rings[s].ring_pos, rings[s].writes = 9, 9, 9
+    cp = K.rswa_shared_checkpoint(c, 0, rings, 4, 2)
+    assert (cp.prefill_len, cp.ring_len, cp.ring_pos, cp.writes, cp.epoch, cp.seq, cp.stream) == \
+        (100, 9, 9, 9, e0[2], 0, 2)
+    for s in range(4):
+        rings[s].ring_len, rings[s].ring_pos, rings[s].writes = 15, 15, 15
+    K.rswa_shared_rollback_to(c, 0, rings, 4, 2, cp)
+    assert (rings[2].ring_len, rings[2].ring_pos, rings[2].writes, rings[2].epoch) == (9, 9, 9, e0[2] + 1)
+    for s in (0, 1, 3):
+        assert (rings[s].ring_len, rings[s].ring_pos, rings[s].writes, rings[s].epoch) == (15, 15, 15, e0[s])
+    assert c.len[0] == 100 + 4 * 128 and c.len[1] == 7
+    cp2 = K.rswa_shared_checkpoint(c, 0, rings, 4, 2)
+    K.rswa_shared_rollback_to(c, 0, rings, 4, 2, cp2)          # nothing discarded: same lineage
+    assert (rings[2].ring_len, rings[2].writes, rings[2].epoch) == (9, 9, e0[2] + 1)
+    # steady state: a rollback of 128 - ring_len writes or fewer is lossless
+    rings[1].ring_len, rings[1].ring_pos, rings[1].writes = 128, 5, 300
+    cp1 = K.rswa_shared_checkpoint(c, 0, rings, 4, 1)
+    rings[1].ring_pos, rings[1].writes = 6, 301
+    with pytest.raises(K.KvqError):
+        K.rswa_shared_rollback_to(c, 0, rings, 4, 1, cp1)
+
+
+def test_shared_rollback_refusals_leave_everything_unchanged():
+    """The refusals of a shared stream's rollback, each before any change:
+    a checkpoint of another cache, sequence or stream, of a single-sequence
+    ring (and a stream's checkpoint on rswa_rollback_to), a stale lineage,
+    a checkpoint from the future, discarded writes past the free slots,
+    indices out of range, a group not recorded or resized, a q8 cache."""
+    c, rings = shared_group()
+    other, orings = shared_group()
+    for s in range(4):
+        rings[s].ring_len, rings[s].ring_pos, rings[s].writes = 20, 20, 20
+        orings[s].ring_len, orings[s].ring_pos, orings[s].writes = 20, 20, 20
+    cp = K.rswa_shared_checkpoint(c, 0, rings, 4, 1)
+    for s in range(4):
+        rings[s].ring_len, rings[s].ring_pos, rings[s].writes = 30, 30, 30
+    before = snapshot(c, rings)
+
+    def refused(code, *args):
+        expect(call("rswa_shared_rollback_to", c.ref, *args), code, c, before, rings)
+
+    foreign = K.rswa_shared_checkpoint(other, 0, orings, 4, 1)
+    refused(K.ESTATE, 0, rings.ref, 4, 1, ctypes.byref(foreign))
+    refused(K.ESTATE, 0, rings.ref, 4, 2, ctypes.byref(cp))                 # another stream
+    wrong_seq = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+    wrong_seq.seq = 1
+    refused(K.ESTATE, 0, rings.ref, 4, 1, ctypes.byref(wrong_seq))
+    single = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+    single.stream = -1
+    refused(K.ESTATE, 0, rings.ref, 4, 1, ctypes.byref(single))
+    expect(call("rswa_rollback_to", c.ref, rings.ref, 0, ctypes.byref(cp)), K.ESTATE, c, before, rings)
+    for field, delta in (("epoch", -1), ("writes", 100), ("prefill_len", 1)):
+        bad = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+        setattr(bad, field, getattr(bad, field) + delta)
+        refused(K.ESTATE, 0, rings.ref, 4, 1, ctypes.byref(bad))
+    wrapped = K.kvq_ring_checkpoint.from_buffer_copy(cp)
+    wrapped.ring_len = 120                       # 10 discarded writes > 128 - 120 free slots
+    refused(K.ESTATE, 0, rings.ref, 4, 1, ctypes.byref(wrapped))
+    refused(K.EINVAL, 0, rings.ref, 4, 1, None)
+    refused(K.EINVAL, 0, rings.ref, 4, 4, ctypes.byref(cp))                 # stream out of range
+    refused(K.EINVAL, 0, rings.ref, 17, 1, ctypes.byref(cp))
+    refused(K.EINVAL, 2, rings.ref, 4, 1, ctypes.byref(cp))                 # seq out of range
+    refused(K.ESTATE, 0, rings.ref, 3, 1, ctypes.byref(cp))                 # len != prefill + 128 x 3
+    refused(K.EINVAL, 0, None, 4, 1, ctypes.byref(cp))
+    out = K.kvq_ring_checkpoint()
+    expect(call("rswa_shared_checkpoint", c.ref, 0, rings.ref, 3, 1, ctypes.byref(out)), K.ESTATE, c, before, rings)
+    expect(call("rswa_shared_checkpoint", c.ref, 0, rings.ref, 4, 1, None), K.EINVAL, c, before, rings)
+    fresh = fake_cache(K.KIND_F32, batch=2, hkv=10, cap=3000)
+    frings = K.Rings(4)
+    fresh.len[:] = [100 + 4 * 128, 0]
+    bf = snapshot(fresh, frings)
+    expect(call("rswa_shared_checkpoint", fresh.ref, 0, frings.ref, 4, 0, ctypes.byref(out)), K.ESTATE,
+           fresh, bf, frings)                                               # group not recorded
+    q = fake_cache(K.KIND_Q8, batch=2, hkv=10, cap=3000)
+    bq = snapshot(q, rings)
+    expect(call("rswa_shared_rollback_to", q.ref, 0, rings.ref, 4, 1, ctypes.byref(cp)), K.ESTATE, q, bq, rings)
+
+
 def test_int8_verify_workspace_holds_the_draft_mirror():
     """On the per-row int8 kind the verify workspace also holds the drafts'
     int8 mirror (batch x drafts x KV heads rows of 2 x (128 codes + a

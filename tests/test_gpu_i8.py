@@ -30,15 +30,15 @@ def rng(seed):
 
 
 def assert_i8_codes_equal(c, b, heads, alive, n):
-    kq, ks, vq, vs = (host(c.view(nm)) for nm in ("kq", "ks", "vq", "vs"))
+    kq, ks, vq, vs = (host(c.view(nm)[b]) for nm in ("kq", "ks", "vq", "vs"))     # sequence b only
     gl = 0
     for g, live in enumerate(alive):
         if not live:
             continue
         h = heads[g]
-        assert np.array_equal(kq[b, gl, :n], h.kq[:n]) and np.array_equal(vq[b, gl, :n], h.vq[:n]), (b, g)
-        assert np.array_equal(ks[b, gl, :n].view(np.uint32), h.ks[:n].view(np.uint32)), (b, g)
-        assert np.array_equal(vs[b, gl, :n].view(np.uint32), h.vs[:n].view(np.uint32)), (b, g)
+        assert np.array_equal(kq[gl, :n], h.kq[:n]) and np.array_equal(vq[gl, :n], h.vq[:n]), (b, g)
+        assert np.array_equal(ks[gl, :n].view(np.uint32), h.ks[:n].view(np.uint32)), (b, g)
+        assert np.array_equal(vs[gl, :n].view(np.uint32), h.vs[:n].view(np.uint32)), (b, g)
         gl += 1
 
 
@@ -143,9 +143,9 @@ def test_i8_workload_batched():
         for b, (k, v, hs) in enumerate(ex.map(build, range(spec.batch))):
             append_rows(c, b, k, v)
             units[b] = [("i8", h) for h in hs]
-            if b % 16 == 0:
-                torch.cuda.synchronize()
-                assert_i8_codes_equal(c, b, hs, [1] * spec.n_kv_heads, int(lens[b]))
+            # every sequence's codes and row scales, bit for bit
+            torch.cuda.synchronize()
+            assert_i8_codes_equal(c, b, hs, [1] * spec.n_kv_heads, int(lens[b]))
     q = spec.query()
     out = torch.full((spec.batch, spec.n_q_heads, 128), np.nan, device="cuda")
     K.decode_attn_i8(c, spec.n_q_heads, dev(q), out)

@@ -3,7 +3,8 @@ trim_window_anchored; [P3] RingCache::checkpoint / rollback_to) through the
 C ABI.  Moved rows, codes and scales are compared bit for bit with the rows
 they came from; decodes after a trim, a truncate or a rollback are compared
 with the oracle over the rows the pages say stay visible, or bit for bit
-with a control cache that never took the detour."""
+with a control cache that never took the detour, and with the oracle's
+stores / ring model taken through the same truncate or rollback."""
 import numpy as np
 import pytest
 import torch
@@ -142,13 +143,40 @@ def test_truncate_then_append_equals_never_appended(kind):
     for nm in BUFS[kind]:
         a, b = host(test.view(nm)), host(ctrl.view(nm))
         assert np.array_equal(a[:, :, :n].view(np.uint8), b[:, :, :n].view(np.uint8)), nm
-    q = dev(r.standard_normal((1, hkv * hpk, 128)).astype(np.float32))
+    qh = r.standard_normal((1, hkv * hpk, 128)).astype(np.float32)
+    q = dev(qh)
     o1, o2 = (torch.full((1, hkv * hpk, 128), np.nan, device="cuda") for _ in range(2))
     fn = DECODE[kind]
     fn(test, hkv * hpk, q, o1)
     fn(ctrl, hkv * hpk, q, o2)
     torch.cuda.synchronize()
     assert np.array_equal(host(o1).view(np.uint32), host(o2).view(np.uint32))
+    # against the oracle: its stores take the same appends and the page's
+    # truncate (q8: the rejected rows were quantised against the frozen
+    # field, which stays), then decode by definition
+    units = [[None] * hkv]
+    for g in range(hkv):
+        if kind == K.KIND_F32:
+            units[0][g] = ("f32", np.concatenate([base_k[:, g], final[0][:, g]]),
+                           np.concatenate([base_v[:, g], final[1][:, g]]))
+            continue
+        h = oracle.Q8Head(cap=200) if kind == K.KIND_Q8 else oracle.I8Head(cap=200)
+        h.append(base_k[:, g], base_v[:, g])
+        h.append(draft[0][:, g], draft[1][:, g])
+        h.truncate_last(5)
+        h.append(final[0][:, g], final[1][:, g])
+        assert h.n == n
+        units[0][g] = ("q8" if kind == K.KIND_Q8 else "i8", h)
+    if kind == K.KIND_Q8:
+        assert_codes_equal(test, 0, [u[1] for u in units[0]], [1] * hkv, n)
+    elif kind == K.KIND_I8:
+        kq, ks = host(test.view("kq"))[0], host(test.view("ks"))[0]
+        for g in range(hkv):
+            assert np.array_equal(kq[g, :n], units[0][g][1].kq[:n])
+            assert np.array_equal(ks[g, :n].view(np.uint32), units[0][g][1].ks[:n].view(np.uint32))
+    err = max_err(host(o1), oracle.decode(qh, units, hkv, threads=THREADS))
+    say("  truncate kind %d max err %.3g" % (kind, err))
+    assert err <= F32_TOL, err
 
 
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
@@ -168,20 +196,51 @@ def test_rswa_rollback_restores_the_accepted_path(kind):
     for cc, rr in ((test, rt), (ctrl, rc)):
         append_rows(cc, 0, ref[0], ref[1])
         K.rswa_record_prefill(cc, rr, 0)
-    acc = [tuple(dev(r.standard_normal((1, nh, 128)).astype(np.float32)) for _ in range(3)) for _ in range(14)]
-    drafts = [tuple(dev(r.standard_normal((1, nh, 128)).astype(np.float32) + 3) for _ in range(3)) for _ in range(6)]
+    acc_h = [tuple(r.standard_normal((1, nh, 128)).astype(np.float32) for _ in range(3)) for _ in range(14)]
+    drafts_h = [tuple(r.standard_normal((1, nh, 128)).astype(np.float32) + 3 for _ in range(3)) for _ in range(6)]
+    acc = [tuple(dev(x) for x in a) for a in acc_h]
+    drafts = [tuple(dev(x) for x in d) for d in drafts_h]
     ot, oc = (torch.zeros((1, nh, 128), device="cuda") for _ in range(2))
+    # the oracle's ring model takes the same writes, checkpoint and rollback
+    model = oracle.RingModel(K.RING_WINDOW)
+    model.record_prefill(pf)
+    rows = {}
+
+    def oracle_out(q):
+        win = model.window()
+        kk = np.concatenate([ref[0], np.stack([rows[u][0] for u in win])])
+        vv = np.concatenate([ref[1], np.stack([rows[u][1] for u in win])])
+        if kind == K.KIND_F32:
+            units = [[("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g])) for g in range(nh)]]
+        else:
+            units = [[]]
+            for g in range(nh):
+                h = oracle.I8Head(cap=kk.shape[0])
+                h.append(kk[:, g], vv[:, g])
+                units[0].append(("i8", h))
+        return oracle.decode(q, units, nh, threads=THREADS)
+
     for t in range(9):
         q, k, v = acc[t]
         K.rswa_decode(test, rt, nh, q, k, v, ot)
         K.rswa_decode(ctrl, rc, nh, q, k, v, oc)
+        rows[("a", t)] = (acc_h[t][1][0], acc_h[t][2][0])
+        model.write(("a", t))
     cp = K.rswa_checkpoint(test, rt, 0)
+    mcp = model.checkpoint()
     assert (cp.ring_len, cp.ring_pos, cp.prefill_len) == (9, 9, pf)
-    for q, k, v in drafts:
+    for i, (q, k, v) in enumerate(drafts):
         K.rswa_decode(test, rt, nh, q, k, v, ot)
+        rows[("d", i)] = (drafts_h[i][1][0], drafts_h[i][2][0])
+        model.write(("d", i))
+    torch.cuda.synchronize()
+    err = max_err(host(ot), oracle_out(drafts_h[-1][0]))          # the last draft step itself
+    assert err <= F32_TOL, err
     assert rt[0].ring_len == 15
     K.rswa_rollback_to(test, rt, 0, cp)
+    model.rollback_to(mcp)
     assert (rt[0].ring_len, rt[0].ring_pos, rt[0].writes, test.len[0]) == (9, 9, 9, pf + 9)
+    assert (model.ring_len, model.ring_pos, model.writes) == (9, 9, 9)
     torch.cuda.synchronize()
     stale = host(drafts[0][1])[0]
     if kind == K.KIND_F32:
@@ -193,8 +252,13 @@ def test_rswa_rollback_restores_the_accepted_path(kind):
         q, k, v = acc[t]
         K.rswa_decode(test, rt, nh, q, k, v, ot)
         K.rswa_decode(ctrl, rc, nh, q, k, v, oc)
+        rows[("a", t)] = (acc_h[t][1][0], acc_h[t][2][0])
+        model.write(("a", t))
         torch.cuda.synchronize()
         assert np.array_equal(host(ot).view(np.uint32), host(oc).view(np.uint32)), t
+        err = max_err(host(ot), oracle_out(acc_h[t][0]))
+        say("  rollback kind %d step %d max err %.3g" % (kind, t, err))
+        assert err <= F32_TOL, (t, err)
     n = pf + 14
     for nm in BUFS[kind]:
         a, b = host(test.view(nm))[:, :, :n], host(ctrl.view(nm))[:, :, :n]

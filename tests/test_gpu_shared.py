@@ -31,9 +31,12 @@ def i8_head(k, v):
 
 
 def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0,
-               kind=K.KIND_F32, spread=False):
+               kind=K.KIND_F32, spread=False, poison=False):
     """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`;
     kind KIND_I8: the int8 mirror (oracle: its codec and int8 decode).
+    poison: every byte of the cache buffers is 0xFF before anything is
+    appended (f32 values and int8 row scales NaN), so a ring slot that is
+    read before it was written shows up as NaN in the outputs.
     spread: the step rows are 0 on channel 0 and every query is +-32 there
     (sign alternating over the queries of a KV head) and 0 elsewhere, so a
     reference row with 64 on channel 0 scores +-181 and every other row 0
@@ -43,6 +46,9 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
     pre = ref_k.shape[0]
     alive = np.ones(hkv, np.uint8) if alive is None else alive
     c = K.KvCache(kind, batch, hkv, pre + W * n_streams + 8, alive=alive)
+    if poison:
+        for buf in c.buffers.values():
+            buf.fill_(255)
     other = (r.standard_normal((5, hkv, 128))).astype(np.float32)
     for b in range(batch):
         if b != seq:
@@ -179,3 +185,98 @@ def test_shared_extreme_score_spread(kind):
     ref_k[45, 1, 0] = 64.0
     shared_run(ref_k, ref_v, n_streams=4, hkv=hkv, hpk=4, steps=140, check={0, 70, 139}, seed=931, kind=kind,
                spread=True)
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+def test_shared_warmup_with_unwritten_slots_holding_nan(kind):
+    """The rings' reserved rows hold NaN until written (buffers filled with
+    0xFF before the reference is appended): through the warm-up every output
+    stays finite and equal to the oracle's -- a slot no stream may read, or
+    the one a step is overwriting, never reaches the value product."""
+    say("case: shared warm-up over NaN slots kind", kind)
+    r = np.random.default_rng(940)
+    hkv = 2
+    ref_k, ref_v = r.standard_normal((2, 200, hkv, 128)).astype(np.float32)
+    shared_run(ref_k, ref_v, n_streams=4, hkv=hkv, hpk=2, steps=24, check=set(range(24)), seed=941, kind=kind,
+               poison=True)
+
+
+def stream_units(models, toks, ref_k, ref_v, hkv, kind):
+    """Oracle units per stream: the reference rows then the stream's live
+    window (the ring model's tokens), per KV head."""
+    units = []
+    for s, m in enumerate(models):
+        win = m.window()
+        kk = np.concatenate([ref_k] + [toks[u][0][s][None] for u in win])
+        vv = np.concatenate([ref_v] + [toks[u][1][s][None] for u in win])
+        if kind == K.KIND_I8:
+            units.append([("i8", i8_head(kk[:, g], vv[:, g])) for g in range(hkv)])
+        else:
+            units.append([("f32", np.ascontiguousarray(kk[:, g]), np.ascontiguousarray(vv[:, g]))
+                          for g in range(hkv)])
+    return units
+
+
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
+@pytest.mark.parametrize("n_accept,n_draft", [(9, 6), (120, 8)])
+def test_shared_checkpoint_rollback_per_stream(kind, n_accept, n_draft):
+    """[P3] BatchedRingCache::checkpoint / rollback_to: streams 1 and 3 of
+    four sharing a reference roll back over n_draft speculative steps (120 +
+    8: the drafts fill the ring exactly, the most a lossless rollback can
+    take back), streams 0 and 2 keep theirs; every later step of every
+    stream equals the oracle's decode over the reference and that stream's
+    window on its own ring model, taken through the same rollback."""
+    say("case: shared rollback kind", kind, "accept", n_accept, "draft", n_draft)
+    r = np.random.default_rng(950 + n_accept)
+    W, hkv, hpk, S, pre = K.RING_WINDOW, 2, 2, 4, 150
+    hq = hkv * hpk
+    c = K.KvCache(kind, 1, hkv, pre + W * S)
+    ref_k, ref_v = r.standard_normal((2, pre, hkv, 128)).astype(np.float32)
+    append_rows(c, 0, ref_k, ref_v)
+    rings = K.Rings(S)
+    K.rswa_shared_record_prefill(c, 0, rings, S)
+    models = []
+    for _ in range(S):
+        m = oracle.RingModel(W)
+        m.record_prefill(pre)
+        models.append(m)
+    toks = {}
+    out = torch.full((S, hq, 128), np.nan, device="cuda")
+    back = (1, 3)
+
+    def step(t, check):
+        q = r.standard_normal((S, hq, 128)).astype(np.float32)
+        kt = r.standard_normal((S, hkv, 128)).astype(np.float32)
+        vt = r.standard_normal((S, hkv, 128)).astype(np.float32)
+        toks[t] = (kt, vt)
+        K.rswa_shared_decode(c, 0, rings, S, hq, dev(q), dev(kt), dev(vt), out)
+        for s in range(S):
+            models[s].write(t)
+            assert (rings[s].ring_len, rings[s].ring_pos) == (models[s].ring_len, models[s].ring_pos)
+        if check:
+            torch.cuda.synchronize()
+            err = max_err(host(out), oracle.decode(q, stream_units(models, toks, ref_k, ref_v, hkv, kind), hkv,
+                                                   threads=THREADS))
+            assert err <= F32_TOL, (t, err)
+            return err
+        return 0.0
+
+    for t in range(n_accept):
+        step(t, check=t == n_accept - 1)
+    cps = {s: K.rswa_shared_checkpoint(c, 0, rings, S, s) for s in back}
+    mcps = {s: models[s].checkpoint() for s in back}
+    for i in range(n_draft):
+        step(1000 + i, check=i == n_draft - 1)
+    for s in back:
+        K.rswa_shared_rollback_to(c, 0, rings, S, s, cps[s])
+        models[s].rollback_to(mcps[s])
+        assert (rings[s].ring_len, rings[s].ring_pos, rings[s].writes) == (
+            models[s].ring_len, models[s].ring_pos, models[s].writes)
+    assert c.len[0] == pre + W * S
+    worst = 0.0
+    for t in range(n_accept, n_accept + 10):
+        worst = max(worst, step(t, check=True))
+    say("  max err %.3g" % worst)
+    # the abandoned branch's checkpoint no longer matches
+    with pytest.raises(K.KvqError):
+        K.rswa_shared_rollback_to(c, 0, rings, S, 1, cps[1])

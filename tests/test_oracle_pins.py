@@ -564,8 +564,8 @@ def test_softcap_closed_forms():
 
 
 def test_sinks_match_value_less_column():
-    """[P2] attend_group_upto: a sink logit joins the max and the denominator
-    and has no value row -- a softmax over the rows plus one extra column of
+    """[P2] attend_group_upto: a sink logit takes part in the maximum and the
+    normaliser and carries no value -- a softmax over the rows plus one extra column of
     value zero."""
     r = rng(3300)
     q = r.standard_normal((4, HD)).astype(np.float32)
@@ -816,6 +816,84 @@ def test_trim_window_anchored_page_example():
         base, n = base + d, n - d
     assert n <= 2 * w
     assert oracle.truncate_last(5, 7) == 0 and oracle.truncate_last(5, 2) == 3
+
+
+def test_head_truncate_page_examples():
+    """[P2] truncate_last on the per-head stores: the page's q8 test appends
+    100 positions (crossing the freeze) and truncates 30, leaving 70 rows;
+    its f32 test keeps positions 0..2 of 5 after dropping 2.  The kept rows
+    keep their codes and scales, and the frozen field stays."""
+    r = rng(4100)
+    k = (r.standard_normal((100, HD)) * 3).astype(np.float32)
+    v = (r.standard_normal((100, HD)) * 3).astype(np.float32)
+    h = oracle.Q8Head(cap=100)
+    h.append(k, v)
+    kq, ks, vq, vs = h.kq.copy(), h.ks.copy(), h.vq.copy(), h.vs.copy()
+    kcol, vcol = h.kcol.copy(), h.vcol.copy()
+    h.truncate_last(30)
+    assert h.n == 70 and h.frozen
+    assert np.array_equal(h.kq[:70], kq[:70]) and np.array_equal(h.vq[:70], vq[:70])
+    assert np.array_equal(h.ks[:70], ks[:70]) and np.array_equal(h.vs[:70], vs[:70])
+    assert np.array_equal(h.kcol, kcol) and np.array_equal(h.vcol, vcol)
+    np.testing.assert_array_equal(h.dequant_k(), oracle.Q8Head.dequant_k(h)[:70])
+    h.truncate_last(500)
+    assert h.n == 0 and h.frozen
+    i = oracle.I8Head(cap=5)
+    rows = np.repeat(np.arange(5, dtype=np.float32)[:, None], HD, 1)
+    i.append(rows, rows)
+    i.truncate_last(2)
+    assert i.n == 3
+    # position 2 survives: a constant row of 2 codes as 127 x (2 / 127)
+    assert (i.kq[2] == 127).all() and i.ks[2] == np.float32(2.0) / np.float32(127.0)
+    np.testing.assert_allclose(i.dequant_k()[2], 2.0, rtol=1e-6)
+
+
+@pytest.mark.parametrize("n0,nd", [(50, 10), (150, 20)])
+def test_head_truncate_then_append_equals_never_appended(n0, nd):
+    """A speculative append, truncated, then the accepted rows: the stores
+    equal a head that only ever saw the accepted rows -- for q8 both when
+    the rejected rows stay below the freeze (the freeze then happens at the
+    same row) and after it (the rejected rows were quantised against the
+    frozen field, which stays)."""
+    r = rng(4200 + n0)
+    base = [(r.standard_normal((n0, HD)) * 2).astype(np.float32) for _ in range(2)]
+    draft = [(r.standard_normal((nd, HD)) * 5).astype(np.float32) for _ in range(2)]
+    final = [(r.standard_normal((30, HD)) * 2).astype(np.float32) for _ in range(2)]
+    for cls in (oracle.Q8Head, oracle.I8Head):
+        t, c = cls(cap=300), cls(cap=300)
+        t.append(*base)
+        t.append(*draft)
+        t.truncate_last(nd)
+        c.append(*base)
+        for h in (t, c):
+            h.append(*final)
+        assert t.n == c.n == n0 + 30
+        for nm in ("kq", "ks", "vq", "vs"):
+            assert np.array_equal(getattr(t, nm)[: t.n], getattr(c, nm)[: c.n]), (cls.__name__, nm)
+        if cls is oracle.Q8Head:
+            assert t.frozen and c.frozen
+            assert np.array_equal(t.kcol, c.kcol) and np.array_equal(t.vcol, c.vcol)
+
+
+def test_q8_truncate_below_warmup_keeps_the_frozen_field():
+    """[P2] truncate_last drops rows only: a head frozen at 64 and truncated
+    to 10 rows quantises its next row against the frozen field (reading
+    c32), not against a field of 1."""
+    r = rng(4300)
+    k = (r.standard_normal((80, HD)) * np.exp(r.uniform(-1, 2, HD))).astype(np.float32)
+    v = (r.standard_normal((80, HD)) * np.exp(r.uniform(-1, 2, HD))).astype(np.float32)
+    h = oracle.Q8Head(cap=100)
+    h.append(k, v)
+    h.truncate_last(70)
+    assert h.n == 10 and h.frozen
+    x = (r.standard_normal((1, HD)) * 4).astype(np.float32)
+    h.append(x, x)
+    kq, ks = oracle.quant_row(x[0], h.kcol)
+    vq, vs = oracle.quant_row(x[0], h.vcol, group=HD)
+    assert np.array_equal(h.kq[10], kq) and np.array_equal(h.ks[10], ks)
+    assert np.array_equal(h.vq[10], vq) and h.vs[10] == vs[0]
+    k1, _ = oracle.quant_row(x[0])
+    assert not np.array_equal(kq, k1)
 
 
 @pytest.mark.parametrize("prefill,n_hist,K", [(7, 5, 4), (7, 126, 5), (3, 300, 6), (0, 0, 3)])
