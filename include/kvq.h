@@ -275,6 +275,24 @@ int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * decode_attn_q8_noalloc -- decode_attn_q8 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same computation and kernels, with the
+ * partial softmax states in a static device array of the library (64 MiB,
+ * one per GPU, held until the process ends) instead of a caller's
+ * workspace.  The call allocates nothing and frees nothing; the caller
+ * still passes q and out (layouts as decode_attn_q8).  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race; calls ordered on one
+ * stream do not.  Nothing in the array needs clearing between calls.
+ * Errors: as decode_attn_q8, plus KVQ_EINVAL when the cache would need more
+ * than 64 MiB of workspace (kvq_workspace_bytes() > 64 MiB: e.g. group
+ * size 8 with min(batch, 128) x live heads > 7939), and KVQ_EDEVICE when
+ * the array's device address cannot be looked up.
+ */
+int decode_attn_q8_noalloc(const kvq_cache* c, int n_q_heads, const float* q, float* out, void* stream);
+
+/*
  * kv_append_i8 -- kv_append_f32 for an i8 cache: each row of each live head
  * is quantised as [P3] quantize_row_i8, separately for K and V:
  *   scale = max|x| / 127 (correctly rounded f32 division), or 1 for an

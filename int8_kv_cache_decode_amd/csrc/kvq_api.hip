@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,6 +21,32 @@ using namespace kvq;
 namespace {
 
 thread_local std::string g_err;
+
+// Workspace of decode_attn_q8_noalloc: the partial softmax states of the
+// split decode live in this device array instead of a caller's buffer.  Each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): it uses the address scratch_address()
+// looked up for the current device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null on a runtime error.
+void* scratch_address() {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static void* addr[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -550,6 +577,29 @@ int decode_attn_q8(const kvq_cache* c, int n_q_heads, const float* q, float* out
     if (rc) return rc;
     int hpk = 0;
     if ((rc = check_decode_args(c, n_q_heads, q, out, ws, ws_bytes, fn, &hpk))) return rc;
+    return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, nullptr,
+                      (hipStream_t)stream, fn);
+}
+
+int decode_attn_q8_noalloc(const kvq_cache* c, int n_q_heads, const float* q, float* out, void* stream) {
+    const char* fn = "decode_attn_q8_noalloc";
+    int rc = check_cache(c, KVQ_KIND_Q8, fn);
+    if (rc) return rc;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "%s: n_q_heads %d is not a multiple of n_kv_heads %d", fn, n_q_heads, c->n_kv_heads);
+    const int hpk = n_q_heads / c->n_kv_heads;
+    if (hpk != 1 && hpk != 2 && hpk != 4 && hpk != 8)
+        return fail(KVQ_EINVAL, "%s: group size %d not in {1,2,4,8}", fn, hpk);
+    if (!q || !out) return fail(KVQ_EINVAL, "%s: null q/out", fn);
+    if (!aligned16(q) || !aligned16(out)) return fail(KVQ_EINVAL, "%s: q/out not 16-byte aligned", fn);
+    const size_t need = ws_need(c, hpk);
+    if (need > kScratchBytes)
+        return fail(KVQ_EINVAL, "%s: this cache needs %zu bytes of workspace, more than the %zu of the static one "
+                    "(use decode_attn_q8 with a workspace)", fn, need, kScratchBytes);
+    // the device array replaces the caller's workspace; nothing in it needs
+    // clearing (the decode kernel writes every partial the combine reads)
+    void* ws = scratch_address();
+    if (!ws) return fail(KVQ_EDEVICE, "%s: no device address for the static workspace", fn);
     return run_decode(c, n_q_heads, hpk, q, out, ws, c->len, nullptr, nullptr, nullptr, nullptr,
                       (hipStream_t)stream, fn);
 }

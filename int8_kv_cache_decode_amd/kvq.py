@@ -88,6 +88,7 @@ _SIGNATURES = [
     ("rswa_shared_record_prefill", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int]),
     ("rswa_shared_decode", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    ("decode_attn_q8_noalloc", ctypes.c_int, [_P, ctypes.c_int, _P, _P, _P]),
     ("rswa_shared_checkpoint", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P]),
     ("rswa_shared_rollback_to", ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, _P]),
     ("kvq_last_error", ctypes.c_char_p, []),
@@ -389,3 +390,6 @@ def rswa_shared_rollback_to(cache: KvCache, seq: int, rings: Rings, n_streams: i
                             cp: kvq_ring_checkpoint) -> None:
     _check(lib().rswa_shared_rollback_to(cache.ref, seq, rings.ref, n_streams, s, ctypes.byref(cp)))
 
+
+def decode_attn_q8_noalloc(cache: KvCache, n_q_heads: int, q, out, stream=None) -> None:
+    _check(lib().decode_attn_q8_noalloc(cache.ref, n_q_heads, _ptr(q), _ptr(out), _stream(stream)))

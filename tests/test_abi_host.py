@@ -543,6 +543,27 @@ def test_shared_rollback_refusals_leave_everything_unchanged():
     expect(call("rswa_shared_rollback_to", q.ref, 0, rings.ref, 4, 1, ctypes.byref(cp)), K.ESTATE, q, bq, rings)
 
 
+def test_noalloc_decode_refusals_before_any_device_work():
+    """decode_attn_q8_noalloc validates like decode_attn_q8, and refuses a
+    cache whose workspace would not fit its 64 MiB static array; all of it
+    before the device is touched."""
+    c = fake_cache(K.KIND_Q8)
+    c.len[:] = [10, 20]
+    before = snapshot(c)
+    for args, code in (((30, FAKE, FAKE), K.EINVAL), ((8 * 16, FAKE, FAKE), K.EINVAL),
+                       ((32, None, FAKE), K.EINVAL), ((32, FAKE, None), K.EINVAL), ((32, FAKE + 8, FAKE), K.EINVAL)):
+        expect(call("decode_attn_q8_noalloc", c.ref, *args, None), code, c, before)
+    f = fake_cache(K.KIND_F32)
+    bf = snapshot(f)
+    expect(call("decode_attn_q8_noalloc", f.ref, 32, FAKE, FAKE, None), K.ESTATE, f, bf)
+    # group 8, 128 sequences x 64 live heads: 2 x 8192 slots x 8 heads x 520 B > 64 MiB
+    big = fake_cache(K.KIND_Q8, batch=128, hkv=64, cap=16)
+    assert K.kvq_workspace_bytes(big, 512) > 64 << 20
+    bb = snapshot(big)
+    expect(call("decode_attn_q8_noalloc", big.ref, 512, FAKE, FAKE, None), K.EINVAL, big, bb)
+    assert "64" in K.last_error() or "static" in K.last_error()
+
+
 def test_int8_verify_workspace_holds_the_draft_mirror():
     """On the per-row int8 kind the verify workspace also holds the drafts'
     int8 mirror (batch x drafts x KV heads rows of 2 x (128 codes + a
