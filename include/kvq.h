@@ -371,8 +371,8 @@ int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
  * tokens.  Nothing is written: the cache and the ring cursors are unchanged
  * (accepting drafts is then rswa_decode, or a checkpoint / rollback).
  * On an i8 cache (the page's int8 mirror, its decode_attention being
- * decode_attention_int8) the drafts are quantised with quantize_row_i8 into
- * the workspace first, and every query per head.
+ * decode_attention_int8) every draft row is quantised with quantize_row_i8
+ * where the kernel reads it (nothing is stored), and every query per head.
  *
  * q        device float [batch][n_draft][n_q_heads][128]
  * k_draft, v_draft  device float [batch][n_draft][n_kv_heads][128]
@@ -388,9 +388,8 @@ int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_
 
 /* Workspace bytes rswa_verify needs with n_draft drafts, and rswa_shared_decode
  * with n_draft streams: partial states for n_draft x (n_q_heads / n_kv_heads)
- * queries per slot (at most 16), slots as kvq_workspace_bytes, and on an i8
- * cache the drafts' int8 mirror (batch x n_draft x n_kv_heads rows of codes
- * and scales); 0 on invalid arguments or more than 16 queries. */
+ * queries per slot (at most 16), slots as kvq_workspace_bytes; 0 on invalid
+ * arguments or more than 16 queries. */
 size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft);
 
 /*
@@ -501,8 +500,9 @@ int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_str
  * ([P3] batched_decode_attention: per stream over its own reference ++ ring).
  * The reference rows are read once for every stream's queries: n_streams x
  * (n_q_heads / n_kv_heads) <= 16 queries per KV head share each row read, a
- * dense contraction on the matrix cores.  On an i8 cache the step rows are
- * quantised into the ring slots first and the decode is the int8 route.
+ * dense contraction on the matrix cores.  On an i8 cache each step row is
+ * quantised with quantize_row_i8 into its ring slot and the decode is the
+ * int8 route.
  *
  * q, out        device float [n_streams][n_q_heads][128]
  * k_new, v_new  device float [n_streams][n_kv_heads][128]

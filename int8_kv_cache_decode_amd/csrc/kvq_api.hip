@@ -807,19 +807,11 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
     return KVQ_OK;
 }
 
-// The per-row int8 verify quantises its drafts into a mirror after the
-// partial states: codes [batch][n_draft][n_kv_heads][128] for K and V, then
-// their scales.
-static size_t draft_mirror_bytes(const kvq_cache* c, int n_draft) {
-    const size_t rows = (size_t)c->batch * n_draft * c->n_kv_heads;
-    return (rows * 2 * (kHD + sizeof(float)) + 255) & ~(size_t)255;
-}
-
 size_t kvq_verify_workspace_bytes(const kvq_cache* c, int n_q_heads, int n_draft) {
     if (!c || c->n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % c->n_kv_heads || n_draft < 1) return 0;
     const int nq = n_draft * (n_q_heads / c->n_kv_heads);
     if (nq > kVerifyMaxQ) return 0;
-    return ws_need(c, nq) + (c->kind == KVQ_KIND_I8 ? draft_mirror_bytes(c, n_draft) : 0);
+    return ws_need(c, nq);
 }
 
 int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_draft, const float* q,
@@ -836,7 +828,7 @@ int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_
     if (!aligned16(q) || !aligned16(k_draft) || !aligned16(v_draft) || !aligned16(out) || !aligned16(ws))
         return fail(KVQ_EINVAL, "%s: q/k_draft/v_draft/out/workspace not 16-byte aligned", fn);
     const bool i8 = c->kind == KVQ_KIND_I8;
-    const size_t need = ws_need(c, n_draft * hpk) + (i8 ? draft_mirror_bytes(c, n_draft) : 0);
+    const size_t need = ws_need(c, n_draft * hpk);
     if (ws_bytes < need) return fail(KVQ_EINVAL, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     for (int b = 0; b < c->batch; ++b) {
         const kvq_ring& r = rings[b];
@@ -868,24 +860,12 @@ int rswa_verify(const kvq_cache* c, const kvq_ring* rings, int n_q_heads, int n_
     memcpy(a.live_slot, c->live_slot, sizeof a.live_slot);
     if (i8) {
         // [P3] write_decode_step of the drafts on a clone of the int8 mirror:
-        // their codes, in a mirror after the partial states
-        const size_t rows = (size_t)c->batch * n_draft * c->n_kv_heads;
-        uint8_t* base = (uint8_t*)ws + ws_need(c, n_draft * hpk);
-        int8_t* kdq = (int8_t*)base;
-        int8_t* vdq = kdq + rows * kHD;
-        float* kds = (float*)(vdq + rows * kHD);
-        float* vds = kds + rows;
+        // the kernel quantises each draft row where it reads it (nothing is
+        // written to the cache)
         a.kq = c->kq;
         a.ks = c->ks;
         a.vq = c->vq;
         a.vs = c->vs;
-        a.kdq = kdq;
-        a.kds = kds;
-        a.vdq = vdq;
-        a.vds = vds;
-        if ((rc = device_status(launch_quant_rows_i8(k_draft, v_draft, (int)rows, kdq, kds, vdq, vds,
-                                                     (hipStream_t)stream), fn)))
-            return rc;
     }
     for (int s0 = 0; s0 < c->batch; s0 += kSeqPerLaunch) {
         const int ns = std::min(kSeqPerLaunch, c->batch - s0);
@@ -981,12 +961,8 @@ int rswa_shared_decode(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, in
     }
     const bool i8 = c->kind == KVQ_KIND_I8;
     if (i8) {
-        // the int8 mirror: the step rows are quantised into the ring slots
-        // first (stream-ordered), then every stream sees its live slots
-        std::vector<Seg> segs;
-        for (int s = 0; s < n_streams; ++s) segs.push_back({seq, s, a.swrow[s], 1, false});
-        if ((rc = launch_segments(c, k_new, v_new, segs, (hipStream_t)stream, fn))) return rc;
-        for (int s = 0; s < n_streams; ++s) a.sring[s] = next[s].ring_len;
+        // the int8 mirror: the kernel quantises each step row where it reads
+        // it and stores its codes in the stream's ring slot
         a.kq = c->kq;
         a.ks = c->ks;
         a.vq = c->vq;
@@ -1015,7 +991,7 @@ int rswa_shared_decode(kvq_cache* c, int seq, kvq_ring* rings, int n_streams, in
     a.seq0 = seq;
     a.n_seq = 1;
     a.prefill[0] = pre;
-    a.len[0] = c->len[seq] + (i8 ? 0 : n_streams);         // reference, rings (f32: then the step rows)
+    a.len[0] = c->len[seq] + n_streams;                     // reference, rings, then the step rows
     a.ntile[0] = (a.len[0] + kTileRows - 1) / kTileRows;
     a.tile_base[0] = 0;
     a.tile_base[1] = a.ntile[0] * c->n_live;

@@ -108,23 +108,6 @@ __global__ __launch_bounds__(128) void k_append_i8(const AppendArgs a) {
     if (lane == 0) (is_k ? a.ks : a.vs)[hrow] = s;
 }
 
-// Per-row int8 codes of plain f32 rows (the verify's draft mirror): block
-// (row, K or V), one wave, lane holds 2 channels; the codec of k_append_i8.
-__global__ __launch_bounds__(64) void k_quant_rows_i8(const float* k, const float* v, int8_t* kq, float* ks,
-                                                      int8_t* vq, float* vs) {
-    const size_t row = blockIdx.x;
-    const bool is_k = blockIdx.y == 0;
-    const int lane = threadIdx.x;
-    const float2 x = *(const float2*)((is_k ? k : v) + row * kHD + 2 * lane);
-    const float am = group_max<64>(fmaxf(fabsf(x.x), fabsf(x.y)));
-    const float s = am > 0.0f ? __fdiv_rn(am, 127.0f) : 1.0f;
-    char2 c;
-    c.x = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(x.x, s)), -127.0f), 127.0f);
-    c.y = (int8_t)(int)fminf(fmaxf(rintf(__fdiv_rn(x.y, s)), -127.0f), 127.0f);
-    *(char2*)((is_k ? kq : vq) + row * kHD + 2 * lane) = c;
-    if (lane == 0) (is_k ? ks : vs)[row] = s;
-}
-
 // Freeze + requantise ([P1] freeze_cols) for one (sequence, live head).
 // block 128: thread d owns channel d.  The RMS sum runs over the rows in
 // order, multiply then add, exactly as the page's loop does per channel.
@@ -257,13 +240,6 @@ hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s) {
 
 hipError_t launch_append_i8(const AppendArgs& a, int n_rows, hipStream_t s) {
     hipLaunchKernelGGL(k_append_i8, dim3(n_rows, a.n_seq, a.n_live), dim3(128), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_quant_rows_i8(const float* k, const float* v, int rows, int8_t* kq, float* ks, int8_t* vq,
-                                float* vs, hipStream_t s) {
-    if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_quant_rows_i8, dim3(rows, 2), dim3(64), 0, s, k, v, kq, ks, vq, vs);
     return hipGetLastError();
 }
 

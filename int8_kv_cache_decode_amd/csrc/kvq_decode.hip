@@ -1210,34 +1210,188 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
 //           codes (lane l: query l % 16, the same channels), one MFMA per
 //           64-channel span; lane l receives rows 4 (l / 16) + r of query
 //           l % 16, scaled in f64;
-//   values  (P V)^T on v_mfma_f32_16x16x4f32 as in k_verify_f32, with the V
-//           codes converted exactly to f32 (lane l: channels 8 (l % 16) ..
-//           + 7 of rows 4 (l / 16) + s, one 8-byte load per row) and each
-//           row's V scale folded into its weight; block cb of the output
-//           holds channels 8 m + cb.
-// Verify: the draft rows come from a quantised mirror of the drafts (the
-// page writes them to a clone of the mirror before each decode).  Shared
-// decode: the step rows are already in the rings, so stream s sees the
-// reference and its live ring slots.
+//   values  (P V)^T = V^T P^T on v_mfma_f32_16x16x32_bf16, one pair per
+//           8-channel block cb (channels 8 m + cb, m = l % 16): lane l's eight
+//           K slots are its four rows 4 (l / 16) + r, twice.  A = those rows'
+//           V codes (exact in bf16, each twice); B = the lane's own query's
+//           weights times the rows' V scales, split exactly into three bf16
+//           parts (hi, mid in the first MFMA's slots, lo and zeros in the
+//           second's), so the f32 accumulators receive the f32 weights' full
+//           products.  Lane l accumulates query l % 16's channels
+//           8 (4 (l / 16) + r) + cb.
+// The running max is lazy (moved only when a tile's max exceeds it by more
+// than kLazy), so the 32 accumulators are rarely rescaled.
+// Rows past the cache's ("trailing rows": the verify's drafts, the shared
+// decode's step rows, one per stream) are quantised with quantize_row_i8 by
+// each wave whose share holds them, into its LDS, at the start of the piece;
+// in the shared decode the wave also stores stream s's quantised step row in
+// the stream's ring slot ([P3] write_decode_step), where no other wave reads
+// it during this call (the slot is masked for stream s, invisible to the
+// others).
+// Verify: query i sees the reference, the ring slots that survive drafts
+// 0..i, and drafts 0..i.  Shared decode: stream s sees the reference, its
+// ring slots live before the step except the one the step overwrites, and its
+// own step row.
 // ---------------------------------------------------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// w = hi + mid + lo exactly (w normal): each part is the top 16 bits (sign,
+// exponent, 7 mantissa bits: a bf16) of the remainder, and the remainders
+// are exact f32 subtractions; the last one has at most 8 significant bits.
+__device__ __forceinline__ void bf16_split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t h = __float_as_uint(w) & 0xffff0000u;
+    const float r1 = w - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(m);
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = __float_as_uint(r2) >> 16;
+}
+// Two bf16 values (the top halves of two f32 that are exact in bf16) in one dword.
+__device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
 template <bool kShared>
 __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
+    // trailing rows of the piece: K / V codes and scales
+    __shared__ __attribute__((aligned(16))) int8_t sm_tq[kWaves][2][kVerifyMaxQ][kHD];
+    __shared__ float sm_ts[kWaves][2][kVerifyMaxQ];
     const int w = share_index();
     if (w >= a.n_shares) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int qi = lane & 15, kb = lane >> 4;
     for_each_piece(a, w, [&](const Piece& it) {
         const int j = it.j;
         const int pre = a.prefill[j];
-        const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft : pre + a.ring_len[j];
+        const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft : pre + a.ring_len[j];   // cache rows
         const size_t ob = kShared ? 0 : (size_t)it.b;
         const int8_t* KQ = a.kq + it.hidx * kq_rows(a.capacity) * kHD;   // tile-major K codes
         const float* KS = a.ks + it.hrow;
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
-        const size_t d0 = ob * a.n_draft * a.n_kv_heads + it.g;       // mirror row of draft 0
-        const size_t dstep = (size_t)a.n_kv_heads;
-        auto mrow = [&](int p) { return d0 + (size_t)(p - L) * dstep; };
+
+        // ---- trailing rows [t0, t1) of this piece, quantised into LDS ----
+        // Lane l takes row t0 + l / 4 and the 32 channels 32 (l % 4) .. of its
+        // K and V (all loads issued at once); a row's scale is the max over its
+        // four lanes.  The loads go out before the first tile's, the
+        // arithmetic after them.
+        const int t0 = max(it.row0, L) - L, t1 = it.row1 - L;
+        const int tr = t0 + (lane >> 2), tc = 32 * (lane & 3);
+        const bool tlane = tr < t1;
+        float4 xk[8], xv[8];
+        if (t1 > 0) {
+            const size_t dstride = (size_t)a.n_kv_heads * kHD;
+            const size_t off = (ob * a.n_draft * a.n_kv_heads + it.g) * kHD + (size_t)(tlane ? tr : t0) * dstride + tc;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                xk[u] = *(const float4*)(a.kd + off + 4 * u);
+                xv[u] = *(const float4*)(a.vd + off + 4 * u);
+            }
+        }
+        auto quantise_trailing = [&]() {
+            float ak = 0.0f, av = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                ak = fmaxf(ak, fmaxf(fmaxf(fabsf(xk[u].x), fabsf(xk[u].y)), fmaxf(fabsf(xk[u].z), fabsf(xk[u].w))));
+                av = fmaxf(av, fmaxf(fmaxf(fabsf(xv[u].x), fabsf(xv[u].y)), fmaxf(fabsf(xv[u].z), fabsf(xv[u].w))));
+            }
+            ak = fmaxf(ak, __shfl_xor(ak, 1, 64));
+            ak = fmaxf(ak, __shfl_xor(ak, 2, 64));
+            av = fmaxf(av, __shfl_xor(av, 1, 64));
+            av = fmaxf(av, __shfl_xor(av, 2, 64));
+            const float sk = ak > 0.0f ? __fdiv_rn(ak, 127.0f) : 1.0f;
+            const float sv = av > 0.0f ? __fdiv_rn(av, 127.0f) : 1.0f;
+            auto code = [](float x, float sc) { return (int)fminf(fmaxf(rintf(__fdiv_rn(x, sc)), -127.0f), 127.0f) & 0xff; };
+            uint32_t ck[8], cv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                ck[u] = code(xk[u].x, sk) | (code(xk[u].y, sk) << 8) | (code(xk[u].z, sk) << 16) | (code(xk[u].w, sk) << 24);
+                cv[u] = code(xv[u].x, sv) | (code(xv[u].y, sv) << 8) | (code(xv[u].z, sv) << 16) | (code(xv[u].w, sv) << 24);
+            }
+            if (tlane) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    *(uint4*)(&sm_tq[wave][0][tr][tc + 16 * h]) = make_uint4(ck[4 * h], ck[4 * h + 1], ck[4 * h + 2], ck[4 * h + 3]);
+                    *(uint4*)(&sm_tq[wave][1][tr][tc + 16 * h]) = make_uint4(cv[4 * h], cv[4 * h + 1], cv[4 * h + 2], cv[4 * h + 3]);
+                }
+                if ((lane & 3) == 0) {
+                    sm_ts[wave][0][tr] = sk;
+                    sm_ts[wave][1][tr] = sv;
+                }
+                if constexpr (kShared) {
+                    // [P3] write_decode_step: stream tr's step row into its ring slot
+                    const int row = a.swrow[tr];
+                    int8_t* kdst = a.kq + it.hidx * kq_rows(a.capacity) * kHD;
+                    int8_t* vdst = a.vq + (it.hrow + row) * kHD + tc;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        *(uint4*)(kdst + kq_offset(row, tc + 16 * h)) = make_uint4(ck[4 * h], ck[4 * h + 1], ck[4 * h + 2], ck[4 * h + 3]);
+                        *(uint4*)(vdst + 16 * h) = make_uint4(cv[4 * h], cv[4 * h + 1], cv[4 * h + 2], cv[4 * h + 3]);
+                    }
+                    if ((lane & 3) == 0) {
+                        a.ks[it.hrow + row] = sk;
+                        a.vs[it.hrow + row] = sv;
+                    }
+                }
+            }
+            wave_lds_sync();
+        };
+        struct Tile {
+            uint4 kc[2];       // K codes of row r0 + qi, spans 0 and 1
+            float ks[4];       // K scales of rows r0 + 4 kb + r
+            uint2 vc[4];       // V codes of rows r0 + 4 kb + s, channels 8 qi ..
+            float vs[4];
+        };
+        auto load_tile = [&](int r0, Tile& t) {
+            if (min(r0 + kTileRows - 1, it.row1 - 1) < L) {
+                // the whole tile in the cache (wave-uniform): no per-row choice
+                // of source, 32-bit offsets from the block's scalar base
+                const uint32_t pk = (uint32_t)min(r0 + qi, it.row1 - 1);
+                t.kc[0] = ld_stream(KQ + kq_offset((int)pk, 16 * kb));
+                t.kc[1] = ld_stream(KQ + kq_offset((int)pk, 64 + 16 * kb));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t p = (uint32_t)min(r0 + 4 * kb + r, it.row1 - 1);
+                    t.ks[r] = KS[p];                   // row scales: plain loads, as in k_decode_q8
+                    ld_v(VQ + (p * kHD + 8 * qi), t.vc[r]);
+                    t.vs[r] = VS[p];
+                }
+                return;
+            }
+            const int pk = min(r0 + qi, it.row1 - 1);
+            if (pk < L) {
+                t.kc[0] = ld_stream(KQ + kq_offset(pk, 16 * kb));
+                t.kc[1] = ld_stream(KQ + kq_offset(pk, 64 + 16 * kb));
+            } else {                                     // a trailing row, from LDS
+                t.kc[0] = *(const uint4*)(&sm_tq[wave][0][pk - L][16 * kb]);
+                t.kc[1] = *(const uint4*)(&sm_tq[wave][0][pk - L][64 + 16 * kb]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int p = min(r0 + 4 * kb + r, it.row1 - 1);
+                if (p < L) {
+                    t.ks[r] = KS[p];
+                    ld_v(VQ + (size_t)p * kHD + 8 * qi, t.vc[r]);
+                    t.vs[r] = VS[p];
+                } else {
+                    t.ks[r] = sm_ts[wave][0][p - L];
+                    t.vc[r] = *(const uint2*)(&sm_tq[wave][1][p - L][8 * qi]);
+                    t.vs[r] = sm_ts[wave][1][p - L];
+                }
+            }
+        };
+        // the first tile's loads go out before the trailing rows' arithmetic
+        // and the query set-up, unless that tile reads trailing rows from LDS
+        // (a piece is never empty)
+        int r0 = it.row0;
+        Tile ta, tb;
+        const bool first_in_cache = min(r0 + kTileRows - 1, it.row1 - 1) < L;
+        if (first_in_cache) load_tile(r0, ta);
+        if (t1 > 0) quantise_trailing();
+        if (!first_in_cache) load_tile(r0, ta);
 
         // this lane's query (B column): draft / stream di, head hh of the group,
         // quantised with quantize_row_i8 in f32 (amax over the 4 lanes of qi)
@@ -1277,65 +1431,20 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         }
         const int rl = a.ring_len[j], old = a.ring_oldest[j];
         const int evict = max(0, rl + di + 1 - KVQ_RING_WINDOW);
-        const int live = kShared ? a.sring[di] : 0;
+        const int live = kShared ? a.sring[di] : 0;                               // ring slots live before the step
+        const int wslot = kShared ? a.swrow[di] - pre - KVQ_RING_WINDOW * di : 0;   // the slot it overwrites
         auto visible = [&](int p) {
             if (p < pre) return true;
             if constexpr (kShared) {
-                return ((p - pre) >> 7) == di && ((p - pre) & (KVQ_RING_WINDOW - 1)) < live;
+                if (p >= L) return p - L == di;
+                const int slot = (p - pre) & (KVQ_RING_WINDOW - 1);
+                return ((p - pre) >> 7) == di && slot < live && slot != wslot;
             } else {
                 if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
                 return p - L <= di;
             }
         };
 
-        struct Tile {
-            uint4 kc[2];       // K codes of row r0 + qi, spans 0 and 1
-            float ks[4];       // K scales of rows r0 + 4 kb + r
-            uint2 vc[4];       // V codes of rows r0 + 4 kb + s, channels 8 qi ..
-            float vs[4];
-        };
-        auto load_tile = [&](int r0, Tile& t) {
-            if (!kShared && min(r0 + kTileRows - 1, it.row1 - 1) < L) {
-                // verify: the whole tile in the cache (wave-uniform), so no
-                // per-row choice of source, and 32-bit offsets from the block's
-                // scalar base (rswa_verify on the int8 mirror 40.6 -> 39.9 us;
-                // the shared decode measured slower with it, 49.2 -> 49.9 us)
-                const uint32_t pk = (uint32_t)min(r0 + qi, it.row1 - 1);
-                t.kc[0] = ld_stream(KQ + kq_offset((int)pk, 16 * kb));
-                t.kc[1] = ld_stream(KQ + kq_offset((int)pk, 64 + 16 * kb));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t p = (uint32_t)min(r0 + 4 * kb + r, it.row1 - 1);
-                    t.ks[r] = KS[p];                   // row scales: plain loads, as in k_decode_q8
-                    ld_v(VQ + (p * kHD + 8 * qi), t.vc[r]);
-                    t.vs[r] = VS[p];
-                }
-                return;
-            }
-            const int pk = min(r0 + qi, it.row1 - 1);
-            if (pk < L) {
-                t.kc[0] = ld_stream(KQ + kq_offset(pk, 16 * kb));
-                t.kc[1] = ld_stream(KQ + kq_offset(pk, 64 + 16 * kb));
-            } else {                                     // the drafts' mirror is row-major
-                const int8_t* kr = a.kdq + mrow(pk) * kHD + 16 * kb;
-                t.kc[0] = *(const uint4*)kr;
-                t.kc[1] = *(const uint4*)(kr + 64);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = min(r0 + 4 * kb + r, it.row1 - 1);
-                if (p < L) {
-                    t.ks[r] = KS[p];
-                    ld_v(VQ + (size_t)p * kHD + 8 * qi, t.vc[r]);
-                    t.vs[r] = VS[p];
-                } else {
-                    const size_t m = mrow(p);
-                    t.ks[r] = a.kds[m];
-                    t.vc[r] = *(const uint2*)(a.vdq + m * kHD + 8 * qi);
-                    t.vs[r] = a.vds[m];
-                }
-            }
-        };
         float m = -INFINITY, l = 0.0f;
         v4f acc[8];
 #pragma unroll
@@ -1358,30 +1467,45 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
                 if (vis[r]) tmax = fmaxf(tmax, (float)s64[r]);
             }
             tmax = max_rows(tmax);
-            const float mnew = fmaxf(m, tmax);
-            const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(m - mnew);
-            float pw[4];
+            // lazy max: weights stay <= 2^kLazy
+            float alpha = 1.0f;
+            if (tmax > m + kLazy) {
+                alpha = fast_exp2(m - tmax);                 // 0 while m is -inf
+                m = tmax;
+            }
+            if (__any(alpha != 1.0f)) {
+                l *= alpha;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pw[r] = vis[r] ? fast_exp2((float)(s64[r] - (double)mnew)) : 0.0f;
-            l = l * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
-            m = mnew;
+                for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
+            }
+            // weights times the rows' V scales (exactly 0 for a row this
+            // query does not see, whatever that row's scale holds), in three
+            // bf16 parts: B1 = (hi, mid), B2 = (lo, 0)
+            uint32_t hi[4], mid[4], lo[4];
+            float psum = 0.0f;
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) acc[cb] *= alpha;
+            for (int r = 0; r < 4; ++r) {
+                const float pw = vis[r] ? fast_exp2((float)(s64[r] - (double)m)) : 0.0f;
+                psum += pw;
+                bf16_split3(vis[r] ? pw * t.vs[r] : 0.0f, hi[r], mid[r], lo[r]);
+            }
+            l += psum;
+            const v4u b1u = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), mid[0] | (mid[1] << 16),
+                             mid[2] | (mid[3] << 16)};
+            const v4u b2u = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), 0u, 0u};
+            const v8bf b1 = __builtin_bit_cast(v8bf, b1u), b2 = __builtin_bit_cast(v8bf, b2u);
+            float vv[4][8];
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                // a row this query does not see weighs exactly 0: its V scale
-                // (of a never-written ring slot, say) never enters the product
-                const float pv = vis[s2] ? pw[s2] * t.vs[s2] : 0.0f;
-                float vv[8];
-                unpack(t.vc[s2], vv);
+            for (int r = 0; r < 4; ++r) unpack(t.vc[r], vv[r]);
 #pragma unroll
-                for (int cb = 0; cb < 8; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[cb], pv, acc[cb], 0, 0, 0);
+            for (int cb = 0; cb < 8; ++cb) {
+                const uint32_t a01 = bf16_pack(vv[0][cb], vv[1][cb]), a23 = bf16_pack(vv[2][cb], vv[3][cb]);
+                const v4u au = {a01, a23, a01, a23};
+                const v8bf av = __builtin_bit_cast(v8bf, au);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b2, acc[cb], 0, 0, 0);
             }
         };
-        int r0 = it.row0;
-        Tile ta, tb;
-        load_tile(r0, ta);
         // ping-pong with one exit at the loop head (as in k_decode_q8)
         while (r0 + kTileRows < it.row1) {
             load_tile(r0 + kTileRows, tb);
@@ -1610,9 +1734,15 @@ hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
                     : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, s);
 }
 
+#ifndef KVQ_VI8_WPS
+#define KVQ_VI8_WPS 1
+#endif
+#ifndef KVQ_VI8S_WPS
+#define KVQ_VI8S_WPS 0
+#endif
 hipError_t launch_verify_i8(const VerifyArgs& a, hipStream_t s) {
-    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, 0, s)
-                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, 1, s);
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, KVQ_VI8S_WPS, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, KVQ_VI8_WPS, s);
 }
 
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kQ8k>(a, s); }

@@ -195,26 +195,18 @@ struct VerifyArgs {
     float* v_store;
     int32_t sring[16];                       // ring slots of stream s live before its step
     int32_t swrow[16];                       // row of the sequence that stream s's step writes
-    // per-row int8 kind: the cache's codes and row scales, and the drafts'
-    // (verify) quantised mirror [batch][n_draft][n_kv_heads] rows
-    const int8_t* kq;
-    const float* ks;
-    const int8_t* vq;
-    const float* vs;
-    const int8_t* kdq;
-    const float* kds;
-    const int8_t* vdq;
-    const float* vds;
+    // per-row int8 kind: the cache's codes and row scales (the drafts and step
+    // rows are quantised inside the kernel), writable for the ring writes
+    int8_t* kq;
+    float* ks;
+    int8_t* vq;
+    float* vs;
 };
 constexpr int kVerifyMaxQ = 16;
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);   // a.shared: the shared-reference decode
 hipError_t launch_verify_i8(const VerifyArgs& a, hipStream_t s);    // the same on the per-row int8 kind
-// [P3] quantize_row_i8 of `rows` f32 rows [rows][128] (K and V) into codes
-// [rows][128] and scales [rows] (the verify's draft mirror)
-hipError_t launch_quant_rows_i8(const float* k, const float* v, int rows, int8_t* kq, float* ks, int8_t* vq,
-                                float* vs, hipStream_t s);
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_i8(const DecodeArgs& a, hipStream_t s);
 

@@ -564,21 +564,20 @@ def test_noalloc_decode_refusals_before_any_device_work():
     assert "64" in K.last_error() or "static" in K.last_error()
 
 
-def test_int8_verify_workspace_holds_the_draft_mirror():
-    """On the per-row int8 kind the verify workspace also holds the drafts'
-    int8 mirror (batch x drafts x KV heads rows of 2 x (128 codes + a
-    scale)); a workspace sized for the f32 kind is refused untouched."""
+def test_int8_verify_workspace_and_refusals():
+    """The verify workspace holds the partial states only, for either kind:
+    the int8 kind quantises its drafts inside the kernel.  A workspace one
+    block short is refused untouched, and a q8 cache has no ring."""
     f = fake_cache(K.KIND_F32, batch=3, hkv=4, cap=300)
     i = fake_cache(K.KIND_I8, batch=3, hkv=4, cap=300)
     wf, wi = K.kvq_verify_workspace_bytes(f, 8, 5), K.kvq_verify_workspace_bytes(i, 8, 5)
-    mirror = 3 * 5 * 4 * 2 * (128 + 4)
-    assert wi - wf == (mirror + 255) // 256 * 256
+    assert wi == wf and wi == K.kvq_workspace_bytes(i, 8 * 5)
     rings = K.Rings(3)
     for b in range(3):
         i.len[b] = 10
         assert call("rswa_record_prefill", i.ref, rings.ref, b) == K.OK
     before = snapshot(i, rings)
-    expect(call("rswa_verify", i.ref, rings.ref, 8, 5, FAKE, FAKE, FAKE, FAKE, FAKE, wf, None), K.EINVAL,
+    expect(call("rswa_verify", i.ref, rings.ref, 8, 5, FAKE, FAKE, FAKE, FAKE, FAKE, wi - 256, None), K.EINVAL,
            i, before, rings)
     q = fake_cache(K.KIND_Q8, batch=3, hkv=4, cap=300)
     bq = snapshot(q, rings)
