@@ -1253,6 +1253,9 @@ __device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
     return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+#ifndef KVQ_VI8_FAST_SHARED
+#define KVQ_VI8_FAST_SHARED 1
+#endif
 template <bool kShared>
 __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
     // trailing rows of the piece: K / V codes and scales
@@ -1346,7 +1349,7 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             float vs[4];
         };
         auto load_tile = [&](int r0, Tile& t) {
-            if (min(r0 + kTileRows - 1, it.row1 - 1) < L) {
+            if ((!kShared || KVQ_VI8_FAST_SHARED) && min(r0 + kTileRows - 1, it.row1 - 1) < L) {
                 // the whole tile in the cache (wave-uniform): no per-row choice
                 // of source, 32-bit offsets from the block's scalar base
                 const uint32_t pk = (uint32_t)min(r0 + qi, it.row1 - 1);
