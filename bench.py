@@ -406,17 +406,40 @@ def main():
                                                                  "kv_append_q8_one_row") if k in parts), 2)
 
     if do_q8:
-        # [P2] trim_window over every sequence (window 8192, slack 64, align 64):
-        # runs once, last, since it shortens the cache.  Bytes: each kept row
-        # of each live head read and written once.
+        # [P1] freeze_cols of one sequence (8 KV heads x 64 rows), the freeze
+        # an append of row 64 runs: 64 sequences frozen by 64 back-to-back
+        # kv_freeze_col_and_requant calls, bracketed by events.  Bytes per
+        # call: each row read once (the requantisation reads it from LDS) and
+        # written once, plus the fields.
+        fr = K.KvCache(K.KIND_Q8, bq.batch, bq.n_kv_heads, 64)
+        fk = t(workloads.normal_f32(workloads.key(bq.seed, 95), (64, bq.n_kv_heads, 128)))
+        fv = t(workloads.normal_f32(workloads.key(bq.seed, 94), (64, bq.n_kv_heads, 128)))
+        for b in range(bq.batch):
+            K.kv_append_q8(fr, b, 64, fk, fv)          # 64 rows: not frozen yet
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s_ev.record(stream)
+        for b in range(bq.batch):
+            K.kv_freeze_col_and_requant(fr, b)
+        e_ev.record(stream)
+        e_ev.synchronize()
+        us = s_ev.elapsed_time(e_ev) * 1e3 / bq.batch
+        nb = bq.n_kv_heads * (64 * 276 * 2 + 2 * 128 * 4)
+        parts["kv_freeze_one_seq_64_rows"] = {
+            "us_per_call": round(us, 2), "bytes": nb, "GBps": round(nb / us / 1e3, 1)}
+        del fr
+
+        # [P2] trim_window over every sequence (window 8192, slack 64, align 64)
+        # in one kv_trim_window call: runs once, last, since it shortens the
+        # cache.  Bytes: each kept row of each live head read and written once.
         lens_before = cq.len.copy()
         s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s_ev.record(stream)
-        dropped = [K.kv_trim_window(cq, b, 0, 8192, 64, 64)[1] for b in range(bq.batch)]
+        _, dropped = K.kv_trim_window(cq, K.ALL_SEQS, [0] * bq.batch, 8192, 64, 64)
         e_ev.record(stream)
         e_ev.synchronize()
-        moved = sum(int(lens_before[b]) - d for b, d in enumerate(dropped) if d > 0)
+        moved = sum(int(lens_before[b]) - int(d) for b, d in enumerate(dropped) if d > 0)
         us = s_ev.elapsed_time(e_ev) * 1e3
         nb = moved * cq.n_live * 276 * 2
         parts["kv_trim_window_all_seqs"] = {

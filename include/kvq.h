@@ -438,11 +438,16 @@ int kv_truncate_last(kvq_cache* c, int seq, int n_drop);
  * on stay, the cut rounded down to a multiple of max(align, 1):
  *   d = (keep_from / align) * align - base   rows are dropped if d > 0,
  * the remaining rows move to the front of the sequence's storage in order
- * (one kernel on `stream`), len -= d, *base += d.  anchor < 0 means none.
+ * (kernels on `stream`), len -= d, *base += d.  anchor < 0 means none.
  * *dropped (may be NULL) receives d.  Windowed decodes of the trimmed
  * sequence (first = len - w) see the same rows as before.
- * Errors: KVQ_EINVAL (null cache/base, seq out of range, *base, w, slack or
- * align < 0), KVQ_EDEVICE (launch failure).
+ * seq == KVQ_ALL_SEQS trims every sequence by the same rule (same w, slack,
+ * align and anchor): base is then a host array of batch entries, each the
+ * position of that sequence's row 0 (in/out), and dropped (may be NULL) an
+ * array of batch entries; all the moves run together, one launch per round
+ * of at most d rows per sequence.
+ * Errors: KVQ_EINVAL (null cache/base, seq out of range, any base, w, slack
+ * or align < 0), KVQ_EDEVICE (launch failure).
  */
 int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int align, int64_t anchor,
                    int* dropped, void* stream);

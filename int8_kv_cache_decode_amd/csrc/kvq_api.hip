@@ -723,39 +723,54 @@ int kv_trim_window(kvq_cache* c, int seq, int64_t* base, int w, int slack, int a
     int rc = check_cache(c, 0, fn);
     if (rc) return rc;
     if (!base) return fail(KVQ_EINVAL, "%s: null base", fn);
-    if (seq < 0 || seq >= c->batch) return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
-    if (*base < 0 || w < 0 || slack < 0 || align < 0)
-        return fail(KVQ_EINVAL, "%s: base %lld, w %d, slack %d, align %d must be >= 0", fn, (long long)*base, w, slack,
-                    align);
-    if (dropped) *dropped = 0;
-    const int64_t n = c->len[seq];
-    // [P2] trim_window_anchored, step by step
-    if (w == 0 || n <= 2 * (int64_t)w) return KVQ_OK;
-    if (c->kind == KVQ_KIND_Q8 && !c->frozen[seq]) return KVQ_OK;
-    const int64_t al = std::max(align, 1);
-    int64_t keep_from = std::max<int64_t>(*base + n - (w + slack), 0);
-    if (anchor >= 0) keep_from = std::min(keep_from, std::max<int64_t>(anchor - (w + slack), 0));
-    const int64_t new_base = keep_from / al * al;
-    if (new_base <= *base) return KVQ_OK;
-    const int d = (int)(new_base - *base);            // < n: new_base <= keep_from < base + n
-    MoveArgs m;
-    memset(&m, 0, sizeof m);
-    m.k = c->k;
-    m.v = c->v;
-    m.kq = c->kq;
-    m.ks = c->ks;
-    m.vq = c->vq;
-    m.vs = c->vs;
-    m.n_live = c->n_live;
-    m.capacity = c->capacity;
-    m.kind = c->kind;
-    m.seq = seq;
-    m.d = d;
-    m.keep = (int)(n - d);
-    if (c->n_live > 0 && (rc = device_status(launch_move_rows(m, (hipStream_t)stream), fn))) return rc;
-    c->len[seq] = (int32_t)(n - d);
-    *base = new_base;
-    if (dropped) *dropped = d;
+    if (seq != KVQ_ALL_SEQS && (seq < 0 || seq >= c->batch))
+        return fail(KVQ_EINVAL, "%s: seq %d outside 0..%d", fn, seq, c->batch - 1);
+    const int b0 = seq == KVQ_ALL_SEQS ? 0 : seq, b1 = seq == KVQ_ALL_SEQS ? c->batch : seq + 1;
+    // base / dropped: one entry, or one per sequence for KVQ_ALL_SEQS
+    int64_t* bases = seq == KVQ_ALL_SEQS ? base : base - b0;
+    int* drops = !dropped ? nullptr : seq == KVQ_ALL_SEQS ? dropped : dropped - b0;
+    if (w < 0 || slack < 0 || align < 0)
+        return fail(KVQ_EINVAL, "%s: w %d, slack %d, align %d must be >= 0", fn, w, slack, align);
+    for (int b = b0; b < b1; ++b)
+        if (bases[b] < 0) return fail(KVQ_EINVAL, "%s: base[%d] = %lld must be >= 0", fn, b, (long long)bases[b]);
+    // [P2] trim_window_anchored, step by step, for each sequence
+    std::vector<TrimMove> moves;
+    std::vector<int64_t> new_base(b1 - b0);
+    for (int b = b0; b < b1; ++b) {
+        new_base[b - b0] = bases[b];
+        const int64_t n = c->len[b];
+        if (w == 0 || n <= 2 * (int64_t)w) continue;
+        if (c->kind == KVQ_KIND_Q8 && !c->frozen[b]) continue;
+        const int64_t al = std::max(align, 1);
+        int64_t keep_from = std::max<int64_t>(bases[b] + n - (w + slack), 0);
+        if (anchor >= 0) keep_from = std::min(keep_from, std::max<int64_t>(anchor - (w + slack), 0));
+        const int64_t nb = keep_from / al * al;
+        if (nb <= bases[b]) continue;
+        const int d = (int)(nb - bases[b]);            // < n: nb <= keep_from < base + n
+        moves.push_back({b, d, (int)(n - d)});
+        new_base[b - b0] = nb;
+    }
+    if (c->n_live > 0 && !moves.empty()) {
+        MoveArgs m;
+        memset(&m, 0, sizeof m);
+        m.k = c->k;
+        m.v = c->v;
+        m.kq = c->kq;
+        m.ks = c->ks;
+        m.vq = c->vq;
+        m.vs = c->vs;
+        m.n_live = c->n_live;
+        m.capacity = c->capacity;
+        m.kind = c->kind;
+        if ((rc = device_status(launch_trim_moves(m, moves.data(), (int)moves.size(), (hipStream_t)stream), fn)))
+            return rc;
+    }
+    for (int b = b0; b < b1; ++b) {
+        const int d = (int)(new_base[b - b0] - bases[b]);
+        c->len[b] -= d;
+        bases[b] = new_base[b - b0];
+        if (drops) drops[b] = d;
+    }
     return KVQ_OK;
 }
 

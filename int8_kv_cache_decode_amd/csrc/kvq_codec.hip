@@ -10,6 +10,8 @@
 // with -ffp-contract=off).
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -108,69 +110,116 @@ __global__ __launch_bounds__(128) void k_append_i8(const AppendArgs a) {
     if (lane == 0) (is_k ? a.ks : a.vs)[hrow] = s;
 }
 
-// Freeze + requantise ([P1] freeze_cols) for one (sequence, live head).
-// block 128: thread d owns channel d.  The RMS sum runs over the rows in
-// order, multiply then add, exactly as the page's loop does per channel.
-__global__ __launch_bounds__(128) void k_freeze(const FreezeArgs a) {
-    __shared__ float red[2][2];
+// Freeze + requantise ([P1] freeze_cols) for one (sequence, live head), one
+// block of kFreezeThreads.  The stored rows are staged in LDS kFreezeRows at a
+// time (K codes in their tile-major order, the K scale records, V codes, V
+// scales) with 16-byte loads.  Threads 0..127 own the K channels and 128..255
+// the V channels for the RMS sum, which runs over the rows in order, multiply
+// then add, exactly as the page's loop does per channel.  Once the field is
+// known every row is requantised on its own: wave w takes rows w, w + 16, ..
+// of the chunk, lane l channels 2 l and 2 l + 1, the K group max over 16
+// lanes and the V row max over the wave.
+constexpr int kFreezeRows = 64;
+constexpr int kFreezeThreads = 1024;
+
+__global__ __launch_bounds__(kFreezeThreads) void k_freeze(const FreezeArgs a) {
+    __shared__ __attribute__((aligned(16))) int8_t s_kq[kFreezeRows * kHD];
+    __shared__ __attribute__((aligned(16))) int8_t s_vq[kFreezeRows * kHD];
+    __shared__ __attribute__((aligned(16))) float s_ks[kFreezeRows * kKScales];
+    __shared__ float s_vs[kFreezeRows];
+    __shared__ float s_col[2 * kHD];
     const int gl = blockIdx.x, j = blockIdx.y;
     const int b = a.seq[j], n = a.n[j];
-    const int d = threadIdx.x, wave = d >> 6, lane = d & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    constexpr int kWavesF = kFreezeThreads / 64;
     const size_t head = (size_t)b * a.n_live + gl;
     const size_t row0 = head * a.capacity;
+    int8_t* KQ = a.kq + head * kq_rows(a.capacity) * kHD;    // tile-major K codes
+    float* KS = a.ks + row0 * kKScales;
+    int8_t* VQ = a.vq + row0 * kHD;
+    float* VS = a.vs + row0;
 
-    // ---- K: group of 32 channels, scale per (row, group) ----
-    {
-        int8_t* q = a.kq + head * kq_rows(a.capacity) * kHD;    // tile-major K codes
-        float* s = a.ks + row0 * kKScales;
-        float acc = 0.0f;
-        for (int p = 0; p < n; ++p) {
-            const float x = (float)q[kq_offset(p, d)] * s[(size_t)p * kKScales + d / kKGroup];
-            const float sq = x * x;
-            acc = acc + sq;
+    // rows [p0, p0 + m) into LDS (p0 a multiple of kFreezeRows; the K tile
+    // holding the last row is whole in storage)
+    auto stage = [&](int p0, int m) {
+        const int m16 = (m + kTileRows - 1) & ~(kTileRows - 1);
+        for (int i = tid; i < m16 * kHD / 16; i += kFreezeThreads)
+            *(uint4*)(s_kq + 16 * i) = *(const uint4*)(KQ + (size_t)p0 * kHD + 16 * i);
+        for (int i = tid; i < m * kHD / 16; i += kFreezeThreads)
+            *(uint4*)(s_vq + 16 * i) = *(const uint4*)(VQ + (size_t)p0 * kHD + 16 * i);
+        for (int i = tid; i < m; i += kFreezeThreads) {
+            *(float4*)(s_ks + kKScales * i) = *(const float4*)(KS + (size_t)(p0 + i) * kKScales);
+            s_vs[i] = VS[p0 + i];
         }
-        const float col = fmaxf(sqrtf(__fdiv_rn(acc, (float)n)), 1e-6f);
-        a.kcol[head * kHD + d] = col;
-        for (int p = 0; p < n; ++p) {
-            const float x = (float)q[kq_offset(p, d)] * s[(size_t)p * kKScales + d / kKGroup];
-            const float r = __fdiv_rn(x, col);
-            const float sc = group_scale(group_max<32>(fabsf(r)));
-            q[kq_offset(p, d)] = quant_code(r, sc);
-            if ((d & (kKGroup - 1)) == 0) s[(size_t)p * kKScales + d / kKGroup] = sc;
+    };
+
+    // ---- the RMS of each channel over the n stored rows, in row order ----
+    const bool is_k = tid < kHD;
+    const int d = tid & (kHD - 1);
+    float acc = 0.0f;
+    for (int p0 = 0; p0 < n; p0 += kFreezeRows) {
+        const int m = min(kFreezeRows, n - p0);
+        if (p0 > 0) __syncthreads();                   // the previous chunk is summed
+        stage(p0, m);
+        __syncthreads();
+        if (tid < 2 * kHD) {
+            for (int p = 0; p < m; ++p) {
+                const float x = is_k ? (float)s_kq[kq_offset(p, d)] * s_ks[kKScales * p + d / kKGroup]
+                                     : (float)s_vq[p * kHD + d] * s_vs[p];
+                const float sq = x * x;
+                acc = acc + sq;
+            }
         }
     }
-    // ---- V: one group of 128 channels, scale per row ----
-    {
-        int8_t* q = a.vq + row0 * kHD;
-        float* s = a.vs + row0;
-        float acc = 0.0f;
-        for (int p = 0; p < n; ++p) {
-            const float x = (float)q[(size_t)p * kHD + d] * s[p];
-            const float sq = x * x;
-            acc = acc + sq;
-        }
+    if (tid < 2 * kHD) {
         const float col = fmaxf(sqrtf(__fdiv_rn(acc, (float)n)), 1e-6f);
-        a.vcol[head * kHD + d] = col;
-        for (int p = 0; p < n; ++p) {
-            const float x = (float)q[(size_t)p * kHD + d] * s[p];
-            const float r = __fdiv_rn(x, col);
-            const float wm = group_max<64>(fabsf(r));
-            if (lane == 0) red[p & 1][wave] = wm;
-            __syncthreads();                       // every thread has read s[p]
-            const float sc = group_scale(fmaxf(red[p & 1][0], red[p & 1][1]));
-            q[(size_t)p * kHD + d] = quant_code(r, sc);
-            if (d == 0) s[p] = sc;
+        (is_k ? a.kcol : a.vcol)[head * kHD + d] = col;
+        s_col[tid] = col;
+    }
+
+    // ---- every row requantised against the field (rows are independent) ----
+    for (int p0 = 0; p0 < n; p0 += kFreezeRows) {
+        const int m = min(kFreezeRows, n - p0);
+        __syncthreads();                               // s_col written; the previous chunk is done
+        if (n > kFreezeRows) {                         // otherwise the only chunk is still staged
+            stage(p0, m);
+            __syncthreads();
+        }
+        const int c = 2 * lane;
+        for (int p = wave; p < m; p += kWavesF) {
+            // K: groups of 32 channels (16 lanes)
+            const char2 kc = *(const char2*)(s_kq + kq_offset(p, c));
+            const float ksc = s_ks[kKScales * p + c / kKGroup];
+            const float r0 = __fdiv_rn((float)kc.x * ksc, s_col[c]);
+            const float r1 = __fdiv_rn((float)kc.y * ksc, s_col[c + 1]);
+            const float sk = group_scale(group_max<16>(fmaxf(fabsf(r0), fabsf(r1))));
+            char2 qk;
+            qk.x = quant_code(r0, sk);
+            qk.y = quant_code(r1, sk);
+            *(char2*)(KQ + kq_offset(p0 + p, c)) = qk;
+            if ((lane & 15) == 0) KS[(size_t)(p0 + p) * kKScales + lane / 16] = sk;
+            // V: one group of 128 channels (the wave)
+            const char2 vc = *(const char2*)(s_vq + p * kHD + c);
+            const float vsc = s_vs[p];
+            const float v0 = __fdiv_rn((float)vc.x * vsc, s_col[kHD + c]);
+            const float v1 = __fdiv_rn((float)vc.y * vsc, s_col[kHD + c + 1]);
+            const float sv = group_scale(group_max<64>(fmaxf(fabsf(v0), fabsf(v1))));
+            char2 qv;
+            qv.x = quant_code(v0, sv);
+            qv.y = quant_code(v1, sv);
+            *(char2*)(VQ + (size_t)(p0 + p) * kHD + c) = qv;
+            if (lane == 0) VS[p0 + p] = sv;
         }
     }
 }
 
-// Front-trim move ([P2] trim_window: the rows that stay keep their order and
-// values), one chunk of m <= d rows per launch: rows [src, src + m) go to
-// [dst, dst + m) with src - dst = d >= m, so a launch's source and
-// destination never overlap, and consecutive launches on the stream order a
-// chunk's reads before the next chunk's writes.  grid (blocks, live head,
-// buffer), block 256, a grid-stride loop of 16-byte copies (4-byte for the
-// one-per-row scales: vs, and ks of the per-row int8 kind).
+// Front-trim moves ([P2] trim_window: the rows that stay keep their order and
+// values), one round per launch for every sequence listed in it: rows [src,
+// src + m) go to [dst, dst + m) with src - dst = d >= m, so a launch's source
+// and destination never overlap, and consecutive launches on the stream order
+// a round's reads before the next round's writes.  grid (blocks, sequence x
+// live head, buffer), block 256, a grid-stride loop of 16-byte copies (4-byte
+// for the one-per-row scales: vs, and ks of the per-row int8 kind).
 template <class T>
 __device__ __forceinline__ void copy_rows(T* base, int units_per_row, int src, int dst, int m) {
     const T* s = base + (size_t)src * units_per_row;
@@ -196,8 +245,10 @@ __device__ __forceinline__ void copy_kq_rows(int8_t* base, int src, int dst, int
     }
 }
 
-__global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, int dst, int m) {
-    const size_t head = (size_t)a.seq * a.n_live + blockIdx.y;
+__global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a) {
+    const int j = blockIdx.y / a.n_live, gl = blockIdx.y - j * a.n_live;
+    const int src = a.src[j], dst = a.dst[j], m = a.m[j];
+    const size_t head = (size_t)a.seq[j] * a.n_live + gl;
     const size_t row0 = head * a.capacity;
     const int z = blockIdx.z;
     const int which = a.kind == KVQ_KIND_F32 ? 4 + z : (a.kind == KVQ_KIND_I8 && z == 1) ? 6 : z;
@@ -214,18 +265,38 @@ __global__ __launch_bounds__(256) void k_move_chunk(const MoveArgs a, int src, i
 
 }  // namespace
 
-hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s) {
-    for (int r = 0; r < a.keep; r += a.d) {
-        const int m = min(a.d, a.keep - r);
-        const bool f32 = a.kind == KVQ_KIND_F32;
-        const size_t units = (size_t)m * (f32 ? kHD / 4 : kHD / 16);     // largest buffer, 16-byte units
-        const size_t want = (units + 1023) / 1024;
-        const int blocks = (int)(want < 128 ? want : 128);
-        hipLaunchKernelGGL(k_move_chunk, dim3(blocks, a.n_live, f32 ? 2 : 4), dim3(256), 0, s, a, a.d + r, r, m);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+hipError_t launch_trim_moves(const MoveArgs& args, const TrimMove* moves, int count, hipStream_t s) {
+    const bool f32 = args.kind == KVQ_KIND_F32;
+    for (int r = 0;; ++r) {                            // round r moves rows [r d, r d + m) of each sequence
+        bool any = false;
+        int i = 0;
+        while (i < count) {
+            MoveArgs a = args;
+            a.n_seq = 0;
+            int mmax = 0;
+            for (; i < count && a.n_seq < kSeqPerLaunch; ++i) {
+                const TrimMove& mv = moves[i];
+                const int64_t at = (int64_t)r * mv.d;
+                if (mv.d <= 0 || at >= mv.keep) continue;
+                const int m = (int)std::min<int64_t>(mv.d, mv.keep - at);
+                a.seq[a.n_seq] = mv.seq;
+                a.src[a.n_seq] = (int)(at + mv.d);
+                a.dst[a.n_seq] = (int)at;
+                a.m[a.n_seq] = m;
+                ++a.n_seq;
+                mmax = std::max(mmax, m);
+            }
+            if (a.n_seq == 0) continue;
+            any = true;
+            const size_t units = (size_t)mmax * (f32 ? kHD / 4 : kHD / 16);   // largest buffer, 16-byte units
+            const size_t want = (units + 1023) / 1024;
+            const int blocks = (int)(want < 128 ? want : 128);
+            hipLaunchKernelGGL(k_move_chunk, dim3(blocks, a.n_live * a.n_seq, f32 ? 2 : 4), dim3(256), 0, s, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (!any) return hipSuccess;
     }
-    return hipSuccess;
 }
 
 hipError_t launch_append_f32(const AppendArgs& a, int n_rows, hipStream_t s) {
@@ -244,7 +315,7 @@ hipError_t launch_append_i8(const AppendArgs& a, int n_rows, hipStream_t s) {
 }
 
 hipError_t launch_freeze(const FreezeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_freeze, dim3(a.n_live, a.n_seq), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_freeze, dim3(a.n_live, a.n_seq), dim3(kFreezeThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -81,8 +81,11 @@ struct FreezeArgs {
     int32_t n[kSeqPerLaunch];                // rows to freeze over
 };
 
-// Front-trim move of one sequence: rows [d, d + keep) of every live head go
-// to rows [0, keep), in order.
+// Front-trim moves ([P2] trim_window): sequence seq[i] drops its first d[i]
+// rows, rows [d, d + keep) of every live head going to rows [0, keep) in
+// order.  The moves run in rounds of at most d rows per sequence, one launch
+// per round for all the sequences that still have rows to move, so that a
+// launch's source and destination rows never overlap.
 struct MoveArgs {
     float* k;
     float* v;
@@ -93,9 +96,14 @@ struct MoveArgs {
     int n_live;
     int capacity;
     int kind;       // KVQ_KIND_*: which buffers move
-    int seq;
-    int d;
-    int keep;
+    int n_seq;      // sequences in this launch
+    int32_t seq[kSeqPerLaunch];
+    int32_t src[kSeqPerLaunch];   // first source row of the round's chunk
+    int32_t dst[kSeqPerLaunch];   // first destination row
+    int32_t m[kSeqPerLaunch];     // rows the round moves
+};
+struct TrimMove {
+    int seq, d, keep;
 };
 
 // grid (n_rows, n_seq, n_live)
@@ -104,8 +112,9 @@ hipError_t launch_append_q8(const AppendArgs& a, int n_rows, hipStream_t s);
 hipError_t launch_append_i8(const AppendArgs& a, int n_rows, hipStream_t s);
 // grid (n_live, n_seq)
 hipError_t launch_freeze(const FreezeArgs& a, hipStream_t s);
-// one launch per chunk of d rows
-hipError_t launch_move_rows(const MoveArgs& a, hipStream_t s);
+// the moves of every listed sequence, one launch per round (a: buffers and
+// geometry; its per-sequence fields are filled here)
+hipError_t launch_trim_moves(const MoveArgs& a, const TrimMove* moves, int count, hipStream_t s);
 
 // ---- decode --------------------------------------------------------------
 struct DecodeArgs {

@@ -340,9 +340,19 @@ def kv_truncate_last(cache: KvCache, seq: int, n_drop: int) -> None:
     _check(lib().kv_truncate_last(cache.ref, seq, n_drop))
 
 
-def kv_trim_window(cache: KvCache, seq: int, base: int, w: int, slack: int, align: int, anchor: int = -1,
+def kv_trim_window(cache: KvCache, seq: int, base, w: int, slack: int, align: int, anchor: int = -1,
                    stream=None):
-    """Returns (new base, rows dropped)."""
+    """Returns (new base, rows dropped).  seq == ALL_SEQS: base is one
+    position per sequence and the result is (bases, dropped) as int64 /
+    int32 arrays."""
+    if seq == ALL_SEQS:
+        b = np.ascontiguousarray(base, np.int64).copy()
+        d = np.zeros(b.shape[0], np.int32)
+        if b.shape[0] != cache.batch:
+            raise ValueError("one base per sequence")
+        _check(lib().kv_trim_window(cache.ref, seq, b.ctypes.data, w, slack, align, anchor, d.ctypes.data,
+                                    _stream(stream)))
+        return b, d
     b = ctypes.c_int64(base)
     d = ctypes.c_int(0)
     _check(lib().kv_trim_window(cache.ref, seq, ctypes.byref(b), w, slack, align, anchor, ctypes.byref(d),

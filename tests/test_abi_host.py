@@ -228,6 +228,13 @@ def test_trim_window_no_op_cases_and_refusals():
         expect(call("kv_trim_window", c.ref, 0, ctypes.byref(base), w, sl, al, -1, None, 0), K.EINVAL, c, before)
     base = ctypes.c_int64(-3)
     expect(call("kv_trim_window", c.ref, 0, ctypes.byref(base), 5, 1, 1, -1, None, 0), K.EINVAL, c, before)
+    # every sequence at once: one base per sequence; a negative one is refused
+    # before anything changes, no-op rows report 0 dropped
+    bases = (ctypes.c_int64 * 2)(0, -1)
+    expect(call("kv_trim_window", c.ref, K.ALL_SEQS, bases, 5, 1, 1, -1, None, 0), K.EINVAL, c, before)
+    assert list(bases) == [0, -1]
+    nb, nd = K.kv_trim_window(c, K.ALL_SEQS, [0, 12], 10, 2, 32, stream=0)   # no sequence trims
+    assert list(nb) == [0, 12] and list(nd) == [0, 0] and list(c.len) == [20, 21]
 
 
 def test_ring_checkpoint_and_rollback_cursors():

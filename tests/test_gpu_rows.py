@@ -37,14 +37,18 @@ TRIMS = [([3000, 2001], 1400, 150, 16, -1),
          ([2001, 700], 1000, 0, 4, -1),
          ([900, 2500], 300, 2, 64, -1),
          ([1500, 1500], 200, 10, 8, 900),
-         ([300, 100], 200, 10, 8, -1)]
+         ([300, 100], 200, 10, 8, -1),
+         # several sequences moving 1 to 10 rounds of rows in the same launches
+         ([3000, 2001, 620, 700, 610, 5], 300, 250, 8, -1)]
 
 
+@pytest.mark.parametrize("all_seqs", [False, True])
 @pytest.mark.parametrize("case", range(len(TRIMS)))
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
-def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
+def test_trim_window_moves_rows_and_keeps_the_window(kind, case, all_seqs):
     lens, w, slack, align, anchor = TRIMS[case]
-    say("case: trim kind", kind, "lens", lens, "w", w, "slack", slack, "align", align, "anchor", anchor)
+    say("case: trim kind", kind, "lens", lens, "w", w, "slack", slack, "align", align, "anchor", anchor,
+        "all sequences" if all_seqs else "one call per sequence")
     r = rng(100 + case + 10 * kind)
     hkv, hpk = 3, 2
     alive = np.array([1, 0, 1], np.uint8)
@@ -59,13 +63,19 @@ def test_trim_window_moves_rows_and_keeps_the_window(kind, case):
     torch.cuda.synchronize()
     before = {nm: host(c.view(nm)).copy() for nm in BUFS[kind]}
     q = r.standard_normal((len(lens), hkv * hpk, 128)).astype(np.float32)
-    bases = []
-    for b, n in enumerate(lens):
-        want = oracle.trim_window(0, n, w, slack, align, None if anchor < 0 else anchor,
-                                  q8_unfrozen=(kind == K.KIND_Q8 and n < 64))
-        base, d = K.kv_trim_window(c, b, 0, w, slack, align, anchor)
-        assert d == want and base == d and c.len[b] == n - d
-        bases.append(base)
+    want = [oracle.trim_window(0, n, w, slack, align, None if anchor < 0 else anchor,
+                               q8_unfrozen=(kind == K.KIND_Q8 and n < 64)) for n in lens]
+    if all_seqs:
+        nb, nd = K.kv_trim_window(c, K.ALL_SEQS, [0] * len(lens), w, slack, align, anchor)
+        assert list(nd) == want and list(nb) == want
+        bases = [int(x) for x in nb]
+    else:
+        bases = []
+        for b, n in enumerate(lens):
+            base, d = K.kv_trim_window(c, b, 0, w, slack, align, anchor)
+            assert d == want[b] and base == d
+            bases.append(base)
+    assert all(c.len[b] == n - want[b] for b, n in enumerate(lens))
     torch.cuda.synchronize()
     # every live head's rows [d, n) now sit at [0, n - d), bit for bit
     for nm in BUFS[kind]:
