@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--replicas", type=int, default=4, help="f32 R-SWA cache replicas (>= 1 GB total)")
-    p.add_argument("--part", choices=["both", "rswa", "q8"], default="both")
+    p.add_argument("--part", choices=["both", "rswa", "q8", "small"], default="both",
+                   help="small: only the three small workloads' per-call timings (no step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-small", action="store_true", help="skip the three small workloads")
     p.add_argument("--cpu-sample-seqs", type=int, default=8)
@@ -371,6 +372,12 @@ def main():
             K.kv_append_q8(cq, K.ALL_SEQS, 1, newk, newv)
         if int(cq.len.max()) + 40 <= cq.capacity:
             parts["kv_append_q8_one_row"] = {"us_per_call": round(time_calls(app_call, 5, repeats=1), 2)}
+
+    if args.part == "small":
+        # the three small workloads only: per-call timings, no decode step
+        small_parts(parts, K, t, dev, time_calls, log, True, True)
+        print(json.dumps({"metric": METRIC, "unit": "KV positions/s", "n_gpus": 1, "parts": parts}), flush=True)
+        return
 
     # ---------------- the timed decode steps ----------------
     # They run after the per-part timing above, so the GPU's clocks have
