@@ -372,20 +372,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 //
 // The online softmax runs in that (head, row) layout with a lazily refreshed
 // max: it moves only when a tile exceeds it by more than kLazy (log2 units),
-// so weights stay <= 2^kLazy and the accumulators are rarely rescaled.  The
-// weights times the V row scales go through a per-wave LDS slot to the V
-// layout -- lane (ri = lane / kVSeg, seg = lane % kVSeg) owns rows
-// ri + kVRows * i of each tile and kVDim channels -- where V codes become f32 (one
-// sign-extending byte convert each) and accumulate per head in f32.  Every
-// KVQ_Q8_FLUSH tiles the f32 accumulators are summed over the four row
-// groups and added into f64 accumulators in LDS (each lane owns 2 hpk of
-// them), and the running sum of weights is f64, so a wave's long share adds
-// no error that grows with its length.  The V column field is applied once
-// in the combine ([P1] attend: acc (.) vcol at the end).
+// so weights stay <= 2^kLazy and the accumulators are rarely rescaled.  Each
+// weight times its row's V scale is split exactly into three bf16 parts and
+// goes through a per-wave LDS slot to the value pass, which runs on
+// v_mfma_f32_16x16x32_bf16 in the V layout -- lane (ri = lane / kVSeg, seg =
+// lane % kVSeg) holds rows ri + kVRows * i of each tile and the kVDim
+// channels of seg -- with the V codes (exact in bf16) as the A operand of
+// each 8-channel block and the weights' parts as the B operand, one column
+// per (part, head).  Every KVQ_Q8_FLUSH tiles the three parts of each f32
+// accumulator are summed (DPP) and added into f64 accumulators in LDS, and
+// the running sum of weights is f64, so a wave's long share adds no error
+// that grows with its length.  The V column field is applied once in the
+// combine ([P1] attend: acc (.) vcol at the end).
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr float kLazy = 8.0f;
+// x plus the x of the lanes 4 and 8 above it in its 16-lane row (DPP row
+// shifts; lanes past the row's end contribute 0).
+__device__ __forceinline__ float add_shl4_shl8(float x) {
+    const float a = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xf, 0xf, true));
+    const float b = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xf, 0xf, true));
+    return (x + a) + b;
+}
+// w = hi + mid + lo exactly (w normal): each part is the top 16 bits (sign,
+// exponent, 7 mantissa bits: a bf16) of the remainder, and the remainders
+// are exact f32 subtractions; the last one has at most 8 significant bits.
+__device__ __forceinline__ void bf16_split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t h = __float_as_uint(w) & 0xffff0000u;
+    const float r1 = w - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(m);
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = __float_as_uint(r2) >> 16;
+}
+// Two bf16 values (the top halves of two f32 that are exact in bf16) in one dword.
+__device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
 
 // V layout of the q8 kernel: lane (ri = lane / 16, seg = lane % 16) owns
 // rows ri + 4 i (i < 4) of a 16-row tile and the 8 channels [8 seg, 8 seg + 8),
@@ -442,7 +469,8 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 template <int HPK, bool kCap, bool kI8>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
-    __shared__ float sm_pw[kWaves][2][16][HPK];       // per wave, two tiles: weight * vs per [row][head]
+    // per wave, two tiles: the bf16 parts of weight * vs, [head][part][row % 4][row / 4]
+    __shared__ __attribute__((aligned(8))) uint16_t sm_wb[kWaves][2][4 * NB][3][4][4];
     __shared__ float sm_alpha[kWaves][2][HPK];        // per wave, two tiles: rescale factor per head
     __shared__ double sm_v64[kWaves][HPK][kHD];       // per wave: flushed V accumulators
     // i8 kind, R-SWA: the ring row's fresh K / V codes and their scales
@@ -644,17 +672,11 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 
         float m[NB];
         double l[NB];
-        float acc[HPK][kVDim];
 #pragma unroll
         for (int hb = 0; hb < NB; ++hb) {
             m[hb] = -INFINITY;
             l[hb] = 0.0;
         }
-#pragma unroll
-        for (int h = 0; h < HPK; ++h)
-#pragma unroll
-            for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
-
         // f64 accumulators of this lane: entries kOwn * ri + i of the seg's
         // (head, channel) list e = kVDim * head + channel.
         constexpr int kOwn = HPK * kVDim / kVRows;
@@ -664,31 +686,34 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         };
 #pragma unroll
         for (int i = 0; i < kOwn; ++i) cell(i) = 0.0;
-        // Sum acc over the four row groups (a transposing butterfly leaves lane
-        // ri with entries [kOwn ri, kOwn ri + kOwn)), add into f64, clear acc.
+        // Value pass on v_mfma_f32_16x16x32_bf16, one per 8-channel block cb
+        // (channels 8 m + cb, m = lane % 16) and block of 4 heads: A = the V
+        // codes of the lane's four rows ri + 4 i (exact in bf16; K slots 4..7
+        // zero), B = the weights times the rows' V scales in three exact bf16
+        // parts, column n = 4 part + head.  Lane l accumulates, for its column
+        // (part, head) = (l % 16 / 4, l % 4), channels 8 (4 (l / 16) + i) + cb.
+        v4f accv[NB][8];
+#pragma unroll
+        for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) accv[hb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+        const int bpart = (lane & 15) >> 2, bhead = lane & 3;
+        // The three parts summed onto the part-0 lanes (DPP), added into f64.
         auto flush = [&]() {
-            constexpr int N = HPK * kVDim;
-            float y[N / 2], z[kOwn];
 #pragma unroll
-            for (int i = 0; i < N / 2; ++i) {
-                // lanes 0..31 keep entry i, lanes 32..63 entry i + N / 2
-                float lo = acc[i / kVDim][i % kVDim], hi = acc[(i + N / 2) / kVDim][(i + N / 2) % kVDim];
-                swap32(lo, hi);
-                y[i] = lo + hi;
+            for (int hb = 0; hb < NB; ++hb) {
+                const int h = 4 * hb + bhead;
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = add_shl4_shl8(accv[hb][cb][i]);
+                        if (bpart == 0 && h < HPK) sm_v64[wave][h][8 * (4 * ri + i) + cb] += (double)x;
+                    }
+#pragma unroll
+                for (int cb = 0; cb < 8; ++cb) accv[hb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int i = 0; i < kOwn; ++i) {
-                // rows with lane bit 4 clear keep y[i], the others y[i + kOwn]
-                float lo = y[i], hi = y[i + kOwn];
-                swap16(lo, hi);
-                z[i] = lo + hi;
-            }
-#pragma unroll
-            for (int i = 0; i < kOwn; ++i) cell(i) += (double)z[i];
-#pragma unroll
-            for (int h = 0; h < HPK; ++h)
-#pragma unroll
-                for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
+            wave_lds_sync();
         };
         int since_flush = 0;
 
@@ -759,7 +784,11 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
                 l[hb] = fma(l[hb], (double)alpha, (double)p);
                 m[hb] = mnew;
                 if (h < HPK) {
-                    sm_pw[wave][buf][n][h] = p * t.vsn;
+                    uint32_t ph, pm, pl;
+                    bf16_split3(p * t.vsn, ph, pm, pl);
+                    sm_wb[wave][buf][h][0][n & 3][n >> 2] = (uint16_t)ph;
+                    sm_wb[wave][buf][h][1][n & 3][n >> 2] = (uint16_t)pm;
+                    sm_wb[wave][buf][h][2][n & 3][n >> 2] = (uint16_t)pl;
                     if (n == 0) sm_alpha[wave][buf][h] = alpha;
                 }
             }
@@ -768,26 +797,36 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             // ---- V accumulation in the (row, channel) layout ----
             if (rescale) {
 #pragma unroll
-                for (int h = 0; h < HPK; ++h) {
-                    const float al = sm_alpha[wave][buf][h];
+                for (int hb = 0; hb < NB; ++hb) {
+                    const int h = 4 * hb + bhead;
+                    const float al = h < HPK ? sm_alpha[wave][buf][h] : 1.0f;
 #pragma unroll
-                    for (int c = 0; c < kVDim; ++c) acc[h][c] *= al;
+                    for (int cb = 0; cb < 8; ++cb) accv[hb][cb] *= al;
                 }
 #pragma unroll
                 for (int i = 0; i < kOwn; ++i) cell(i) *= (double)sm_alpha[wave][buf][(kOwn * ri + i) / kVDim];
             }
-            // f32 FMA chains of 4 rows per tile between two f64 flushes
+            v8bf bw[NB];
 #pragma unroll
-            for (int i = 0; i < kVLoads; ++i) {
-                float w[HPK];
+            for (int hb = 0; hb < NB; ++hb) {
+                v4u bu = {0u, 0u, 0u, 0u};
+                if (bpart < 3 && 4 * hb + bhead < HPK) {
+                    const uint2 x = *(const uint2*)(&sm_wb[wave][buf][4 * hb + bhead][bpart][ri][0]);
+                    bu[0] = x.x;
+                    bu[1] = x.y;
+                }
+                bw[hb] = __builtin_bit_cast(v8bf, bu);
+            }
+            float vf[kVLoads][kVDim];
 #pragma unroll
-                for (int h = 0; h < HPK; ++h) w[h] = sm_pw[wave][buf][ri + kVRows * i][h];
-                float vf[kVDim];
-                unpack(t.vx[i], vf);
+            for (int i = 0; i < kVLoads; ++i) unpack(t.vx[i], vf[i]);
 #pragma unroll
-                for (int h = 0; h < HPK; ++h)
+            for (int cb = 0; cb < kVDim; ++cb) {
+                const v4u au = {bf16_pack(vf[0][cb], vf[1][cb]), bf16_pack(vf[2][cb], vf[3][cb]), 0u, 0u};
+                const v8bf av = __builtin_bit_cast(v8bf, au);
 #pragma unroll
-                    for (int c = 0; c < kVDim; ++c) acc[h][c] = fmaf(w[h], vf[c], acc[h][c]);
+                for (int hb = 0; hb < NB; ++hb)
+                    accv[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[hb], accv[hb][cb], 0, 0, 0);
             }
             buf ^= 1;
             if (++since_flush == KVQ_Q8_FLUSH) {
@@ -1233,26 +1272,6 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
 // ring slots live before the step except the one the step overwrites, and its
 // own step row.
 // ---------------------------------------------------------------------------
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
-// w = hi + mid + lo exactly (w normal): each part is the top 16 bits (sign,
-// exponent, 7 mantissa bits: a bf16) of the remainder, and the remainders
-// are exact f32 subtractions; the last one has at most 8 significant bits.
-__device__ __forceinline__ void bf16_split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-    const uint32_t h = __float_as_uint(w) & 0xffff0000u;
-    const float r1 = w - __uint_as_float(h);
-    const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
-    const float r2 = r1 - __uint_as_float(m);
-    hi = h >> 16;
-    mid = m >> 16;
-    lo = __float_as_uint(r2) >> 16;
-}
-// Two bf16 values (the top halves of two f32 that are exact in bf16) in one dword.
-__device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
 #ifndef KVQ_VI8_FAST_SHARED
 #define KVQ_VI8_FAST_SHARED 1
 #endif
