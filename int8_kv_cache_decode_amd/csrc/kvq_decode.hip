@@ -240,6 +240,107 @@ __device__ __forceinline__ double soft_cap(double s, double c2, double inv_c2) {
     return copysign(c2 * ((1.0 - e) / (1.0 + e)), s);
 }
 
+// The fold of one piece of an f32 segment by one wave: the online-softmax
+// state per Q head of the group over rows [row0, row1) -- max m and sum l in
+// log2 units (l summed over the wave) and the weighted V sum acc, lane l < 32
+// holding channels 4 l .. 4 l + 3.  The wave whose piece holds the R-SWA row
+// stores it into the ring first (nobody else reads that row).
+template <int HPK, bool kCap>
+__device__ __forceinline__ void f32_piece(const DecodeArgs& a, const Piece& it, float (&m)[HPK], float (&lsum)[HPK],
+                                          float4 (&acc)[HPK]) {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5, seg = lane & 31;
+    const double inv_c2 = kCap ? 1.0 / a.softcap2 : 0.0;
+    const float* K = a.k + it.hrow * kHD;
+    const float* V = a.v + it.hrow * kHD;
+    const int wrow = a.wrow[it.j];
+    const bool has_w = wrow >= it.row0 && wrow < it.row1;
+    const float* kn = has_w ? a.k_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : K;
+    const float* vn = has_w ? a.v_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : V;
+
+    // R-SWA ring write: this wave's share holds the row, nobody else reads it.
+    if (has_w && lane < 32) {
+        *(float4*)(a.k_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(kn + 4 * lane);
+        *(float4*)(a.v_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(vn + 4 * lane);
+    }
+
+    float4 qv[HPK];
+#pragma unroll
+    for (int h = 0; h < HPK; ++h) {
+        const float4 t = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 4 * seg);
+        qv[h] = make_float4(t.x * kQScale, t.y * kQScale, t.z * kQScale, t.w * kQScale);
+    }
+    float l[HPK];
+#pragma unroll
+    for (int h = 0; h < HPK; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+        acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // kF32Tiles 16-row tiles per step: all their loads leave before the
+    // step's arithmetic (rows clamped into the piece; a tile that starts
+    // past the piece's end is loaded but not computed)
+    constexpr int kF32Tiles = 2;
+    for (int r = it.row0; r < it.row1; r += kF32Tiles * kTileRows) {
+        float4 kx[8 * kF32Tiles], vx[8 * kF32Tiles];
+#pragma unroll
+        for (int i = 0; i < 8 * kF32Tiles; ++i) {
+            const int row = min(r + 2 * i + half, it.row1 - 1);
+            const bool wr = has_w && row == wrow;
+            kx[i] = ld_stream((wr ? kn : K + (size_t)row * kHD) + 4 * seg);
+            vx[i] = ld_stream((wr ? vn : V + (size_t)row * kHD) + 4 * seg);
+        }
+#pragma unroll
+        for (int tt = 0; tt < kF32Tiles; ++tt) {
+            const int rt = r + tt * kTileRows;
+            if (tt > 0 && rt >= it.row1) break;
+            const int myrow = rt + 2 * (seg >> 2) + half;
+#pragma unroll
+            for (int h = 0; h < HPK; ++h) {
+                float part[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 kt = kx[8 * tt + i];
+                    float d = qv[h].x * kt.x;
+                    d = fmaf(qv[h].y, kt.y, d);
+                    d = fmaf(qv[h].z, kt.z, d);
+                    d = fmaf(qv[h].w, kt.w, d);
+                    part[i] = d;
+                }
+                float sc = reduce8_over32(part, seg);
+                if (kCap) sc = (float)soft_cap((double)sc, a.softcap2, inv_c2);
+                if (myrow >= it.row1) sc = -INFINITY;
+                const float mnew = fmaxf(m[h], wave_max(sc));
+                const float alpha = fast_exp2(m[h] - mnew);
+                const float p = fast_exp2(sc - mnew);
+                l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
+                float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float pi = __shfl(p, half * 32 + 4 * i, 64);
+                    const float4 vt = vx[8 * tt + i];
+                    ac.x = fmaf(pi, vt.x, ac.x);
+                    ac.y = fmaf(pi, vt.y, ac.y);
+                    ac.z = fmaf(pi, vt.z, ac.z);
+                    ac.w = fmaf(pi, vt.w, ac.w);
+                }
+                acc[h] = ac;
+                m[h] = mnew;
+            }
+        }
+    }
+    // sum the two row halves' accumulators, and the sums over the wave
+#pragma unroll
+    for (int h = 0; h < HPK; ++h) {
+        lsum[h] = wave_sum(l[h]);
+        acc[h].x += __shfl_xor(acc[h].x, 32, 64);
+        acc[h].y += __shfl_xor(acc[h].y, 32, 64);
+        acc[h].z += __shfl_xor(acc[h].z, 32, 64);
+        acc[h].w += __shfl_xor(acc[h].w, 32, 64);
+    }
+}
+
 // One wave per SIMD streams the f32 rows (the launch gives one share per
 // SIMD); the occupancy hint lets the scheduler keep more of a step's loads
 // in flight.  Measured on the 32k R-SWA step: two tiles per step with the
@@ -250,104 +351,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int lane = threadIdx.x & 63;
-    const int half = lane >> 5, seg = lane & 31;
-    const double inv_c2 = kCap ? 1.0 / a.softcap2 : 0.0;
     for_each_piece(a, w, [&](const Piece& it) {
-        const float* K = a.k + it.hrow * kHD;
-        const float* V = a.v + it.hrow * kHD;
-        const int wrow = a.wrow[it.j];
-        const bool has_w = wrow >= it.row0 && wrow < it.row1;
-        const float* kn = has_w ? a.k_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : K;
-        const float* vn = has_w ? a.v_new + ((size_t)it.b * a.n_kv_heads + it.g) * kHD : V;
-
-        // R-SWA ring write: this wave's share holds the row, nobody else reads it.
-        if (has_w && lane < 32) {
-            *(float4*)(a.k_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(kn + 4 * lane);
-            *(float4*)(a.v_store + (it.hrow + wrow) * kHD + 4 * lane) = *(const float4*)(vn + 4 * lane);
-        }
-
-        float4 qv[HPK];
-#pragma unroll
-        for (int h = 0; h < HPK; ++h) {
-            const float4 t = *(const float4*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 4 * seg);
-            qv[h] = make_float4(t.x * kQScale, t.y * kQScale, t.z * kQScale, t.w * kQScale);
-        }
         float m[HPK], l[HPK];
         float4 acc[HPK];
+        f32_piece<HPK, kCap>(a, it, m, l, acc);
+        // the piece's partial: (max, sum) and the accumulators
 #pragma unroll
         for (int h = 0; h < HPK; ++h) {
-            m[h] = -INFINITY;
-            l[h] = 0.0f;
-            acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-
-        // kF32Tiles 16-row tiles per step: all their loads leave before the
-        // step's arithmetic (rows clamped into the piece; a tile that starts
-        // past the piece's end is loaded but not computed)
-        constexpr int kF32Tiles = 2;
-        for (int r = it.row0; r < it.row1; r += kF32Tiles * kTileRows) {
-            float4 kx[8 * kF32Tiles], vx[8 * kF32Tiles];
-#pragma unroll
-            for (int i = 0; i < 8 * kF32Tiles; ++i) {
-                const int row = min(r + 2 * i + half, it.row1 - 1);
-                const bool wr = has_w && row == wrow;
-                kx[i] = ld_stream((wr ? kn : K + (size_t)row * kHD) + 4 * seg);
-                vx[i] = ld_stream((wr ? vn : V + (size_t)row * kHD) + 4 * seg);
-            }
-#pragma unroll
-            for (int tt = 0; tt < kF32Tiles; ++tt) {
-                const int rt = r + tt * kTileRows;
-                if (tt > 0 && rt >= it.row1) break;
-                const int myrow = rt + 2 * (seg >> 2) + half;
-#pragma unroll
-                for (int h = 0; h < HPK; ++h) {
-                    float part[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float4 kt = kx[8 * tt + i];
-                        float d = qv[h].x * kt.x;
-                        d = fmaf(qv[h].y, kt.y, d);
-                        d = fmaf(qv[h].z, kt.z, d);
-                        d = fmaf(qv[h].w, kt.w, d);
-                        part[i] = d;
-                    }
-                    float sc = reduce8_over32(part, seg);
-                    if (kCap) sc = (float)soft_cap((double)sc, a.softcap2, inv_c2);
-                    if (myrow >= it.row1) sc = -INFINITY;
-                    const float mnew = fmaxf(m[h], wave_max(sc));
-                    const float alpha = fast_exp2(m[h] - mnew);
-                    const float p = fast_exp2(sc - mnew);
-                    l[h] = l[h] * alpha + ((seg & 3) == 0 ? p : 0.0f);
-                    float4 ac = make_float4(acc[h].x * alpha, acc[h].y * alpha, acc[h].z * alpha, acc[h].w * alpha);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float pi = __shfl(p, half * 32 + 4 * i, 64);
-                        const float4 vt = vx[8 * tt + i];
-                        ac.x = fmaf(pi, vt.x, ac.x);
-                        ac.y = fmaf(pi, vt.y, ac.y);
-                        ac.z = fmaf(pi, vt.z, ac.z);
-                        ac.w = fmaf(pi, vt.w, ac.w);
-                    }
-                    acc[h] = ac;
-                    m[h] = mnew;
-                }
-            }
-        }
-
-        // the piece's partial: (max, sum) and the two row halves' accumulators
-#pragma unroll
-        for (int h = 0; h < HPK; ++h) {
-            const float lt = wave_sum(l[h]);
-            float4 at = acc[h];
-            at.x += __shfl_xor(at.x, 32, 64);
-            at.y += __shfl_xor(at.y, 32, 64);
-            at.z += __shfl_xor(at.z, 32, 64);
-            at.w += __shfl_xor(at.w, 32, 64);
             const size_t ix = (size_t)it.slot * HPK + h;
-            if (half == 0) *(float4*)(a.ws_acc + ix * kHD + 4 * seg) = at;
+            if (lane < 32) *(float4*)(a.ws_acc + ix * kHD + 4 * lane) = acc[h];
             if (lane == 0) {
                 a.ws_ml[ix * 2] = m[h];
-                a.ws_ml[ix * 2 + 1] = lt;
+                a.ws_ml[ix * 2 + 1] = l[h];
             }
         }
     });
