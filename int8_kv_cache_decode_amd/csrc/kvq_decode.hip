@@ -484,8 +484,15 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 template <int HPK, bool kCap, bool kI8>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
+    // The value pass runs on the matrix cores for groups of 4 or 8 heads, on
+    // the VALU for 1 or 2 (there the MFMA's 16 columns would hold 3 or 6
+    // and the register cost lowers occupancy: the R-SWA step on the int8
+    // mirror, group 1, 22.4 us on the VALU against 25.6 us).
+    constexpr bool kPvMfma = HPK >= 4;
     // per wave, two tiles: the bf16 parts of weight * vs, [head][part][row % 4][row / 4]
-    __shared__ __attribute__((aligned(8))) uint16_t sm_wb[kWaves][2][4 * NB][3][4][4];
+    __shared__ __attribute__((aligned(8))) uint16_t sm_wb[kPvMfma ? kWaves : 1][2][kPvMfma ? 4 * NB : 1][3][4][4];
+    // per wave, two tiles: weight * vs per [row][head] (VALU value pass)
+    __shared__ float sm_pw[kPvMfma ? 1 : kWaves][2][16][kPvMfma ? 1 : HPK];
     __shared__ float sm_alpha[kWaves][2][HPK];        // per wave, two tiles: rescale factor per head
     __shared__ double sm_v64[kWaves][HPK][kHD];       // per wave: flushed V accumulators
     // i8 kind, R-SWA: the ring row's fresh K / V codes and their scales
@@ -701,20 +708,54 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         };
 #pragma unroll
         for (int i = 0; i < kOwn; ++i) cell(i) = 0.0;
+        // VALU value pass: per-lane f32 accumulators, head h channels kVDim seg ..
+        float acc[kPvMfma ? 1 : HPK][kVDim];
+#pragma unroll
+        for (int h = 0; h < (kPvMfma ? 1 : HPK); ++h)
+#pragma unroll
+            for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
         // Value pass on v_mfma_f32_16x16x32_bf16, one per 8-channel block cb
         // (channels 8 m + cb, m = lane % 16) and block of 4 heads: A = the V
         // codes of the lane's four rows ri + 4 i (exact in bf16; K slots 4..7
         // zero), B = the weights times the rows' V scales in three exact bf16
         // parts, column n = 4 part + head.  Lane l accumulates, for its column
         // (part, head) = (l % 16 / 4, l % 4), channels 8 (4 (l / 16) + i) + cb.
-        v4f accv[NB][8];
+        v4f accv[kPvMfma ? NB : 1][8];
 #pragma unroll
-        for (int hb = 0; hb < NB; ++hb)
+        for (int hb = 0; hb < (kPvMfma ? NB : 1); ++hb)
 #pragma unroll
             for (int cb = 0; cb < 8; ++cb) accv[hb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
         const int bpart = (lane & 15) >> 2, bhead = lane & 3;
-        // The three parts summed onto the part-0 lanes (DPP), added into f64.
+        // The three parts summed onto the part-0 lanes (DPP), added into f64;
+        // on the VALU path acc summed over the four row groups (a transposing
+        // butterfly leaves lane ri with entries [kOwn ri, kOwn ri + kOwn)),
+        // added into f64.  Both clear their accumulators.
         auto flush = [&]() {
+            if constexpr (!kPvMfma) {
+                constexpr int N = HPK * kVDim;
+                float y[N / 2], z[kOwn];
+#pragma unroll
+                for (int i = 0; i < N / 2; ++i) {
+                    // lanes 0..31 keep entry i, lanes 32..63 entry i + N / 2
+                    float lo = acc[i / kVDim][i % kVDim], hi = acc[(i + N / 2) / kVDim][(i + N / 2) % kVDim];
+                    swap32(lo, hi);
+                    y[i] = lo + hi;
+                }
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    // rows with lane bit 4 clear keep y[i], the others y[i + kOwn]
+                    float lo = y[i], hi = y[i + kOwn];
+                    swap16(lo, hi);
+                    z[i] = lo + hi;
+                }
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) cell(i) += (double)z[i];
+#pragma unroll
+                for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                    for (int c = 0; c < kVDim; ++c) acc[h][c] = 0.0f;
+                return;
+            }
 #pragma unroll
             for (int hb = 0; hb < NB; ++hb) {
                 const int h = 4 * hb + bhead;
@@ -799,17 +840,46 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
                 l[hb] = fma(l[hb], (double)alpha, (double)p);
                 m[hb] = mnew;
                 if (h < HPK) {
-                    uint32_t ph, pm, pl;
-                    bf16_split3(p * t.vsn, ph, pm, pl);
-                    sm_wb[wave][buf][h][0][n & 3][n >> 2] = (uint16_t)ph;
-                    sm_wb[wave][buf][h][1][n & 3][n >> 2] = (uint16_t)pm;
-                    sm_wb[wave][buf][h][2][n & 3][n >> 2] = (uint16_t)pl;
+                    if constexpr (kPvMfma) {
+                        uint32_t ph, pm, pl;
+                        bf16_split3(p * t.vsn, ph, pm, pl);
+                        sm_wb[wave][buf][h][0][n & 3][n >> 2] = (uint16_t)ph;
+                        sm_wb[wave][buf][h][1][n & 3][n >> 2] = (uint16_t)pm;
+                        sm_wb[wave][buf][h][2][n & 3][n >> 2] = (uint16_t)pl;
+                    } else {
+                        sm_pw[wave][buf][n][h] = p * t.vsn;
+                    }
                     if (n == 0) sm_alpha[wave][buf][h] = alpha;
                 }
             }
             wave_lds_sync();
 
             // ---- V accumulation in the (row, channel) layout ----
+            if constexpr (!kPvMfma) {
+                if (rescale) {
+#pragma unroll
+                    for (int h = 0; h < HPK; ++h) {
+                        const float al = sm_alpha[wave][buf][h];
+#pragma unroll
+                        for (int c = 0; c < kVDim; ++c) acc[h][c] *= al;
+                    }
+#pragma unroll
+                    for (int i = 0; i < kOwn; ++i) cell(i) *= (double)sm_alpha[wave][buf][(kOwn * ri + i) / kVDim];
+                }
+                // f32 FMA chains of 4 rows per tile between two f64 flushes
+#pragma unroll
+                for (int i = 0; i < kVLoads; ++i) {
+                    float wv[HPK];
+#pragma unroll
+                    for (int h = 0; h < HPK; ++h) wv[h] = sm_pw[wave][buf][ri + kVRows * i][h];
+                    float vf[kVDim];
+                    unpack(t.vx[i], vf);
+#pragma unroll
+                    for (int h = 0; h < HPK; ++h)
+#pragma unroll
+                        for (int c = 0; c < kVDim; ++c) acc[h][c] = fmaf(wv[h], vf[c], acc[h][c]);
+                }
+            } else {
             if (rescale) {
 #pragma unroll
                 for (int hb = 0; hb < NB; ++hb) {
@@ -842,6 +912,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #pragma unroll
                 for (int hb = 0; hb < NB; ++hb)
                     accv[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[hb], accv[hb][cb], 0, 0, 0);
+            }
             }
             buf ^= 1;
             if (++since_flush == KVQ_Q8_FLUSH) {
