@@ -481,14 +481,15 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #ifndef KVQ_Q8_MIN_WAVES
 #define KVQ_Q8_MIN_WAVES 3
 #endif
-template <int HPK, bool kCap, bool kI8>
+template <int HPK, bool kCap, bool kI8, bool kMf>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
-    // The value pass runs on the matrix cores for groups of 4 or 8 heads, on
-    // the VALU for 1 or 2 (there the MFMA's 16 columns would hold 3 or 6
-    // and the register cost lowers occupancy: the R-SWA step on the int8
-    // mirror, group 1, 22.4 us on the VALU against 25.6 us).
-    constexpr bool kPvMfma = HPK >= 4;
+    // The value pass runs on the matrix cores (kMf) for groups of 4 or 8
+    // heads, on the VALU for 1 or 2 (there the MFMA's 16 columns would hold 3
+    // or 6 and the register cost lowers occupancy: the R-SWA step on the int8
+    // mirror, group 1, 22.4 us on the VALU against 25.6 us).  The launcher
+    // takes the VALU instance for short launches too.
+    constexpr bool kPvMfma = kMf && HPK >= 4;
     // per wave, two tiles: the bf16 parts of weight * vs, [head][part][row % 4][row / 4]
     __shared__ __attribute__((aligned(8))) uint16_t sm_wb[kPvMfma ? kWaves : 1][2][kPvMfma ? 4 * NB : 1][3][4][4];
     // per wave, two tiles: weight * vs per [row][head] (VALU value pass)
@@ -1694,7 +1695,7 @@ int combine_threads(const DecodeArgs& a, int lpg) {
 constexpr int kMaxDevices = 64;
 int resident_waves(const void* kernel, int which) {
     // host threads may race to fill an entry; they all store the same value
-    static std::atomic<int> cache[kMaxDevices][28];
+    static std::atomic<int> cache[kMaxDevices][52];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
     std::atomic<int>& c = cache[dev][which];
@@ -1732,11 +1733,19 @@ int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; 
 // Cache kinds of the decode launcher.
 constexpr int kF32 = 0, kQ8k = 1, kI8k = 2;
 
-// The kernel instance for a group size, cache kind and soft-cap switch.
+// The kernel instance for a group size, cache kind, soft-cap switch and
+// value pass (mf: on the matrix cores; groups of 1 or 2 heads have only the
+// VALU one).
+template <int HPK, bool kCap, bool kI8>
+const void* q8_kernel(bool mf) {
+    if constexpr (HPK >= 4)
+        return mf ? (const void*)k_decode_q8<HPK, kCap, kI8, true> : (const void*)k_decode_q8<HPK, kCap, kI8, false>;
+    return (const void*)k_decode_q8<HPK, kCap, kI8, false>;
+}
 template <int HPK, int kKind>
-const void* decode_kernel(bool cap) {
-    if (kKind == kI8k) return (const void*)k_decode_q8<HPK, false, true>;
-    if (kKind == kQ8k) return cap ? (const void*)k_decode_q8<HPK, true, false> : (const void*)k_decode_q8<HPK, false, false>;
+const void* decode_kernel(bool cap, bool mf) {
+    if (kKind == kI8k) return q8_kernel<HPK, false, true>(mf);
+    if (kKind == kQ8k) return cap ? q8_kernel<HPK, true, false>(mf) : q8_kernel<HPK, false, false>(mf);
     return cap ? (const void*)k_decode_f32<HPK, true> : (const void*)k_decode_f32<HPK, false>;
 }
 
@@ -1757,6 +1766,16 @@ const void* decode_kernel(bool cap) {
 // kernel in the dependent shuffles of their tiles, and more waves overlap them.
 
 constexpr int kQ8MinTilesPerWave = 4;
+// The q8 / int8 value pass goes to the matrix cores only when a launch has
+// at least this many tiles per resident wave; below that the VALU instance
+// runs.  Measured on MI355X, 32 Q / 8 KV heads, q8 (matrix cores against
+// VALU): one 8192-row sequence 15.8 / 14.8 us, one of 131072 rows (11 tiles
+// per wave) 60.0 / 58.6, 4 x 32768 rows (21 per wave) 59.5 / 57.7, 8 x 32768
+// (43 per wave) 100.1 / 100.1, the 64-sequence batch of 1024..32768 rows
+// (167 per wave) 363.7 / 366.3; int8 alike.
+#ifndef KVQ_Q8_PV_MIN_TILES
+#define KVQ_Q8_PV_MIN_TILES 48
+#endif
 
 template <int kKind>
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
@@ -1766,14 +1785,23 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
     if (a.n_tiles > 0) {
         const bool cap = a.softcap2 > 0.0;
         const void* fn = nullptr;
-        switch (a.hpk) {
-            case 1: fn = decode_kernel<1, kKind>(cap); break;
-            case 2: fn = decode_kernel<2, kKind>(cap); break;
-            case 4: fn = decode_kernel<4, kKind>(cap); break;
-            case 8: fn = decode_kernel<8, kKind>(cap); break;
-            default: return hipErrorInvalidValue;
+        auto pick = [&](bool mf) -> const void* {
+            switch (a.hpk) {
+                case 1: return decode_kernel<1, kKind>(cap, mf);
+                case 2: return decode_kernel<2, kKind>(cap, mf);
+                case 4: return decode_kernel<4, kKind>(cap, mf);
+                case 8: return decode_kernel<8, kKind>(cap, mf);
+                default: return nullptr;
+            }
+        };
+        const int which = 8 * kKind + 4 * cap + hpk_index(a.hpk);
+        fn = pick(true);
+        if (fn == nullptr) return hipErrorInvalidValue;
+        int shares = kQ8 ? resident_waves(fn, which) : simd_count();
+        if (kQ8 && a.hpk >= 4 && shares > 0 && (int64_t)a.n_tiles < (int64_t)KVQ_Q8_PV_MIN_TILES * shares) {
+            fn = pick(false);
+            shares = resident_waves(fn, which + 28);   // entries 28.. (24..27: verify)
         }
-        int shares = kQ8 ? resident_waves(fn, 8 * kKind + 4 * cap + hpk_index(a.hpk)) : simd_count();
         if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = simd_count();
         // f32, short launch: one tile per wave (gqa 4096 rows x 6 heads: 16.8 -> 15.2 us per call)
         if (!kQ8 && shares > 0 && a.n_tiles < 2 * shares) shares = a.n_tiles;

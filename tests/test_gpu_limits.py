@@ -48,19 +48,16 @@ def units_for(kind, k, v, alive, cap):
     return out
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
-def test_sequence_at_max_capacity(kind):
-    """2^24 rows in one (sequence, head): 64 random rows, zero rows, then a
-    4096-row random window at the top of the row range.  A zero row scores 0
-    and carries a zero value, so the full decode equals the oracle's decode
-    of the 64 + 4096 random rows with a value-less logit ln(#zero rows) per
-    Q head; the windowed decode (first = 2^24 - 4096) sees the top rows only.
-    The top rows' storage is compared bit for bit."""
-    cap, hkv, hpk, W, H0 = K.MAX_CAPACITY, 2, 4, 4096, 64
-    say("case: max capacity kind", kind, "rows", cap)
-    r = rng(900 + kind)
-    alive = np.array([0, 1], np.uint8)
+def zero_filled_case(kind, cap, alive, hpk, seed, check_window=True):
+    """One sequence of cap rows: 64 random rows, zero rows, then a 4096-row
+    random window at the top of the row range.  A zero row scores 0 and
+    carries a zero value, so the full decode equals the oracle's decode of
+    the 64 + 4096 random rows with a value-less logit ln(#zero rows) per Q
+    head; the windowed decode (first = cap - 4096) sees the top rows only.
+    The top rows' storage of the last live head is compared bit for bit."""
+    W, H0 = 4096, 64
+    hkv = len(alive)
+    r = rng(seed)
     c = K.KvCache(kind, 1, hkv, cap, alive=alive)
     head_k, head_v = r.standard_normal((2, H0, hkv, 128)).astype(np.float32)
     win_k = (r.standard_normal((W, hkv, 128)) * 2).astype(np.float32)
@@ -81,20 +78,22 @@ def test_sequence_at_max_capacity(kind):
     assert int(c.len[0]) == cap
     rows_k, rows_v = np.concatenate([head_k, win_k]), np.concatenate([head_v, win_v])
     units = [units_for(kind, rows_k, rows_v, alive, H0 + W)]
-    u = units[0][1]
+    g = int(np.flatnonzero(alive)[-1])
+    sl = int(alive[:g].sum())                      # its live slot
+    u = units[0][g]
     top = slice(cap - W, cap)
     if kind == K.KIND_F32:
-        assert np.array_equal(host(c.view("k")[0, 0, top]), win_k[:, 1])
-        assert np.array_equal(host(c.view("v")[0, 0, top]), win_v[:, 1])
+        assert np.array_equal(host(c.view("k")[0, sl, top]), win_k[:, g])
+        assert np.array_equal(host(c.view("v")[0, sl, top]), win_v[:, g])
     else:
         h = u[1]
         for nm, want in (("kq", h.kq), ("ks", h.ks), ("vq", h.vq), ("vs", h.vs)):
-            got = host(c.view(nm)[0, 0, top])
+            got = host(c.view(nm)[0, sl, top])
             assert np.array_equal(got.view(np.uint8), np.ascontiguousarray(want[H0:H0 + W]).view(np.uint8)), nm
         if kind == K.KIND_Q8:
             assert int(c.frozen[0]) == 1
-            assert np.array_equal(host(c.view("kcol")[0, 0]).view(np.uint32), h.kcol.view(np.uint32))
-            assert np.array_equal(host(c.view("vcol")[0, 0]).view(np.uint32), h.vcol.view(np.uint32))
+            assert np.array_equal(host(c.view("kcol")[0, sl]).view(np.uint32), h.kcol.view(np.uint32))
+            assert np.array_equal(host(c.view("vcol")[0, sl]).view(np.uint32), h.vcol.view(np.uint32))
     hq = hkv * hpk
     q = (r.standard_normal((1, hq, 128)) * 2).astype(np.float32)
     out = torch.full((1, hq, 128), np.nan, device="cuda")
@@ -105,8 +104,9 @@ def test_sequence_at_max_capacity(kind):
     err = max_err(got, ref)
     say("  full context max err %.3g (|out| up to %.2f)" % (err, np.abs(ref).max()))
     assert err <= F32_TOL, err
-    assert not got[0, :hpk].any()
-    if kind != K.KIND_I8:
+    for gd in np.flatnonzero(alive == 0):
+        assert not got[0, gd * hpk:(gd + 1) * hpk].any()
+    if kind != K.KIND_I8 and check_window:
         ex = K.decode_attn_f32_ex if kind == K.KIND_F32 else K.decode_attn_q8_ex
         out2 = torch.full((1, hq, 128), np.nan, device="cuda")
         ex(c, hq, dev(q), out2, K.DecodeOpts(first=np.array([cap - W], np.int32)))
@@ -115,6 +115,27 @@ def test_sequence_at_max_capacity(kind):
         err2 = max_err(host(out2), ref2)
         say("  top-window max err %.3g" % err2)
         assert err2 <= F32_TOL, err2
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
+def test_sequence_at_max_capacity(kind):
+    """2^24 rows in one (sequence, head), the largest row offset the kernels
+    address, built as in zero_filled_case (one dead and one live KV head, 4 Q
+    heads each)."""
+    say("case: max capacity kind", kind, "rows", K.MAX_CAPACITY)
+    zero_filled_case(kind, K.MAX_CAPACITY, np.array([0, 1], np.uint8), 4, 900 + kind)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind", [K.KIND_Q8, K.KIND_I8])
+def test_group_of_8_long_launch(kind):
+    """Groups of 8 Q heads over 4 KV heads x 2^20 rows (262144 16-row tiles,
+    more than 48 per resident wave, so the value pass runs on the matrix
+    cores; shorter launches, as in the other group-of-8 tests, run it on the
+    VALU), built as in zero_filled_case."""
+    say("case: group of 8, long launch, kind", kind)
+    zero_filled_case(kind, 1 << 20, np.ones(4, np.uint8), 8, 950 + kind)
 
 
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_Q8, K.KIND_I8])
