@@ -40,7 +40,7 @@ __device__ __forceinline__ float group_max(float x) {
 // f32 append: copy one row of one live head.  block 64, each lane 2 channels.
 __global__ __launch_bounds__(64) void k_append_f32(const AppendArgs a) {
     const int r = blockIdx.x, j = blockIdx.y, gl = blockIdx.z;
-    const int g = a.live_head[gl];
+    const int g = arg_byte(a.live_head, gl);
     const int lane = threadIdx.x;
     const size_t src = ((size_t)(a.src_row0[j] + r) * a.n_kv_heads + g) * kHD + 2 * lane;
     const size_t dst = (((size_t)a.seq[j] * a.n_live + gl) * a.capacity + a.dst_row0[j] + r) * kHD
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64) void k_append_f32(const AppendArgs a) {
 // 16 lanes per group), wave 1 the V row (one group of 128).
 __global__ __launch_bounds__(128) void k_append_q8(const AppendArgs a) {
     const int r = blockIdx.x, j = blockIdx.y, gl = blockIdx.z;
-    const int g = a.live_head[gl];
+    const int g = arg_byte(a.live_head, gl);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bool is_k = (wave == 0);
     const size_t src = ((size_t)(a.src_row0[j] + r) * a.n_kv_heads + g) * kHD + 2 * lane;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(128) void k_append_q8(const AppendArgs a) {
 // (1 for a zero row), code = clamp(round_ties_even(x / scale), -127, 127).
 __global__ __launch_bounds__(128) void k_append_i8(const AppendArgs a) {
     const int r = blockIdx.x, j = blockIdx.y, gl = blockIdx.z;
-    const int g = a.live_head[gl];
+    const int g = arg_byte(a.live_head, gl);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bool is_k = (wave == 0);
     const size_t src = ((size_t)(a.src_row0[j] + r) * a.n_kv_heads + g) * kHD + 2 * lane;

@@ -162,7 +162,7 @@ __device__ __forceinline__ void for_each_piece(const Args& a, int w, F&& f) {
         p.j = j;
         p.gl = gl;
         p.b = a.seq0 + j;
-        p.g = a.live_head[gl];
+        p.g = arg_byte(a.live_head, gl);
         p.row0 = seg_first(a, j) + kTileRows * (t - sb);
         p.row1 = min(seg_first(a, j) + kTileRows * (pe - sb), a.len[j]);
         p.lo = seg_lo(a, j);
@@ -424,9 +424,12 @@ __device__ __forceinline__ void bf16_split3(float w, uint32_t& hi, uint32_t& mid
     mid = m >> 16;
     lo = __float_as_uint(r2) >> 16;
 }
-// Two bf16 values (the top halves of two f32 that are exact in bf16) in one dword.
+// Two f32 values that are exact in bf16 (small integers), packed as bf16 in one dword.
 __device__ __forceinline__ uint32_t bf16_pack(float a, float b) {
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf2));
 }
 
 // V layout of the q8 kernel: lane (ri = lane / 16, seg = lane % 16) owns
@@ -475,6 +478,18 @@ __device__ __forceinline__ int take_digit(int& x) {
     return d;
 }
 
+// rint(x / s) with the quotient correctly rounded, as quantize_row_i8 takes
+// it ([P3]), for |x / s| <= 128, from y = x * inv (inv = 1 / s correctly
+// rounded): y is then within 2^-15 of the rounded quotient, so both round to
+// the same integer unless y lies within 2^-14 of a half-integer; there (and
+// for a NaN or infinite y) the quotient itself is formed.
+__device__ __forceinline__ float rint_div(float x, float s, float inv) {
+    const float y = x * inv;
+    const float f = y - floorf(y);
+    if (!(fabsf(f - 0.5f) >= 6.103515625e-05f)) return rintf(__fdiv_rn(x, s));
+    return rintf(y);
+}
+
 // Orders this wave's LDS writes before its following LDS reads.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
         const float* KS = a.ks + it.hrow * (kI8 ? 1 : kKScales);
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
-        const bool frz = !kI8 && a.frozen[it.j] != 0;
+        const bool frz = !kI8 && arg_byte(a.frozen, it.j) != 0;
         const float* kcol = a.kcol + ((size_t)it.b * a.n_live + it.gl) * kHD;
 
         // [P3] write_decode_step on the int8 mirror: the wave whose piece holds
@@ -1096,7 +1111,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     const int j = blockIdx.y, tid = threadIdx.x;
     const int b = a.seq0 + j;
     const int g = h / a.hpk, hh = h - g * a.hpk;
-    const int gl = a.live_slot[g];
+    const int gl = arg_byte(a.live_slot, g);
     float* o = a.out + ((size_t)b * a.n_q_heads + h) * kHD + ch0;
     const int nt = a.ntile[j];
     if (gl < 0 || nt == 0) {
@@ -1113,7 +1128,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     if (!combine_partials(a.ws_ml + (it0 * a.hpk + hh) * 2, a.ws_acc + (it0 * a.hpk + hh) * kHD,
                           (size_t)a.hpk * 2, (size_t)a.hpk * kHD, nch, zs, lpg, ch0, &rr))
         return;
-    if (kQ8 && a.frozen[j]) {
+    if (kQ8 && arg_byte(a.frozen, j)) {
         const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + ch0 + 4 * tid);
         rr.x *= vc.x;
         rr.y *= vc.y;
@@ -1362,8 +1377,15 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
 #ifndef KVQ_VI8_FAST_SHARED
 #define KVQ_VI8_FAST_SHARED 1
 #endif
+// Tiles a wave keeps in flight (registers) while it computes: one share per
+// SIMD, so a wave has the SIMD's registers to itself and its loads, not its
+// occupancy, hide the memory latency.
+#ifndef KVQ_VI8_DEPTH
+#define KVQ_VI8_DEPTH 4
+#endif
 template <bool kShared>
 __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
+    constexpr int D = KVQ_VI8_DEPTH;
     // trailing rows of the piece: K / V codes and scales
     __shared__ __attribute__((aligned(16))) int8_t sm_tq[kWaves][2][kVerifyMaxQ][kHD];
     __shared__ float sm_ts[kWaves][2][kVerifyMaxQ];
@@ -1373,6 +1395,21 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
     const int lane = threadIdx.x & 63;
     const int qi = lane & 15, kb = lane >> 4;
     for_each_piece(a, w, [&](const Piece& it) {
+        if (it.row0 >= it.row1) {
+            // only padding tiles past the segment's rows (see launch_verify_i8):
+            // an empty partial
+            if (qi < a.nq) {
+                const size_t ix = (size_t)it.slot * a.nq + qi;
+                if (kb == 0) {
+                    a.ws_ml[ix * 2] = -INFINITY;
+                    a.ws_ml[ix * 2 + 1] = 0.0f;
+                }
+                float* dst = a.ws_acc + ix * kHD + 32 * kb;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) *(float4*)(dst + 4 * r) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            return;
+        }
         const int j = it.j;
         const int pre = a.prefill[j];
         const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft : pre + a.ring_len[j];   // cache rows
@@ -1381,6 +1418,21 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         const float* KS = a.ks + it.hrow;
         const int8_t* VQ = a.vq + it.hrow * kHD;
         const float* VS = a.vs + it.hrow;
+
+        // this lane's query (B column): draft / stream di, head hh of the
+        // group; its loads go out first, ahead of the trailing rows' and the
+        // tiles', so that its quantisation waits for it alone
+        const bool qvalid = qi < a.nq;
+        const int di = qvalid ? qi / a.hpk : 0, hh = qvalid ? qi - di * a.hpk : 0;
+        float4 qv[2][4];
+        {
+            const float* qp = a.q + ((ob * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 16 * kb;
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4)
+                    qv[sp][t4] = qvalid ? *(const float4*)(qp + 64 * sp + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 
         // ---- trailing rows [t0, t1) of this piece, quantised into LDS ----
         // Lane l takes row t0 + l / 4 and the 32 channels 32 (l % 4) .. of its
@@ -1413,12 +1465,15 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             av = fmaxf(av, __shfl_xor(av, 2, 64));
             const float sk = ak > 0.0f ? __fdiv_rn(ak, 127.0f) : 1.0f;
             const float sv = av > 0.0f ? __fdiv_rn(av, 127.0f) : 1.0f;
-            auto code = [](float x, float sc) { return (int)fminf(fmaxf(rintf(__fdiv_rn(x, sc)), -127.0f), 127.0f) & 0xff; };
+            const float ik = __fdiv_rn(1.0f, sk), iv = __fdiv_rn(1.0f, sv);
+            auto code = [](float x, float sc, float inv) { return (int)fminf(fmaxf(rint_div(x, sc, inv), -127.0f), 127.0f) & 0xff; };
             uint32_t ck[8], cv[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                ck[u] = code(xk[u].x, sk) | (code(xk[u].y, sk) << 8) | (code(xk[u].z, sk) << 16) | (code(xk[u].w, sk) << 24);
-                cv[u] = code(xv[u].x, sv) | (code(xv[u].y, sv) << 8) | (code(xv[u].z, sv) << 16) | (code(xv[u].w, sv) << 24);
+                ck[u] = code(xk[u].x, sk, ik) | (code(xk[u].y, sk, ik) << 8) | (code(xk[u].z, sk, ik) << 16) |
+                        (code(xk[u].w, sk, ik) << 24);
+                cv[u] = code(xv[u].x, sv, iv) | (code(xv[u].y, sv, iv) << 8) | (code(xv[u].z, sv, iv) << 16) |
+                        (code(xv[u].w, sv, iv) << 24);
             }
             if (tlane) {
 #pragma unroll
@@ -1492,31 +1547,72 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
                 }
             }
         };
-        // the first tile's loads go out before the trailing rows' arithmetic
-        // and the query set-up, unless that tile reads trailing rows from LDS
-        // (a piece is never empty)
-        int r0 = it.row0;
-        Tile ta, tb;
-        const bool first_in_cache = min(r0 + kTileRows - 1, it.row1 - 1) < L;
-        if (first_in_cache) load_tile(r0, ta);
-        if (t1 > 0) quantise_trailing();
-        if (!first_in_cache) load_tile(r0, ta);
+        // a whole tile of cache rows (no per-row clamp or choice of source):
+        // the lane's four consecutive rows' scales in one (dword-aligned) load
+        // per buffer
+        auto load_whole = [&](int r0, Tile& t) {
+            const uint32_t pk = (uint32_t)(r0 + qi), p = (uint32_t)(r0 + 4 * kb);
+            t.kc[0] = ld_stream(KQ + kq_offset((int)pk, 16 * kb));
+            t.kc[1] = ld_stream(KQ + kq_offset((int)pk, 64 + 16 * kb));
+            const float4 k4 = *(const float4*)(KS + p);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ld_v(VQ + ((p + r) * kHD + 8 * qi), t.vc[r]);
+            const float4 v4 = *(const float4*)(VS + p);
+            t.ks[0] = k4.x, t.ks[1] = k4.y, t.ks[2] = k4.z, t.ks[3] = k4.w;
+            t.vs[0] = v4.x, t.vs[1] = v4.y, t.vs[2] = v4.z, t.vs[3] = v4.w;
+        };
+        // either loader, as the tile asks
+        auto load_any = [&](int r0, Tile& t) {
+            if (r0 + kTileRows <= min(L, it.row1))
+                load_whole(r0, t);
+            else
+                load_tile(r0, t);
+        };
+        // The first D tiles' loads go out before the trailing rows' arithmetic
+        // and the query set-up (a piece is never empty).  In the verify, when
+        // the piece starts with whole tiles of cache rows, D whole-tile loads
+        // (8 loads each) go out unconditionally (past the last whole tile:
+        // that one again), so the waits below count exactly the loads in
+        // flight, and stay within what the wave's counter tracks (63); the
+        // tiles they did not cover (partial, or reading trailing rows from
+        // LDS) load after the trailing rows are quantised.  (The shared
+        // decode keeps the conditional loads: with the unconditional ones its
+        // registers spill and its last wave per head slows down.)
+        const int ntl = (it.row1 - it.row0 + kTileRows - 1) / kTileRows;
+        const int nwhole = (min(L, it.row1) - it.row0) / kTileRows;
+        auto in_cache = [&](int r0) { return min(r0 + kTileRows - 1, it.row1 - 1) < L; };
+        Tile tl[D];
+        if (!kShared && nwhole > 0) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) load_whole(it.row0 + kTileRows * min(i, nwhole - 1), tl[i]);
+            if (t1 > 0) quantise_trailing();
+#pragma unroll
+            for (int i = 0; i < D; ++i)
+                if (i >= nwhole && i < ntl) load_tile(it.row0 + kTileRows * i, tl[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < D; ++i)
+                if (i < ntl && in_cache(it.row0 + kTileRows * i)) load_tile(it.row0 + kTileRows * i, tl[i]);
+            if (t1 > 0) {
+                quantise_trailing();
+#pragma unroll
+                for (int i = 0; i < D; ++i)
+                    if (i < ntl && !in_cache(it.row0 + kTileRows * i)) load_tile(it.row0 + kTileRows * i, tl[i]);
+            }
+        }
 
-        // this lane's query (B column): draft / stream di, head hh of the group,
-        // quantised with quantize_row_i8 in f32 (amax over the 4 lanes of qi)
-        const bool qvalid = qi < a.nq;
-        const int di = qvalid ? qi / a.hpk : 0, hh = qvalid ? qi - di * a.hpk : 0;
+        // the query quantised with quantize_row_i8 in f32 (amax over the 4
+        // lanes of qi)
         v4i qa[2];
         double qsc;
         {
-            const float* qp = a.q + ((ob * a.n_draft + di) * a.n_q_heads + it.g * a.hpk + hh) * kHD + 16 * kb;
             float x[2][16];
             float amax = 0.0f;
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) {
-                    const float4 v = qvalid ? *(const float4*)(qp + 64 * sp + 4 * t4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const float4 v = qv[sp][t4];
                     x[sp][4 * t4 + 0] = v.x;
                     x[sp][4 * t4 + 1] = v.y;
                     x[sp][4 * t4 + 2] = v.z;
@@ -1526,12 +1622,13 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
             const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
+            const float iq = __fdiv_rn(1.0f, qs);
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
                 v4i pk = {0, 0, 0, 0};
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    const int c = (int)fminf(fmaxf(rintf(__fdiv_rn(x[sp][t], qs)), -127.0f), 127.0f);
+                    const int c = (int)fminf(fmaxf(rint_div(x[sp][t], qs, iq), -127.0f), 127.0f);
                     pk[t >> 2] |= (c & 0xff) << (8 * (t & 3));
                 }
                 qa[sp] = pk;
@@ -1542,15 +1639,17 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
         const int evict = max(0, rl + di + 1 - KVQ_RING_WINDOW);
         const int live = kShared ? a.sring[di] : 0;                               // ring slots live before the step
         const int wslot = kShared ? a.swrow[di] - pre - KVQ_RING_WINDOW * di : 0;   // the slot it overwrites
+        // every condition evaluated and combined with & and | (no branches:
+        // the rows of a lane differ in which case applies)
         auto visible = [&](int p) {
-            if (p < pre) return true;
+            const int q = p - pre;
             if constexpr (kShared) {
-                if (p >= L) return p - L == di;
-                const int slot = (p - pre) & (KVQ_RING_WINDOW - 1);
-                return ((p - pre) >> 7) == di && slot < live && slot != wslot;
+                const int slot = q & (KVQ_RING_WINDOW - 1);
+                const bool ring = (q >= 0) & (p < L) & ((q >> 7) == di) & (slot < live) & (slot != wslot);
+                return (q < 0) | ring | ((p >= L) & (p - L == di));
             } else {
-                if (p < L) return ((p - pre - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict;
-                return p - L <= di;
+                const bool ring = (q >= 0) & (p < L) & (((q - old + KVQ_RING_WINDOW) & (KVQ_RING_WINDOW - 1)) >= evict);
+                return (q < 0) | ring | ((p >= L) & (p - L <= di));
             }
         };
 
@@ -1568,10 +1667,18 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
             double s64[4];
             float tmax = -INFINITY;
             bool vis[4];
+            if (r0 + kTileRows <= min(pre, it.row1)) {      // reference rows only: every query sees them
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vis[r] = qvalid;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = r0 + 4 * kb + r;
+                    vis[r] = qvalid & (p < it.row1) & visible(p);
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int p = r0 + 4 * kb + r;
-                vis[r] = qvalid && p < it.row1 && visible(p);
                 s64[r] = (double)d[r] * (qsc * (double)t.ks[r]);
                 if (vis[r]) tmax = fmaxf(tmax, (float)s64[r]);
             }
@@ -1615,15 +1722,29 @@ __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
                 acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b2, acc[cb], 0, 0, 0);
             }
         };
-        // ping-pong with one exit at the loop head (as in k_decode_q8)
-        while (r0 + kTileRows < it.row1) {
-            load_tile(r0 + kTileRows, tb);
-            compute_tile(r0, ta);
-            load_tile(r0 + 2 * kTileRows, ta);
-            compute_tile(r0 + kTileRows, tb);
-            r0 += 2 * kTileRows;
+        // D tiles in flight: slot i holds tile k + i.  The main loop runs full
+        // rounds (every slot refilled) while the tiles it loads are whole
+        // tiles of cache rows: one straight path whose loop exits only at its
+        // head, so that it waits for exactly the loads it uses.  The last
+        // tiles (partial, or reading trailing rows) take the general path.
+        int k = 0;
+        while (k + 2 * D <= nwhole) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                compute_tile(it.row0 + kTileRows * (k + i), tl[i]);
+                load_whole(it.row0 + kTileRows * (k + D + i), tl[i]);
+            }
+            k += D;
         }
-        if (r0 < it.row1) compute_tile(r0, ta);
+        while (k < ntl) {
+#pragma unroll
+            for (int i = 0; i < D; ++i)
+                if (k + i < ntl) {
+                    compute_tile(it.row0 + kTileRows * (k + i), tl[i]);
+                    if (k + D + i < ntl) load_any(it.row0 + kTileRows * (k + D + i), tl[i]);
+                }
+            k += D;
+        }
         // the piece's partial for each valid query: lane (qi, kb) holds
         // channels 8 (4 kb + r) + cb
         const float lt = sum_rows(l);
@@ -1652,7 +1773,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine_verify(const Verify
     const int i = x / a.n_q_heads, h = x - i * a.n_q_heads;
     const int b = a.shared ? 0 : a.seq0 + j;              // shared decode: out is [streams][n_q_heads][128]
     const int g = h / a.hpk, hh = h - g * a.hpk;
-    const int gl = a.live_slot[g];
+    const int gl = arg_byte(a.live_slot, g);
     float* o = a.out + (((size_t)b * a.n_draft + i) * a.n_q_heads + h) * kHD + ch0;
     const int nt = a.ntile[j];
     if (gl < 0 || nt == 0) {
@@ -1730,6 +1851,30 @@ int simd_count() {
 
 int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; }
 
+// Shares rounded down to a multiple of the segment count when every
+// (sequence, live head) segment has the same number of tiles (one sequence,
+// or a batch of equal lengths): the split then puts every share inside one
+// segment, and no wave pays a second piece's set-up, drain and partial.
+// Used by the int8 kernels, whose piece set-up (query quantisation, first
+// tiles' latency) is long: on MI355X, in the 32k R-SWA verify the 8 waves
+// whose shares crossed a head boundary ended 10 us after the others, and
+// aligned shares took the call from 35.5 to 30.8 us (shared decode 43.4 to
+// 38.9 us).  The f32 kernels got slower with it (R-SWA step 57.1 against
+// 65.4 us: the shares become unequal by a tile).
+template <class Args>
+int align_shares(const Args& a, int shares) {
+    int nt = -1;
+    for (int j = 0; j < a.n_seq; ++j) {
+        if (a.ntile[j] == 0) continue;
+        if (nt >= 0 && a.ntile[j] != nt) return shares;
+        nt = a.ntile[j];
+    }
+    int nseg = 0;
+    for (int j = 0; j < a.n_seq; ++j) nseg += a.ntile[j] > 0 ? a.n_live : 0;
+    if (nseg == 0 || nseg > shares) return shares;
+    return shares / nseg * nseg;
+}
+
 // Cache kinds of the decode launcher.
 constexpr int kF32 = 0, kQ8k = 1, kI8k = 2;
 
@@ -1806,6 +1951,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
         // f32, short launch: one tile per wave (gqa 4096 rows x 6 heads: 16.8 -> 15.2 us per call)
         if (!kQ8 && shares > 0 && a.n_tiles < 2 * shares) shares = a.n_tiles;
         if (shares == 0) return hipErrorInvalidDevice;
+        if (kQ8) shares = align_shares(a, shares);
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};
@@ -1828,14 +1974,16 @@ namespace {
 
 // The query-batched launch: the kernel, then its combine.  which: the
 // resident-wave cache entry of the kernel; one share per wps resident waves,
-// or one per SIMD when wps is 0.
-hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int which, int wps, hipStream_t s) {
+// or one per SIMD when wps is 0; align: shares aligned to equal segments.
+hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int which, int wps, bool align,
+                                hipStream_t s) {
     VerifyArgs a = args;
     a.n_shares = 1;
     if (a.n_tiles > 0) {                          // zero only when every group is dead
         const int wv = wps ? resident_waves(fn, which) : simd_count();
         if (wv == 0) return hipErrorInvalidDevice;
-        const int shares = wps ? (wv + wps - 1) / wps : wv;
+        const int shares0 = wps ? (wv + wps - 1) / wps : wv;
+        const int shares = align ? align_shares(a, shares0) : shares0;
         a.n_shares = shares < a.n_tiles ? shares : a.n_tiles;
         const dim3 grid((a.n_shares + kWaves - 1) / kWaves), block(kWaves * 64);
         void* kargs[] = {&a};
@@ -1865,24 +2013,51 @@ hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int whic
 // Shares: up to 16 queries per row make these waves compute-heavy, unlike the
 // single-query decode.  Measured on MI355X (32k R-SWA reference): the f32
 // kernel (2 waves/SIMD) is fastest with one share per 2 resident waves
-// (verify 70.0 -> 68.0 us), the i8 kernel (3 waves/SIMD) with one per wave
-// (verify 43.1 us; 47.2 us with one per 2, 44.9 against 39.7 us with one per
-// SIMD), except the shared decode, whose 16 queries per head double the
-// partials: one share per SIMD took it from 49.0 to 45.0 us.
+// (verify 70.0 -> 68.0 us).  The i8 kernel runs one share per SIMD with
+// KVQ_VI8_DEPTH tiles in flight and shares aligned to the heads: verify 30.8
+// us, shared decode 38.9 us (one share per resident wave, 3 waves/SIMD and
+// one tile in flight: 35.5 and 43.4 us).
 hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
-    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, s)
-                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, s);
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, false, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, false, s);
 }
 
 #ifndef KVQ_VI8_WPS
-#define KVQ_VI8_WPS 1
+#define KVQ_VI8_WPS 0
 #endif
 #ifndef KVQ_VI8S_WPS
 #define KVQ_VI8S_WPS 0
 #endif
-hipError_t launch_verify_i8(const VerifyArgs& a, hipStream_t s) {
-    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, KVQ_VI8S_WPS, s)
-                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, KVQ_VI8_WPS, s);
+// Padding tiles per segment: the wave whose share holds a segment's last
+// tiles also quantises its trailing rows (and, in the shared decode, reads
+// the rings, whose visibility costs more per tile); padding tiles at the end
+// of every segment, which hold no rows, give that share fewer real tiles.
+// Measured on MI355X (32k R-SWA reference, 10 heads): that wave ended 5 us
+// (verify) and 11 us (shared decode) after the median one; with padding
+// (verify, shared) 0/0 tiles 30.4 / 39.0 us per call, 4/6 28.0 / 35.2,
+// 8/14 26.3 / 33.5, 10/18 26.2 / 33.6.
+#ifndef KVQ_VI8_PAD
+#define KVQ_VI8_PAD 9
+#endif
+#ifndef KVQ_VI8S_PAD
+#define KVQ_VI8S_PAD 14
+#endif
+hipError_t launch_verify_i8(const VerifyArgs& args, hipStream_t s) {
+    VerifyArgs a = args;
+    const int pad = a.shared ? KVQ_VI8S_PAD : KVQ_VI8_PAD;
+    if (pad > 0) {
+        int64_t tiles = 0;
+        for (int j = 0; j < a.n_seq; ++j) {
+            a.tile_base[j] = (int32_t)tiles;
+            if (a.ntile[j] > 0) a.ntile[j] += pad;
+            tiles += (int64_t)a.ntile[j] * a.n_live;
+        }
+        if (tiles >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+        a.tile_base[a.n_seq] = (int32_t)tiles;
+        a.n_tiles = (int)tiles;
+    }
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, KVQ_VI8S_WPS, true, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, KVQ_VI8_WPS, true, s);
 }
 
 hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t s) { return launch_decode<kQ8k>(a, s); }

@@ -8,6 +8,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "kvq.h"
@@ -161,6 +162,16 @@ struct DecodeArgs {
     uint8_t frozen[kSeqPerLaunch];           // q8: column fields hold the frozen RMS
 };
 
+// A byte of a kernel-argument array, read through its aligned dword: with a
+// wave-uniform index that is one scalar load (the byte itself would take a
+// vector load and a wait for it, a microsecond at a piece's start).
+template <class T>
+__device__ __forceinline__ int arg_byte(const T* arr, int i) {
+    static_assert(sizeof(T) == 1, "a byte array");
+    const int32_t w = reinterpret_cast<const int32_t*>(arr)[i >> 2];
+    return (int)(T)(w >> (8 * (i & 3)));
+}
+
 // Partial slots a launch can use: n_shares + n_seq * n_live.
 inline size_t max_slots(int n_seq, int n_live) { return (size_t)kMaxWaves + (size_t)n_seq * n_live; }
 
@@ -212,6 +223,13 @@ struct VerifyArgs {
     float* vs;
 };
 constexpr int kVerifyMaxQ = 16;
+
+// the byte arrays read with arg_byte start on a dword and hold whole dwords
+static_assert(offsetof(AppendArgs, live_head) % 4 == 0, "");
+static_assert(offsetof(DecodeArgs, live_head) % 4 == 0 && offsetof(DecodeArgs, live_slot) % 4 == 0 &&
+              offsetof(DecodeArgs, frozen) % 4 == 0, "");
+static_assert(offsetof(VerifyArgs, live_head) % 4 == 0 && offsetof(VerifyArgs, live_slot) % 4 == 0, "");
+static_assert(KVQ_MAX_KV_HEADS % 4 == 0 && kSeqPerLaunch % 4 == 0, "");
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);   // a.shared: the shared-reference decode

@@ -30,8 +30,25 @@ def i8_head(k, v):
     return h
 
 
+def tie_rows(r, shape):
+    """Rows [*shape][128] whose entries x sit at or near half-integer
+    multiples of the row's int8 scale s = amax / 127 (f32 division, as
+    quantize_row_i8 forms it): x = (k + 1/2 + d) s for offsets d from 0 to
+    1e-3, one entry +-amax; the codes then hang on the correctly rounded
+    quotient and on ties to even."""
+    offs = np.array([0.0, 2.0 ** -20, -2.0 ** -20, 2.0 ** -16, -2.0 ** -16, 2.0 ** -15, -2.0 ** -15,
+                     2.0 ** -14, -2.0 ** -14, 2.0 ** -13, -2.0 ** -13, 1e-3, -1e-3])
+    amax = r.uniform(0.5, 3.0, shape).astype(np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    k = r.integers(-126, 126, shape + (128,)).astype(np.float64)
+    d = offs[r.integers(0, len(offs), shape + (128,))]
+    x = ((k + 0.5 + d) * s[..., None].astype(np.float64)).astype(np.float32)
+    x[..., 0] = np.where(r.integers(0, 2, shape) == 0, amax, -amax)
+    return x
+
+
 def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None, seq=1, batch=2, step_scale=1.0,
-               kind=K.KIND_F32, spread=False, poison=False):
+               kind=K.KIND_F32, spread=False, poison=False, ties=False):
     """ref_k/ref_v [pre][hkv][128]: the shared reference of sequence `seq`;
     kind KIND_I8: the int8 mirror (oracle: its codec and int8 decode).
     poison: every byte of the cache buffers is 0xFF before anything is
@@ -40,7 +57,8 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
     spread: the step rows are 0 on channel 0 and every query is +-32 there
     (sign alternating over the queries of a KV head) and 0 elsewhere, so a
     reference row with 64 on channel 0 scores +-181 and every other row 0
-    (see tests/test_gpu_spread.py)."""
+    (see tests/test_gpu_spread.py).
+    ties: step rows and queries from tie_rows (int8 codes at rounding ties)."""
     r = np.random.default_rng(seed)
     W = K.RING_WINDOW
     pre = ref_k.shape[0]
@@ -70,6 +88,8 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
         q = (r.standard_normal((n_streams, hq, 128)) * step_scale).astype(np.float32)
         kt = (r.standard_normal((n_streams, hkv, 128)) * step_scale).astype(np.float32)
         vt = r.standard_normal((n_streams, hkv, 128)).astype(np.float32)
+        if ties:
+            q, kt, vt = tie_rows(r, (n_streams, hq)), tie_rows(r, (n_streams, hkv)), tie_rows(r, (n_streams, hkv))
         if spread:
             kt[..., 0] = 0.0
             q[:] = 0.0
@@ -129,6 +149,17 @@ def shared_run(ref_k, ref_v, n_streams, hkv, hpk, steps, check, seed, alive=None
             assert np.array_equal(vv[seq, :, pre + W * s + slot], toks[t][1][s][live])
     say("  max err %.3g" % worst)
     return rings
+
+
+def test_shared_i8_step_rows_at_rounding_ties():
+    """The int8 shared decode quantises each stream's step row in the kernel
+    and stores it in the stream's ring: rows built at and near rounding ties
+    of quantize_row_i8 ([P3]) are stored bit for bit as the oracle quantises
+    them, and the decodes (queries near ties too) match the oracle."""
+    say("case: shared i8 step rows at rounding ties")
+    r = np.random.default_rng(77)
+    ref_k, ref_v = r.standard_normal((2, 40, 3, 128)).astype(np.float32)
+    shared_run(ref_k, ref_v, 5, 3, 2, 12, {0, 5, 11}, 78, kind=K.KIND_I8, ties=True)
 
 
 @pytest.mark.parametrize("kind", [K.KIND_F32, K.KIND_I8])
