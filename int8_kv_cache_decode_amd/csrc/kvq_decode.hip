@@ -1175,6 +1175,24 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
     const int lane = threadIdx.x & 63;
     const int qi = lane & 15, kb = lane >> 4;
     for_each_piece(a, w, [&](const Piece& it) {
+        if (it.row0 >= it.row1) {
+            // only padding tiles past the segment's rows (see launch_verify_f32):
+            // an empty partial
+            if (qi < a.nq) {
+                const size_t ix = (size_t)it.slot * a.nq + qi;
+                if (kb == 0) {
+                    a.ws_ml[ix * 2] = -INFINITY;
+                    a.ws_ml[ix * 2 + 1] = 0.0f;
+                }
+                float* dst = a.ws_acc + ix * kHD + 16 * kb;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    *(float4*)(dst + 4 * r) = make_float4(0.f, 0.f, 0.f, 0.f);
+                    *(float4*)(dst + 64 + 4 * r) = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+            return;
+        }
         const int j = it.j;
         const int pre = a.prefill[j];
         const int L = kShared ? pre + KVQ_RING_WINDOW * a.n_draft       // reference + rings; step rows follow
@@ -1189,12 +1207,22 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
             return p < L ? C + (size_t)p * kHD : D + (size_t)(p - L) * dstride;
         };
         if constexpr (kShared) {
-            // [P3] write_decode_step of each stream whose step row is in this piece
-            for (int s = 0; s < a.n_draft; ++s) {
-                if (L + s >= it.row0 && L + s < it.row1 && lane < 32) {
-                    const size_t wr = it.hrow + (size_t)a.swrow[s];
-                    *(float4*)(a.k_store + wr * kHD + 4 * lane) = *(const float4*)(KD + s * dstride + 4 * lane);
-                    *(float4*)(a.v_store + wr * kHD + 4 * lane) = *(const float4*)(VD + s * dstride + 4 * lane);
+            // [P3] write_decode_step of each stream whose step row is in this
+            // piece: lane l copies stream l / 4's channels 32 (l % 4) .., all
+            // its loads issued before its stores
+            const int s = lane >> 2, c0 = 32 * (lane & 3);
+            if (s < a.n_draft && L + s >= it.row0 && L + s < it.row1) {
+                const size_t wr = it.hrow + (size_t)a.swrow[s];
+                float4 kx[8], vx[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    kx[u] = *(const float4*)(KD + s * dstride + c0 + 4 * u);
+                    vx[u] = *(const float4*)(VD + s * dstride + c0 + 4 * u);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    *(float4*)(a.k_store + wr * kHD + c0 + 4 * u) = kx[u];
+                    *(float4*)(a.v_store + wr * kHD + c0 + 4 * u) = vx[u];
                 }
             }
         }
@@ -1855,12 +1883,12 @@ int hpk_index(int hpk) { return hpk == 1 ? 0 : hpk == 2 ? 1 : hpk == 4 ? 2 : 3; 
 // (sequence, live head) segment has the same number of tiles (one sequence,
 // or a batch of equal lengths): the split then puts every share inside one
 // segment, and no wave pays a second piece's set-up, drain and partial.
-// Used by the int8 kernels, whose piece set-up (query quantisation, first
-// tiles' latency) is long: on MI355X, in the 32k R-SWA verify the 8 waves
-// whose shares crossed a head boundary ended 10 us after the others, and
-// aligned shares took the call from 35.5 to 30.8 us (shared decode 43.4 to
-// 38.9 us).  The f32 kernels got slower with it (R-SWA step 57.1 against
-// 65.4 us: the shares become unequal by a tile).
+// Used by the query-batched kernels and the q8 / int8 decode, whose piece
+// set-up (query quantisation, first tiles' latency) is long: on MI355X, in
+// the 32k R-SWA int8 verify the 8 waves whose shares crossed a head boundary
+// ended 10 us after the others, and aligned shares took the call from 35.5
+// to 30.8 us (shared decode 43.4 to 38.9 us).  The f32 decode got slower with
+// it (R-SWA step 57.1 against 65.4 us: the shares become unequal by a tile).
 template <class Args>
 int align_shares(const Args& a, int shares) {
     int nt = -1;
@@ -2017,9 +2045,38 @@ hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int whic
 // KVQ_VI8_DEPTH tiles in flight and shares aligned to the heads: verify 30.8
 // us, shared decode 38.9 us (one share per resident wave, 3 waves/SIMD and
 // one tile in flight: 35.5 and 43.4 us).
-hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
-    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, false, s)
-                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, false, s);
+// Adds pad tiles, which hold no rows, to the end of every segment of a.
+bool pad_segments(VerifyArgs& a, int pad) {
+    if (pad <= 0) return true;
+    int64_t tiles = 0;
+    for (int j = 0; j < a.n_seq; ++j) {
+        a.tile_base[j] = (int32_t)tiles;
+        if (a.ntile[j] > 0) a.ntile[j] += pad;
+        tiles += (int64_t)a.ntile[j] * a.n_live;
+    }
+    if (tiles >= ((int64_t)1 << 31)) return false;
+    a.tile_base[a.n_seq] = (int32_t)tiles;
+    a.n_tiles = (int)tiles;
+    return true;
+}
+
+// The f32 kernel, likewise (shares aligned to the heads, padding tiles per
+// segment; measured on MI355X, 32k R-SWA reference: verify 67.3 -> 65.4 us,
+// shared decode 72.4 -> 70.7 us).
+#ifndef KVQ_VF32_PAD
+#define KVQ_VF32_PAD 8
+#endif
+#ifndef KVQ_VF32S_PAD
+#define KVQ_VF32S_PAD 16
+#endif
+#ifndef KVQ_VF32_ALIGN
+#define KVQ_VF32_ALIGN 1
+#endif
+hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
+    VerifyArgs a = args;
+    if (!pad_segments(a, a.shared ? KVQ_VF32S_PAD : KVQ_VF32_PAD)) return hipErrorInvalidValue;
+    return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, KVQ_VF32_ALIGN, s)
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, KVQ_VF32_ALIGN, s);
 }
 
 #ifndef KVQ_VI8_WPS
@@ -2044,18 +2101,7 @@ hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s) {
 #endif
 hipError_t launch_verify_i8(const VerifyArgs& args, hipStream_t s) {
     VerifyArgs a = args;
-    const int pad = a.shared ? KVQ_VI8S_PAD : KVQ_VI8_PAD;
-    if (pad > 0) {
-        int64_t tiles = 0;
-        for (int j = 0; j < a.n_seq; ++j) {
-            a.tile_base[j] = (int32_t)tiles;
-            if (a.ntile[j] > 0) a.ntile[j] += pad;
-            tiles += (int64_t)a.ntile[j] * a.n_live;
-        }
-        if (tiles >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-        a.tile_base[a.n_seq] = (int32_t)tiles;
-        a.n_tiles = (int)tiles;
-    }
+    if (!pad_segments(a, a.shared ? KVQ_VI8S_PAD : KVQ_VI8_PAD)) return hipErrorInvalidValue;
     return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<true>), 27, KVQ_VI8S_WPS, true, s)
                     : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_i8<false>), 26, KVQ_VI8_WPS, true, s);
 }
