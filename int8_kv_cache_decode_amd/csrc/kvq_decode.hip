@@ -496,6 +496,9 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #ifndef KVQ_Q8_MIN_WAVES
 #define KVQ_Q8_MIN_WAVES 3
 #endif
+#ifndef KVQ_Q8_PRIO
+#define KVQ_Q8_PRIO 1
+#endif
 template <int HPK, bool kCap, bool kI8, bool kMf>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
@@ -526,6 +529,24 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     const double inv_c2 = kCap ? 1.0 / a.softcap2 : 0.0;
     const int hq = lane >> 4, n = lane & 15;          // score layout
     const int ri = lane / kVSeg, seg = lane % kVSeg;  // V layout
+    // Wave priority by progress: the SIMD issues the oldest ready wave first,
+    // so with equal shares the first workgroups on a compute unit would
+    // finish long before the last ones and leave the tail of the launch to
+    // one wave per SIMD.  Each wave lowers its priority as it passes each
+    // quarter of its share, so a wave that has fallen behind is issued first.
+    const int share_tiles = max(1, (int)((int64_t)(w + 1) * a.n_tiles / a.n_shares) -
+                                       (int)((int64_t)w * a.n_tiles / a.n_shares));
+    int done = 0, lvl = 0;
+    if (KVQ_Q8_PRIO) __builtin_amdgcn_s_setprio(3);
+    auto progress = [&](int tiles) {
+        done += tiles;
+        if (KVQ_Q8_PRIO && lvl < 3 && 4 * done >= (lvl + 1) * share_tiles) {
+            ++lvl;
+            if (lvl == 1) __builtin_amdgcn_s_setprio(2);
+            else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
+    };
     for_each_piece(a, w, [&](const Piece& it) {
         const int8_t* KQ = a.kq + it.hidx * kq_rows(a.capacity) * kHD;   // tile-major K codes
         const float* KS = a.ks + it.hrow * (kI8 ? 1 : kKScales);
@@ -957,6 +978,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             load_step(r0 + 2 * kStep, ta);
             compute_step(r0 + kStep, tb);
             r0 += 2 * kStep;
+            progress(2 * kTiles);
         }
         if (r0 < it.row1) compute_step(r0, ta);
 
@@ -1938,7 +1960,13 @@ const void* decode_kernel(bool cap, bool mf) {
 // which takes one tile per wave: with one wave per SIMD its waves spend the
 // kernel in the dependent shuffles of their tiles, and more waves overlap them.
 
-constexpr int kQ8MinTilesPerWave = 4;
+#ifndef KVQ_Q8_MIN_TPW
+#define KVQ_Q8_MIN_TPW 4
+#endif
+#ifndef KVQ_Q8_SHORT_SPS
+#define KVQ_Q8_SHORT_SPS 1
+#endif
+constexpr int kQ8MinTilesPerWave = KVQ_Q8_MIN_TPW;
 // The q8 / int8 value pass goes to the matrix cores only when a launch has
 // at least this many tiles per resident wave; below that the VALU instance
 // runs.  Measured on MI355X, 32 Q / 8 KV heads, q8 (matrix cores against
@@ -1975,7 +2003,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
             fn = pick(false);
             shares = resident_waves(fn, which + 28);   // entries 28.. (24..27: verify)
         }
-        if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = simd_count();
+        if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = KVQ_Q8_SHORT_SPS * simd_count();
         // f32, short launch: one tile per wave (gqa 4096 rows x 6 heads: 16.8 -> 15.2 us per call)
         if (!kQ8 && shares > 0 && a.n_tiles < 2 * shares) shares = a.n_tiles;
         if (shares == 0) return hipErrorInvalidDevice;
