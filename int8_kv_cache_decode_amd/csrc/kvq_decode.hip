@@ -534,6 +534,9 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     // finish long before the last ones and leave the tail of the launch to
     // one wave per SIMD.  Each wave lowers its priority as it passes each
     // quarter of its share, so a wave that has fallen behind is issued first.
+    // (A launch-wide progress counter, one device-scope atomic per wave every
+    // 4 tiles, made the batched q8 decode four times slower: every wave hits
+    // one address.)
     const int share_tiles = max(1, (int)((int64_t)(w + 1) * a.n_tiles / a.n_shares) -
                                        (int)((int64_t)w * a.n_tiles / a.n_shares));
     int done = 0, lvl = 0;
