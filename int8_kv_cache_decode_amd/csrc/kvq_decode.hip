@@ -499,6 +499,14 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 #ifndef KVQ_Q8_PRIO
 #define KVQ_Q8_PRIO 1
 #endif
+// progress (sixteenths of the share) at which a wave's priority drops to 2,
+// 1, 0: finer toward the end, where the spread left over decides the tail
+// (batched q8, same box: quarters 355.9 us, 8 12 14 352.7 us, 6 10 14 353.8,
+// 10 13 15 353.4, 2 6 12 356.4)
+#ifndef KVQ_Q8_PRIO_STEPS
+#define KVQ_Q8_PRIO_STEPS 8, 12, 14
+#endif
+__device__ constexpr int kPrioStep[3] = {KVQ_Q8_PRIO_STEPS};
 template <int HPK, bool kCap, bool kI8, bool kMf>
 __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_decode_q8(const DecodeArgs a) {
     constexpr int NB = (HPK + 3) / 4;                 // blocks of 4 heads (MFMA rows = 4 heads x 4 digits)
@@ -532,8 +540,9 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     // Wave priority by progress: the SIMD issues the oldest ready wave first,
     // so with equal shares the first workgroups on a compute unit would
     // finish long before the last ones and leave the tail of the launch to
-    // one wave per SIMD.  Each wave lowers its priority as it passes each
-    // quarter of its share, so a wave that has fallen behind is issued first.
+    // one wave per SIMD.  Each wave lowers its priority step by step as it
+    // passes fixed fractions of its share (kPrioStep), so a wave that has
+    // fallen behind is issued first.
     // (A launch-wide progress counter, one device-scope atomic per wave every
     // 4 tiles, made the batched q8 decode four times slower: every wave hits
     // one address.)
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
     if (KVQ_Q8_PRIO) __builtin_amdgcn_s_setprio(3);
     auto progress = [&](int tiles) {
         done += tiles;
-        if (KVQ_Q8_PRIO && lvl < 3 && 4 * done >= (lvl + 1) * share_tiles) {
+        if (KVQ_Q8_PRIO && lvl < 3 && 16 * done >= kPrioStep[lvl] * share_tiles) {
             ++lvl;
             if (lvl == 1) __builtin_amdgcn_s_setprio(2);
             else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
