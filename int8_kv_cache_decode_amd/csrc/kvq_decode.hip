@@ -1158,12 +1158,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
     const int nch = tile_owner(sb + nt - 1, a.n_tiles, a.n_shares) - first + 1;
     const size_t it0 = (size_t)first + (size_t)j * a.n_live + gl;
     const float zs = a.sinks ? (float)((double)a.sinks[h] * 1.4426950408889634) : -INFINITY;
+    // the V column field is loaded before the partials, so that its latency
+    // overlaps theirs
+    const bool frz = kQ8 && arg_byte(a.frozen, j);
+    float4 vc = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (frz && tid < lpg) vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + ch0 + 4 * tid);
     float4 rr;
     if (!combine_partials(a.ws_ml + (it0 * a.hpk + hh) * 2, a.ws_acc + (it0 * a.hpk + hh) * kHD,
                           (size_t)a.hpk * 2, (size_t)a.hpk * kHD, nch, zs, lpg, ch0, &rr))
         return;
-    if (kQ8 && arg_byte(a.frozen, j)) {
-        const float4 vc = *(const float4*)(a.vcol + ((size_t)b * a.n_live + gl) * kHD + ch0 + 4 * tid);
+    if (frz) {
         rr.x *= vc.x;
         rr.y *= vc.y;
         rr.z *= vc.z;
