@@ -1976,13 +1976,10 @@ const void* decode_kernel(bool cap, bool mf) {
 // which takes one tile per wave: with one wave per SIMD its waves spend the
 // kernel in the dependent shuffles of their tiles, and more waves overlap them.
 
-#ifndef KVQ_Q8_MIN_TPW
-#define KVQ_Q8_MIN_TPW 4
-#endif
-#ifndef KVQ_Q8_SHORT_SPS
-#define KVQ_Q8_SHORT_SPS 1
-#endif
-constexpr int kQ8MinTilesPerWave = KVQ_Q8_MIN_TPW;
+// (Also measured on the R-SWA step on the int8 mirror, 5 tiles per resident
+// wave: one share per SIMD 23.7 against 22.3 us; two per SIMD 22.3 us, and
+// two per SIMD on the short q8 launch above 16.6 against 15.1 us.)
+constexpr int kQ8MinTilesPerWave = 4;
 // The q8 / int8 value pass goes to the matrix cores only when a launch has
 // at least this many tiles per resident wave; below that the VALU instance
 // runs.  Measured on MI355X, 32 Q / 8 KV heads, q8 (matrix cores against
@@ -2019,7 +2016,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
             fn = pick(false);
             shares = resident_waves(fn, which + 28);   // entries 28.. (24..27: verify)
         }
-        if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = KVQ_Q8_SHORT_SPS * simd_count();
+        if (kQ8 && shares > 0 && a.n_tiles < kQ8MinTilesPerWave * shares) shares = simd_count();
         // f32, short launch: one tile per wave (gqa 4096 rows x 6 heads: 16.8 -> 15.2 us per call)
         if (!kQ8 && shares > 0 && a.n_tiles < 2 * shares) shares = a.n_tiles;
         if (shares == 0) return hipErrorInvalidDevice;
