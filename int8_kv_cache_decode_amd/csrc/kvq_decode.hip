@@ -1325,11 +1325,27 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
             }
             float sc[4];
             float tmax = -INFINITY;
+            if (kShared && r0 >= pre && r0 + kTileRows <= min(L, it.row1) &&
+                ((r0 - pre) >> 7) == ((r0 + kTileRows - 1 - pre) >> 7)) {
+                // a whole tile of stream ts's ring (wave-uniform): only that
+                // stream's queries see it, each of its live slots but the one
+                // this step overwrites (on MI355X, 32k reference and 16
+                // streams, 70.6 -> 68.3 us per call against the general test)
+                const int ts = (r0 - pre) >> 7;
+                const int s0 = ((r0 - pre) & (KVQ_RING_WINDOW - 1)) + 4 * kb;
+                const bool mine = qvalid && di == ts;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int p = r0 + 4 * kb + r;
-                sc[r] = (qvalid && p < it.row1 && visible(p)) ? c[r] : -INFINITY;
-                tmax = fmaxf(tmax, sc[r]);
+                for (int r = 0; r < 4; ++r) {
+                    sc[r] = (mine && s0 + r < live && s0 + r != wslot) ? c[r] : -INFINITY;
+                    tmax = fmaxf(tmax, sc[r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int p = r0 + 4 * kb + r;
+                    sc[r] = (qvalid && p < it.row1 && visible(p)) ? c[r] : -INFINITY;
+                    tmax = fmaxf(tmax, sc[r]);
+                }
             }
             tmax = max_rows(tmax);
             const float mnew = fmaxf(m, tmax);
