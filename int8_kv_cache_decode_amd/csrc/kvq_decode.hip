@@ -639,8 +639,25 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
 #pragma unroll
             for (int k = 0; k < kTiles; ++k) load_tile(r + 16 * k, t[k]);
         };
-        // The first step's loads go out before the query set-up below (a piece
-        // is never empty).
+        // The query's loads (and the K column field's) go out first, then the
+        // first step's tile loads, then the query set-up below (a piece is
+        // never empty): the set-up waits for the query alone.  With the
+        // query loaded after the tiles, on a short launch -- where every
+        // wave's first tiles fill the memory queues at once -- the set-up
+        // waited 3 us for it (one 8192-row sequence, 32 Q / 8 KV heads: 4
+        // tiles per wave in 8.7 us; the call went from 15.2 to 14.3 us).
+        // (Same box, three alternations: batched q8 350.7 against 353.3 us, the
+        // soft-cap + sinks call 355.4 against 358.1 us, int8 unchanged at
+        // 325.1 us.)
+        float2 qraw[HPK];
+        float2 kcv = make_float2(1.f, 1.f);
+#pragma unroll
+        for (int h = 0; h < HPK; ++h)
+            qraw[h] = *(const float2*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 2 * lane);
+        if constexpr (!kI8) {
+            const float2 kc = *(const float2*)(kcol + 2 * lane);   // loaded either way: no branch
+            kcv = frz ? kc : kcv;
+        }
         int r0 = it.row0;
         Tile ta[kTiles], tb[kTiles];
         load_step(r0, ta);
@@ -660,10 +677,10 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             // 16 lanes that hold its 32 channels, and the four digits, written
             // into a per-wave LDS copy of the A operands; each lane then reads
             // its 16 digit bytes.  The group exponents go through LDS too.
-            const float2 cv = frz ? *(const float2*)(kcol + 2 * lane) : make_float2(1.f, 1.f);
+            const float2 cv = kcv;
 #pragma unroll
             for (int h = 0; h < HPK; ++h) {
-                const float2 qv = *(const float2*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 2 * lane);
+                const float2 qv = qraw[h];
                 const double q0 = (double)qv.x * (double)cv.x, q1 = (double)qv.y * (double)cv.y;   // exact
                 double gmax = fmax(fabs(q0), fabs(q1));
 #pragma unroll
@@ -713,7 +730,7 @@ __global__ __launch_bounds__(256, (HPK <= 4 ? KVQ_Q8_MIN_WAVES : 2)) void k_deco
             float qsh[HPK];
 #pragma unroll
             for (int h = 0; h < HPK; ++h) {
-                const float2 x = *(const float2*)(a.q + ((size_t)it.b * a.n_q_heads + it.g * HPK + h) * kHD + 2 * lane);
+                const float2 x = qraw[h];
                 const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
                 const float qs = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 1.0f;
                 char2 cq;
