@@ -432,8 +432,8 @@ int kv_truncate_last(kvq_cache* c, int seq, int n_drop);
  * `seq`: drop the front rows a sliding-window layer of window w can never
  * read again.  *base (host, in/out) is the absolute position of the
  * sequence's row 0.  Nothing happens while len <= 2w, for w == 0, or on a q8
- * sequence whose column field is not frozen yet (the freeze reads every
- * row).  Otherwise the rows from
+ * sequence before its freeze (the column field is computed over all stored
+ * rows, so none may go before it).  Otherwise the rows from
  *   keep_from = min(base + len - (w + slack), anchor - (w + slack))  (>= 0)
  * on stay, the cut rounded down to a multiple of max(align, 1):
  *   d = (keep_from / align) * align - base   rows are dropped if d > 0,

@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kFreezeThreads) void k_freeze(const FreezeArgs a) {
     }
 }
 
-// Front-trim moves ([P2] trim_window: the rows that stay keep their order and
-// values), one round per launch for every sequence listed in it: rows [src,
+// Front-trim moves ([P2] trim_window: the kept rows move to the front,
+// unchanged and in order), one round per launch for every sequence listed in it: rows [src,
 // src + m) go to [dst, dst + m) with src - dst = d >= m, so a launch's source
 // and destination never overlap, and consecutive launches on the stream order
 // a round's reads before the next round's writes.  grid (blocks, sequence x

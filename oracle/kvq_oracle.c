@@ -232,9 +232,9 @@ static double q8_elem(const void* ctx, int p, int d)
  *            at least one row is (rows before it get probability 0);
  *   softcap  > 0: the scaled scores are soft-capped (Gemma-2),
  *            s = softcap * tanh(s / softcap); 0 leaves them as they are;
- *   sinks    NULL, or one learned logit per head that joins the softmax as a
- *            column without a value row: it takes part in the max and adds
- *            exp(sink - max) to the denominator; it is not capped.        */
+ *   sinks    NULL, or one learned logit per head, treated as one more
+ *            score with no value row: the max is taken over it too, and its
+ *            exponential enters the normaliser only; it is not capped.     */
 static void attend_generic(int n, int hd, int hpk, const float* q,
                            orc_elem_fn kf, const void* kctx,
                            orc_elem_fn vf, const void* vctx,
