@@ -82,7 +82,7 @@ extern "C" {
  * contiguous rows of 128 channels ([P1] module doc: one contiguous
  * [pos x head_dim] block per KV head).  Dead KV heads -- GQA groups whose Q
  * heads are all masked -- own no storage at all and get no work ([P1] module
- * doc: masked heads cost neither FLOPs nor memory); live heads are numbered
+ * doc: a masked head is neither stored nor computed); live heads are numbered
  * densely by live_slot.  The alive mask is fixed when the cache is created.
  *
  * f32 kind: K and V rows as float.
@@ -502,7 +502,7 @@ int rswa_shared_record_prefill(kvq_cache* c, int seq, kvq_ring* rings, int n_str
  * what rswa_decode would give it alone: its step's K/V go to its ring slot
  * (the same cursor rules, row prefill + 128 s + slot), then its Q heads
  * attend, with no mask, over the reference rows and its own live ring slots
- * ([P3] batched_decode_attention: per stream over its own reference ++ ring).
+ * ([P3] batched_decode_attention: stream s attends reference ++ ring s).
  * The reference rows are read once for every stream's queries: n_streams x
  * (n_q_heads / n_kv_heads) <= 16 queries per KV head share each row read, a
  * dense contraction on the matrix cores.  On an i8 cache each step row is

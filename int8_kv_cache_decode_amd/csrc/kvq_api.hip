@@ -798,7 +798,7 @@ int rswa_decode(kvq_cache* c, kvq_ring* rings, int n_q_heads, const float* q, co
             return fail(KVQ_ESTATE, "%s: sequence %d: len %d != prefill %d + ring %d (appended since record?)", fn,
                         b, c->len[b], r.prefill_len, r.ring_len);
         int slot;
-        if (r.ring_len < KVQ_RING_WINDOW) {   // warm-up: append, no eviction
+        if (r.ring_len < KVQ_RING_WINDOW) {   // ring not full yet: next free slot, nothing evicted
             slot = r.ring_len;
             r.ring_len += 1;
             r.ring_pos = r.ring_len % KVQ_RING_WINDOW;

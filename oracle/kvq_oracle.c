@@ -192,7 +192,7 @@ int orc_q8_freeze_head(int hd, int8_t* kq, float* ks, int8_t* vq, float* vs,
 /* Attention, by definition, in double precision.                            */
 /*                                                                            */
 /* One KV row set of n rows and hpk query heads that share it (a GQA group;  */
-/* [P1] attend_group: "head h belongs to group h / hpk").                     */
+/* [P1] attend_group: Q head h reads KV head h / hpk).                        */
 /*   q[hpk][hd]   f32 queries                                                 */
 /*   out[hpk][hd] double results; n == 0 gives zeros ([P1] attend_group:      */
 /*                "stored == 0 -> out = 0").                                  */
