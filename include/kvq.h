@@ -321,7 +321,7 @@ int decode_attn_i8(const kvq_cache* c, int n_q_heads, const float* q, float* out
  * first    host int32 [batch], or NULL for 0: sequence b attends rows
  *          [first[b], len[b]) only (a sliding window is first = len - W);
  *          first[b] >= len[b] is clamped to len[b] - 1, so at least one row
- *          stays visible.  Rows before first get probability exactly 0.
+ *          stays visible.  Rows below first carry weight 0 exactly.
  * softcap  > 0: every scaled score s becomes softcap * tanh(s / softcap)
  *          (Gemma-2 soft-capping) before the softmax; 0 = off.
  * sinks    device float [n_q_heads], or NULL for none: one learned logit per
@@ -362,8 +362,8 @@ int decode_attn_q8_ex(const kvq_cache* c, int n_q_heads, const float* q, float* 
 int rswa_record_prefill(kvq_cache* c, kvq_ring* rings, int seq);
 
 /*
- * rswa_verify -- [P3] verify_attention: the query-batched verify of
- * speculative decoding.  For every sequence b and draft i < n_draft, out[b][i]
+ * rswa_verify -- [P3] verify_attention: checks n_draft speculated tokens in
+ * one call.  For every sequence b and draft i < n_draft, out[b][i]
  * is what the i-th of n_draft sequential rswa_decode steps fed with the draft
  * tokens 0..i would return: each Q head attends, with no mask, to the
  * reference rows, the ring as it would stand after draft tokens 0..i were
