@@ -1,9 +1,12 @@
 """Plants plausible mistakes in a COPY of the oracle source (CPU only) and
 checks that the oracle pins catch every one of them.
 
-Each mutant is a one-line edit of oracle/kvq_oracle.c, compiled into a
+Each C mutant is a one-line edit of oracle/kvq_oracle.c, compiled into a
 temporary library that a child pytest process loads in place of the real
-oracle; the pin suite must fail for it.  (A lower clamp of -128 is not listed:
+oracle; each Python mutant is an edit of a copy of oracle/__init__.py (the
+ring cursor model, rollback, the verify, the batch driver's GQA mapping,
+truncate and the trim) that the child process imports in place of the real
+package.  The pin suite must fail for every one.  (A lower clamp of -128 is not listed:
 |r/s| never rounds beyond 127, so that edit cannot change any output.)
 """
 import os
@@ -85,3 +88,60 @@ def test_pins_catch_mutant(name, tmp_path):
     r = subprocess.run([sys.executable, str(runner), str(so), ROOT, pins],
                        capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "mutant survived the pins: " + name
+
+
+# Mutants of the oracle's Python half (oracle/__init__.py): the R-SWA ring
+# cursor model, checkpoint / rollback, the K-draft verify, the GQA mapping of
+# the batch driver, truncate and the sliding-window trim.
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = {
+    "ring_steady_slot_ahead": ("            slot = self.ring_pos\n            self.ring_pos = (self.ring_pos + 1) % self.W",
+                               "            slot = (self.ring_pos + 1) % self.W\n            self.ring_pos = (self.ring_pos + 1) % self.W"),
+    "ring_pos_stuck": ("self.ring_pos = (self.ring_pos + 1) % self.W", "self.ring_pos = self.ring_pos % self.W"),
+    "window_one_short": ("return self.tokens[-self.W:] if self.tokens else []",
+                         "return self.tokens[-(self.W - 1):] if self.tokens else []"),
+    "rollback_allows_eviction": ('discarded > self.W - cp["ring_len"]', 'discarded > self.W'),
+    "rollback_keeps_lineage": ("        if discarded:\n            self.epoch += 1", "        pass"),
+    "verify_sees_next_draft": ("toks_k = np.concatenate([history_k[g], draft_k[: i + 1, g]])",
+                               "toks_k = np.concatenate([history_k[g], draft_k[: i + 2, g]])"),
+    "verify_ring_one_long": ("rows_k = np.concatenate([ref_k[g], toks_k[-window:]])",
+                             "rows_k = np.concatenate([ref_k[g], toks_k[-window - 1:]])"),
+    "decode_wrong_group": ("qg = np.ascontiguousarray(q[b, g * hpk:(g + 1) * hpk])",
+                           "qg = np.ascontiguousarray(q[b, g:g + hpk])"),
+    "truncate_one_more": ("return n - min(n_drop, n)", "return max(n - n_drop - 1, 0)"),
+    "trim_no_slack": ("keep_from = max(base + n - (w + slack), 0)", "keep_from = max(base + n - w, 0)"),
+    "trim_trigger_strict": ("if w == 0 or n <= 2 * w or q8_unfrozen:", "if w == 0 or n < 2 * w or q8_unfrozen:"),
+    "trim_align_up": ("new_base = keep_from // align * align", "new_base = -(-keep_from // align) * align"),
+    "trim_anchor_ignored": ("        keep_from = min(keep_from, max(anchor - (w + slack), 0))", "        pass"),
+}
+
+PY_RUNNER = r'''
+import sys
+sys.path.insert(0, sys.argv[2])
+sys.path.insert(0, sys.argv[1])
+import oracle
+assert oracle.__file__.startswith(sys.argv[1]), oracle.__file__
+import pytest
+sys.exit(pytest.main(["-q", "-x", "-p", "no:cacheprovider", sys.argv[3]]))
+'''
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_python_mutant(name, tmp_path):
+    import shutil
+    src = open(PY_SRC).read()
+    old, new = PY_MUTANTS[name]
+    assert src.count(old) == 1, "mutation site not found: " + name
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    shutil.copy2(os.path.join(ROOT, "oracle", "kvq_oracle.c"), pkg / "kvq_oracle.c")
+    built = os.path.join(ROOT, "oracle", "libkvq_oracle.so")
+    if os.path.exists(built):
+        shutil.copy2(built, pkg / "libkvq_oracle.so")
+    (pkg / "__init__.py").write_text(src.replace(old, new))
+    runner = tmp_path / "run.py"
+    runner.write_text(PY_RUNNER)
+    pins = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+    r = subprocess.run([sys.executable, str(runner), str(tmp_path), ROOT, pins],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "mutant survived the pins: " + name + "\n" + r.stdout[-2000:]

@@ -795,6 +795,32 @@ def test_trim_window_page_invariants():
     assert oracle.trim_window(0, 500, 10, 2, 4, q8_unfrozen=True) == 0   # q8 field not frozen yet
 
 
+def test_trim_window_page_bounds_sweep():
+    """[P2] LayerKvCache::trim_window (doc and body): with at most 2w rows
+    stored nothing is dropped; past that the front is drained down to
+    w + slack rows, the cut rounded down to an absolute position that is a
+    multiple of align, so that w + slack .. w + slack + align - 1 rows stay
+    (nothing is dropped when the rounded cut does not pass the base).  Swept
+    over w, slack, align, base and length; align 1 leaves exactly w + slack
+    rows."""
+    for w in (1, 3, 10, 64):
+        for slack in (0, 1, 5):
+            for align in (1, 2, 4, 16):
+                for base in (0, 3, 37, 64):
+                    assert oracle.trim_window(base, 2 * w, w, slack, align) == 0
+                    for n in (2 * w + 1, 2 * w + 7, 5 * w + 3, 1000):
+                        d = oracle.trim_window(base, n, w, slack, align)
+                        cut = (base + n - (w + slack)) // align * align
+                        if cut <= base:
+                            assert d == 0, (w, slack, align, base, n, d)
+                            continue
+                        stay = n - d
+                        assert (base + d) % align == 0, (w, slack, align, base, n, d)
+                        assert w + slack <= stay <= w + slack + align - 1, (w, slack, align, base, n, d)
+                        if align == 1:
+                            assert stay == w + slack
+
+
 def test_trim_window_anchored_page_example():
     """[P2] test swa_anchored_trim_keeps_the_rollback_window: with anchor 40
     (w 6, slack 2, align 4) the base never passes anchor - slack + 1 - w, so
