@@ -113,6 +113,12 @@ PY_MUTANTS = {
     "trim_trigger_strict": ("if w == 0 or n <= 2 * w or q8_unfrozen:", "if w == 0 or n < 2 * w or q8_unfrozen:"),
     "trim_align_up": ("new_base = keep_from // align * align", "new_base = -(-keep_from // align) * align"),
     "trim_anchor_ignored": ("        keep_from = min(keep_from, max(anchor - (w + slack), 0))", "        pass"),
+    "decode_first_shifted": ("f = 0 if first is None else int(first[b])", "f = 0 if first is None else int(first[b]) + 1"),
+    "decode_sinks_wrong_heads": ("np.asarray(sinks, np.float32)[g * hpk:(g + 1) * hpk]",
+                                 "np.asarray(sinks, np.float32)[g:g + hpk]"),
+    "rollback_from_future": ('if cp["writes"] > self.writes:', 'if cp["writes"] > self.writes + 1:'),
+    "prefill_keeps_ring": ("        self.prefill_len = n\n        self.ring_len = 0",
+                           "        self.prefill_len = n\n        self.ring_len = self.ring_len"),
 }
 
 PY_RUNNER = r'''

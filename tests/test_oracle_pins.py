@@ -626,6 +626,45 @@ def test_all_options_on_q8_rows():
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
 
 
+def test_batched_driver_routes_first_and_sinks_per_sequence_and_head():
+    """[P1] attend_group / [P2] attend_group_upto through the batched driver:
+    Q head h reads KV head h // hpk, sequence b's first visible row is its own
+    (clamped to its last row), and the sink logit of Q head h is sinks[h];
+    each (b, h) against torch SDPA in f64 with the masked rows and the sink
+    column written out, and dead groups give zeros."""
+    r = rng(3500)
+    B, hkv, hpk = 3, 3, 2
+    hq = hkv * hpk
+    lens = [37, 9, 20]
+    first = [5, 40, 19]                               # inside, past the end (clamped to 8), the last row
+    sinks = np.array([0.8, -2.5, 3.0, 0.1, -1.0, 4.5], np.float32)
+    units = [[None] * hkv for _ in range(B)]
+    for b, n in enumerate(lens):
+        for g in range(hkv):
+            if (b, g) == (1, 2):
+                continue                              # a dead group
+            units[b][g] = ("f32", (r.standard_normal((n, HD)) * 2).astype(np.float32),
+                           r.standard_normal((n, HD)).astype(np.float32))
+    q = r.standard_normal((B, hq, HD)).astype(np.float32)
+    got = oracle.decode(q, units, hkv, first=first, sinks=sinks)
+    for b in range(B):
+        for g in range(hkv):
+            sl = slice(g * hpk, (g + 1) * hpk)
+            if units[b][g] is None:
+                assert not got[b, sl].any()
+                continue
+            _, k, v = units[b][g]
+            ref = options_reference(q[b, sl], k, v, first[b], 0.0, sinks[sl])
+            np.testing.assert_allclose(got[b, sl], ref, rtol=0, atol=1e-12)
+    plain = oracle.decode(q, units, hkv)
+    for b in range(B):
+        for g in range(hkv):
+            if units[b][g] is not None:
+                sl = slice(g * hpk, (g + 1) * hpk)
+                np.testing.assert_allclose(plain[b, sl], options_reference(q[b, sl], units[b][g][1], units[b][g][2],
+                                                                           0, 0.0, None), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # R-SWA ring cursors
 # ---------------------------------------------------------------------------
@@ -770,6 +809,22 @@ def test_ring_rollback_refusals_page_examples():
         m.write(1)
     with pytest.raises(ValueError):
         m.rollback_to(cp)
+
+
+def test_ring_reprefill_resets_cursors():
+    """[P3] RingCache::record_prefill: a new prefill empties the ring -- length,
+    position and write count back to 0 -- so the effective length is the new
+    reference length and the next write lands in slot 0, from steady state
+    as from warm-up."""
+    for writes in (7, oracle.RING_W + 37):
+        m = oracle.RingModel()
+        m.record_prefill(11)
+        for t in range(writes):
+            m.write(t)
+        m.record_prefill(23)
+        assert (m.prefill_len, m.ring_len, m.ring_pos, m.writes) == (23, 0, 0, 0)
+        assert m.window() == [] and m.physical() == [] and m.effective_len() == 23
+        assert m.write("new") == 0 and m.window() == ["new"] and m.effective_len() == 24
 
 
 def test_trim_window_page_invariants():
