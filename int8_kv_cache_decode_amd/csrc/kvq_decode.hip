@@ -1223,8 +1223,15 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const DecodeArgs a)
 // reference, its ring slots that were live before this step except the one
 // the step overwrites, and its own step row.  The wave whose share holds
 // step row s also stores it into stream s's ring.
+// Occupancy: the verify (kShared false) runs one wave per SIMD and may use
+// the whole register file (up to 512 registers); the shared decode stays at
+// two waves' worth (256).  Measured on MI355X, 32k R-SWA reference, 8
+// drafts: 65.2 -> 64.0 us per call.  The shared decode was slower with the
+// same setting (78.4 against 75.0 us, both measured with a variant of its
+// step-row copy).  More tiles in flight did not pay for the verify: 3 tiles
+// 65.4 us, 4 tiles 68.3 us.
 template <bool kShared>
-__global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
+__global__ __launch_bounds__(256, kShared ? 2 : 1) void k_verify_f32(const VerifyArgs a) {
     const int w = share_index();
     if (w >= a.n_shares) return;
     const int lane = threadIdx.x & 63;
@@ -1482,6 +1489,10 @@ __global__ __launch_bounds__(256, 2) void k_verify_f32(const VerifyArgs a) {
 #ifndef KVQ_VI8_DEPTH
 #define KVQ_VI8_DEPTH 4
 #endif
+// Two waves' worth of registers (256).  Measured on MI355X, 32k R-SWA
+// reference: with the whole register file (one wave per SIMD, up to 512)
+// the verify took 27.0 against 26.6 us and the shared decode 30.1 against
+// 29.2 us; 6 tiles in flight there 27.9 / 31.2 us.
 template <bool kShared>
 __global__ __launch_bounds__(256, 2) void k_verify_i8(const VerifyArgs a) {
     constexpr int D = KVQ_VI8_DEPTH;
@@ -2127,8 +2138,9 @@ hipError_t launch_query_batched(const VerifyArgs& args, const void* fn, int whic
 
 // Shares: up to 16 queries per row make these waves compute-heavy, unlike the
 // single-query decode.  Measured on MI355X (32k R-SWA reference): the f32
-// kernel (2 waves/SIMD) is fastest with one share per 2 resident waves
-// (verify 70.0 -> 68.0 us).  The i8 kernel runs one share per SIMD with
+// kernel at 2 waves/SIMD was fastest with one share per 2 resident waves,
+// i.e. one per SIMD (verify 70.0 -> 68.0 us), which the verify now takes
+// directly at one wave per SIMD.  The i8 kernel runs one share per SIMD with
 // KVQ_VI8_DEPTH tiles in flight and shares aligned to the heads: verify 30.8
 // us, shared decode 38.9 us (one share per resident wave, 3 waves/SIMD and
 // one tile in flight: 35.5 and 43.4 us).
@@ -2162,8 +2174,9 @@ bool pad_segments(VerifyArgs& a, int pad) {
 hipError_t launch_verify_f32(const VerifyArgs& args, hipStream_t s) {
     VerifyArgs a = args;
     if (!pad_segments(a, a.shared ? KVQ_VF32S_PAD : KVQ_VF32_PAD)) return hipErrorInvalidValue;
+    // the shared decode: one share per 2 resident waves; the verify: one per SIMD
     return a.shared ? launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<true>), 25, 2, KVQ_VF32_ALIGN, s)
-                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 2, KVQ_VF32_ALIGN, s);
+                    : launch_query_batched(a, reinterpret_cast<const void*>(k_verify_f32<false>), 24, 0, KVQ_VF32_ALIGN, s);
 }
 
 #ifndef KVQ_VI8_WPS
