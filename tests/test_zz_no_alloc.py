@@ -61,3 +61,34 @@ def test_noalloc_decode_twice_second_smaller():
         err = max_err(g, oracle.decode(qh, units, hkv, threads=THREADS))
         say("  max err vs oracle %.3g" % err)
         assert err <= F32_TOL, err
+
+
+def test_noalloc_decode_replays_from_a_graph():
+    """The callers this entry point is for include code under HIP graph
+    capture: a captured call is replayed four times, each time after an eager
+    call of the same entry point on another cache has overwritten the static
+    array, and every replay equals decode_attn_q8 with a caller's workspace
+    bit for bit."""
+    say("case: noalloc q8 decode captured in a graph")
+    c, qh, _ = build_case(7200, [900, 33, 0, 64], 3, 4, np.array([1, 0, 1], np.uint8))
+    other, qo_h, _ = build_case(7201, [2500, 1200], 2, 8, np.array([1, 1], np.uint8))
+    hq, hq_o = 3 * 4, 2 * 8
+    q, qo = dev(qh), dev(qo_h)
+    want_t = torch.full((4, hq, 128), np.nan, device="cuda")
+    K.decode_attn_q8(c, hq, q, want_t)
+    out = torch.full((4, hq, 128), np.nan, device="cuda")
+    out_o = torch.empty((2, hq_o, 128), device="cuda")
+    K.decode_attn_q8_noalloc(c, hq, q, out)          # eager first: the device address lookup happens here
+    torch.cuda.synchronize()
+    want = host(want_t).copy()
+    assert np.array_equal(host(out).view(np.uint32), want.view(np.uint32))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.decode_attn_q8_noalloc(c, hq, q, out)
+    for i in range(4):
+        K.decode_attn_q8_noalloc(other, hq_o, qo, out_o)   # another call leaves its partials in the array
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), want.view(np.uint32)), i
+    assert not host(out)[2].any()                    # the empty sequence
