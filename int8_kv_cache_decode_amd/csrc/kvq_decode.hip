@@ -1272,21 +1272,24 @@ __global__ __launch_bounds__(256, kShared ? 2 : 1) void k_verify_f32(const Verif
         if constexpr (kShared) {
             // [P3] write_decode_step of each stream whose step row is in this
             // piece: lane l copies stream l / 4's channels 32 (l % 4) .., all
-            // its loads issued before its stores
+            // its loads issued before its stores.  Named registers: as two
+            // float4[8] arrays the copy was kept in scratch memory (272 bytes
+            // per lane), at the same speed.
             const int s = lane >> 2, c0 = 32 * (lane & 3);
             if (s < a.n_draft && L + s >= it.row0 && L + s < it.row1) {
                 const size_t wr = it.hrow + (size_t)a.swrow[s];
-                float4 kx[8], vx[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    kx[u] = *(const float4*)(KD + s * dstride + c0 + 4 * u);
-                    vx[u] = *(const float4*)(VD + s * dstride + c0 + 4 * u);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    *(float4*)(a.k_store + wr * kHD + c0 + 4 * u) = kx[u];
-                    *(float4*)(a.v_store + wr * kHD + c0 + 4 * u) = vx[u];
-                }
+                const float4* ksrc = (const float4*)(KD + s * dstride + c0);
+                const float4* vsrc = (const float4*)(VD + s * dstride + c0);
+                float4* kdst = (float4*)(a.k_store + wr * kHD + c0);
+                float4* vdst = (float4*)(a.v_store + wr * kHD + c0);
+                const float4 k0 = ksrc[0], k1 = ksrc[1], k2 = ksrc[2], k3 = ksrc[3];
+                const float4 k4 = ksrc[4], k5 = ksrc[5], k6 = ksrc[6], k7 = ksrc[7];
+                const float4 v0 = vsrc[0], v1 = vsrc[1], v2 = vsrc[2], v3 = vsrc[3];
+                const float4 v4 = vsrc[4], v5 = vsrc[5], v6 = vsrc[6], v7 = vsrc[7];
+                kdst[0] = k0; kdst[1] = k1; kdst[2] = k2; kdst[3] = k3;
+                kdst[4] = k4; kdst[5] = k5; kdst[6] = k6; kdst[7] = k7;
+                vdst[0] = v0; vdst[1] = v1; vdst[2] = v2; vdst[3] = v3;
+                vdst[4] = v4; vdst[5] = v5; vdst[6] = v6; vdst[7] = v7;
             }
         }
         // this lane's query (MFMA column): draft (stream) di, head hh of the group
